@@ -1,0 +1,321 @@
+"""Float64 CPU oracle for Multi-Head Latent Attention decode over a latent KV cache.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import this module; the product path never does.  It shares
+no code with the HIP library: it reads the logical (unpaged) arrays, or unpacks
+a paged pool with its own reader, and computes everything in float64 numpy.
+
+What it computes, and where the pages fix it:
+
+* MLA caches one latent vector c per token plus a narrow RoPE key k_rope; the
+  latent is up-projected into per-head keys and values when decoding
+  (RAQ-MLA abstract, searcharxiv "Linchuan Xie" author page).  The RoPE key
+  only enters the attention score, the latent supplies the values (same
+  abstract).
+* Two decoding paths over the same weights are algebraically equivalent: the
+  unabsorbed one that materialises K and V per head, and the absorbed MQA one
+  where W_UK is folded into the query (GQLA abstract, thelatestinai.com paper
+  cards page).  ``decode_unabsorbed`` is the plain definition; ``decode_absorbed``
+  is its twin; the P1 pin checks they agree.
+* The low-bit cache is dequantised inside attention with no full-precision
+  copy of the history (QuantMLA English abstract, arxivdaily QuantMLA page, and
+  the cache-layout part of the QuantMLA podcast page).  The oracle dequantises
+  element by element: RNE_bf16((code - z) * s), integer zero-point z and fp16
+  scale s per (token, group); the product is exact, the bf16 rounding is the
+  only rounding (a reading: the pages give no formula).
+
+Conventions (readings where the pages are silent): W_UK[h] is [d_n, d_c] with
+k_nope = W_UK[h] c; W_UV[h] is [d_c, d_v] with v = c W_UV[h]; query i of s_q
+attends cached tokens 0 .. L - s_q + i; lse is the natural log of the softmax
+denominator of the scaled scores.
+
+Every function here is pinned by tests against closed forms, invariants, brute
+force or library routines; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 64
+
+
+# --------------------------------------------------------------------------- bf16 / codes
+
+def bf16_round(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even, for values exact in float32.
+
+    Input float64 values must be exactly representable in float32 (true for the
+    dequant products below); the float32 bit pattern is rounded at bit 16.
+    Returns float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), x, equal_nan=True):
+        raise ValueError("bf16_round expects float32-exact inputs")
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
+    """Codes from packed bytes: element e lives in byte e*bits//8 at bit (e*bits) % 8."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    e = np.arange(n)
+    byte = packed[..., (e * bits) // 8].astype(np.int64)
+    return ((byte >> ((e * bits) % 8)) & ((1 << bits) - 1)).astype(np.uint8)
+
+
+def dequant(codes: np.ndarray, sz: np.ndarray, group: int) -> np.ndarray:
+    """x_hat = RNE_bf16((code - z) * s) per element; sz[..., g, :] = (s, z) as fp16.
+
+    codes [..., d] uint8, sz [..., d/group, 2] float16.  Float64 result.
+    """
+    codes = np.asarray(codes).astype(np.float64)
+    s = np.asarray(sz[..., 0], dtype=np.float16).astype(np.float64)
+    z = np.asarray(sz[..., 1], dtype=np.float16).astype(np.float64)
+    s_e = np.repeat(s, group, axis=-1)
+    z_e = np.repeat(z, group, axis=-1)
+    return bf16_round((codes - z_e) * s_e)
+
+
+def quantise_rtn(x: np.ndarray, group: int, bits: int):
+    """Round-to-nearest asymmetric quantiser (independent of the input generator's).
+
+    Per group: s = fp16((max-min)/(2^b-1)) (1 if 0); z = clamp(rint(-min/s), 0, 2^b-1);
+    code = clamp(rint(x/s) + z, 0, 2^b-1).  Used to pin the stored codes.
+    """
+    qmax = 2 ** bits - 1
+    x = np.asarray(x, dtype=np.float64)
+    lead = x.shape[:-1]
+    ng = x.shape[-1] // group
+    codes = np.empty(x.shape, dtype=np.uint8)
+    sz = np.empty(lead + (ng, 2), dtype=np.float16)
+    for g in range(ng):
+        seg = x[..., g * group:(g + 1) * group]
+        lo = seg.min(axis=-1)
+        hi = seg.max(axis=-1)
+        s = ((hi - lo) / qmax).astype(np.float16)
+        s[s == 0] = np.float16(1)
+        sd = s.astype(np.float64)
+        z = np.minimum(np.maximum(np.rint(-lo / sd), 0), qmax)
+        q = np.rint(seg / sd[..., None]) + z[..., None]
+        codes[..., g * group:(g + 1) * group] = np.minimum(np.maximum(q, 0), qmax).astype(np.uint8)
+        sz[..., g, 0] = s
+        sz[..., g, 1] = z.astype(np.float16)
+    return codes, sz
+
+
+# --------------------------------------------------------------------------- cache layout
+
+FMT_BITS = {"int4": 4, "int2": 2}
+FMT_BYTES = {"f32": 4, "bf16": 2}
+
+
+def token_bytes(latent_fmt: str, rope_fmt: str, d_c: int, d_r: int,
+                g_c: int = 0, g_r: int = 0) -> int:
+    """Bytes one cached token occupies: values, or codes plus an fp16 (s, z) pair per group."""
+    if latent_fmt in FMT_BYTES:
+        return (d_c + d_r) * FMT_BYTES[latent_fmt]
+    lat = d_c * FMT_BITS[latent_fmt] // 8 + (d_c // g_c) * 4
+    rope = d_r * FMT_BITS[rope_fmt] // 8 + (d_r // g_r) * 4
+    return lat + rope
+
+
+def block_planes(latent_fmt: str, rope_fmt: str, d_c: int, d_r: int, g_c: int = 0, g_r: int = 0):
+    """Plane byte offsets inside one 64-token block; each plane starts 16-byte aligned."""
+    if latent_fmt in FMT_BYTES:
+        return {"row": 0}, BLOCK * token_bytes(latent_fmt, rope_fmt, d_c, d_r)
+    sizes = [("lc", BLOCK * d_c * FMT_BITS[latent_fmt] // 8), ("ls", BLOCK * (d_c // g_c) * 4),
+             ("rc", BLOCK * d_r * FMT_BITS[rope_fmt] // 8), ("rs", BLOCK * (d_r // g_r) * 4)]
+    off, pos = {}, 0
+    for name, size in sizes:
+        off[name] = pos
+        pos += -(-size // 16) * 16
+    return off, pos
+
+
+def read_pool(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray, latent_fmt: str,
+              rope_fmt: str, d_c: int, d_r: int, g_c: int = 0, g_r: int = 0) -> Dict[str, List[np.ndarray]]:
+    """Gather the logical per-sequence cache out of a paged pool (own reader).
+
+    Returns lists over sequences of: 'c', 'k_rope' (float formats, float64) or
+    'c_codes', 'c_sz', 'r_codes', 'r_sz' (quantised formats).
+    """
+    off, bb = block_planes(latent_fmt, rope_fmt, d_c, d_r, g_c, g_r)
+    pool = np.asarray(pool, dtype=np.uint8).reshape(-1, bb)
+    out: Dict[str, List[np.ndarray]] = {}
+    for b, L in enumerate(np.asarray(seq_lens)):
+        L = int(L)
+        nb = -(-L // BLOCK)
+        blocks = pool[np.asarray(block_table[b][:nb], dtype=np.int64)]
+        if latent_fmt in FMT_BYTES:
+            dt = np.float32 if latent_fmt == "f32" else np.uint16
+            rows = blocks.view(dt).reshape(nb * BLOCK, d_c + d_r)[:L]
+            if latent_fmt == "bf16":
+                rows = (rows.astype(np.uint32) << 16).view(np.float32)
+            rows = rows.astype(np.float64)
+            out.setdefault("c", []).append(rows[:, :d_c])
+            out.setdefault("k_rope", []).append(rows[:, d_c:])
+        else:
+            lb, rb = FMT_BITS[latent_fmt], FMT_BITS[rope_fmt]
+
+            def plane(name, per_tok):
+                p = blocks[:, off[name]: off[name] + BLOCK * per_tok]
+                return p.reshape(nb * BLOCK, per_tok)[:L]
+
+            out.setdefault("c_codes", []).append(unpack_codes(plane("lc", d_c * lb // 8), lb, d_c))
+            out.setdefault("c_sz", []).append(
+                np.ascontiguousarray(plane("ls", (d_c // g_c) * 4)).view(np.float16).reshape(L, d_c // g_c, 2))
+            out.setdefault("r_codes", []).append(unpack_codes(plane("rc", d_r * rb // 8), rb, d_r))
+            out.setdefault("r_sz", []).append(
+                np.ascontiguousarray(plane("rs", (d_r // g_r) * 4)).view(np.float16).reshape(L, d_r // g_r, 2))
+    return out
+
+
+# --------------------------------------------------------------------------- attention
+
+def _softmax_attend(s: np.ndarray, values: np.ndarray):
+    """Numerically exact-ish float64 softmax of scores s [T] applied to values [T, d]."""
+    m = s.max()
+    e = np.exp(s - m)
+    den = e.sum()
+    return (e / den) @ values, m + np.log(den)
+
+
+def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """q_lat[..., h, :] = q_nope[..., h, :] @ W_UK[h]  (W_UK folded into the query)."""
+    return np.einsum("...hn,hnc->...hc", np.asarray(q_nope, np.float64), np.asarray(w_uk, np.float64))
+
+
+def out_proj(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """out[..., h, :] = o_lat[..., h, :] @ W_UV[h]  (latent output up-projected to values)."""
+    return np.einsum("...hc,hcv->...hv", np.asarray(o_lat, np.float64), np.asarray(w_uv, np.float64))
+
+
+def attend_latent(q_lat, q_rope, c, k_rope, seq_lens, s_q: int, sm_scale: float,
+                  rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Absorbed-form attention over the shared latent (the decode stage).
+
+    s_t = sm_scale * (q_lat . c_t + q_rope . k_rope_t) for t <= L - s_q + i;
+    o_lat = softmax(s) @ c; lse = log-sum-exp of s.
+    q_lat [B, s_q, H, d_c], q_rope [B, s_q, H, d_r]; c / k_rope indexable per
+    sequence as [L, d].  ``rows`` restricts to (b, i, h) triples (others NaN).
+    Returns o_lat [B, s_q, H, d_c], lse [B, s_q, H].
+    """
+    q_lat = np.asarray(q_lat, np.float64)
+    q_rope = np.asarray(q_rope, np.float64)
+    B, S, H, d_c = q_lat.shape
+    o = np.full((B, S, H, d_c), np.nan)
+    lse = np.full((B, S, H), np.nan)
+    want = None if rows is None else {}
+    if rows is not None:
+        for (b, i, h) in rows:
+            want.setdefault(b, set()).add((i, h))
+    for b in range(B):
+        if want is not None and b not in want:
+            continue
+        L = int(seq_lens[b])
+        cb = np.asarray(c[b][:L], np.float64)
+        kb = np.asarray(k_rope[b][:L], np.float64)
+        for i in range(S):
+            n = L - s_q + i + 1
+            for h in range(H):
+                if want is not None and (i, h) not in want[b]:
+                    continue
+                s = sm_scale * (cb[:n] @ q_lat[b, i, h] + kb[:n] @ q_rope[b, i, h])
+                o[b, i, h], lse[b, i, h] = _softmax_attend(s, cb[:n])
+    return o, lse
+
+
+def decode_unabsorbed(q_nope, q_rope, w_uk, w_uv, c, k_rope, seq_lens, s_q: int, sm_scale: float,
+                      rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """The plain MLA decode: per head, K = [c W_UK[h]^T | k_rope], V = c W_UV[h], softmax attention.
+
+    Returns out [B, s_q, H, d_v], lse [B, s_q, H] (NaN outside ``rows`` if given).
+    """
+    q_nope = np.asarray(q_nope, np.float64)
+    q_rope = np.asarray(q_rope, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    B, S, H, _ = q_nope.shape
+    d_v = w_uv.shape[-1]
+    out = np.full((B, S, H, d_v), np.nan)
+    lse = np.full((B, S, H), np.nan)
+    sel = None if rows is None else set(rows)
+    for b in range(B):
+        L = int(seq_lens[b])
+        cb = np.asarray(c[b][:L], np.float64)
+        kb = np.asarray(k_rope[b][:L], np.float64)
+        for h in range(H):
+            if sel is not None and not any((b, i, h) in sel for i in range(S)):
+                continue
+            k_nope = cb @ w_uk[h].T          # [L, d_n]
+            v = cb @ w_uv[h]                 # [L, d_v]
+            for i in range(S):
+                if sel is not None and (b, i, h) not in sel:
+                    continue
+                n = L - s_q + i + 1
+                s = sm_scale * (k_nope[:n] @ q_nope[b, i, h] + kb[:n] @ q_rope[b, i, h])
+                out[b, i, h], lse[b, i, h] = _softmax_attend(s, v[:n])
+    return out, lse
+
+
+def decode_absorbed(q_nope, q_rope, w_uk, w_uv, c, k_rope, seq_lens, s_q: int, sm_scale: float,
+                    rows=None):
+    """The absorbed twin: q_lat = q_nope W_UK, attend the latent, then up-project by W_UV."""
+    q_lat = absorb_q(q_nope, w_uk)
+    o_lat, lse = attend_latent(q_lat, q_rope, c, k_rope, seq_lens, s_q, sm_scale, rows)
+    return {"q_lat": q_lat, "o_lat": o_lat, "lse": lse, "out": out_proj(o_lat, w_uv)}
+
+
+def merge_partials(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
+    """Combine attention results over disjoint token subsets: lse = log sum exp(lse_u),
+    o = sum_u exp(lse_u - lse) o_u.  Parts with lse = -inf contribute nothing."""
+    lse_parts = [np.asarray(x, np.float64) for x in lse_parts]
+    m = np.max(np.stack(lse_parts), axis=0)
+    w = [np.exp(l - m) for l in lse_parts]
+    tot = sum(w)
+    lse = m + np.log(tot)
+    o = sum(wi[..., None] * np.asarray(oi, np.float64) for wi, oi in zip(w, o_parts)) / tot[..., None]
+    return o, lse
+
+
+def dequant_cache(c_codes, c_sz, r_codes, r_sz, g_c: int, g_r: int):
+    """Per-sequence float64 latent and RoPE key from codes (brute force, element by element)."""
+    c = [dequant(cc, cs, g_c) for cc, cs in zip(c_codes, c_sz)]
+    k = [dequant(rc, rs, g_r) for rc, rs in zip(r_codes, r_sz)]
+    return c, k
+
+
+def exact_dequant_value(code: int, z: float, s: float) -> float:
+    """RNE_bf16 of the exact rational (code - z) * s, computed with Fractions (a second,
+    independent route to the same number, used by the pins)."""
+    v = (Fraction(int(code)) - Fraction(z)) * Fraction(s)
+    if v == 0:
+        return 0.0
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    # bf16: 8 significant bits (1 implicit + 7 stored); normal range only
+    scaled = a * 128
+    lo = scaled.numerator // scaled.denominator
+    rem = scaled - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return float(sign * Fraction(lo, 128) * (Fraction(2) ** e))
+
+
+__all__ = ["bf16_round", "unpack_codes", "dequant", "quantise_rtn", "token_bytes", "block_planes",
+           "read_pool", "absorb_q", "out_proj", "attend_latent", "decode_unabsorbed", "decode_absorbed",
+           "merge_partials", "dequant_cache", "exact_dequant_value"]
