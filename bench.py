@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of one MLA decode step on one MI355X, as one JSON line.
+
+A step is the whole hot path on one synthetic batch already resident in HBM:
+  mla_absorb_q (q_nope . W_UK) -> mla_decode_paged (paged latent attention, split
+  partitions + log-sum-exp combine) -> mla_out_proj (o_lat . W_UV).
+Default workload: DeepSeek-V2-Lite-shaped bf16 decode, 32 sequences x 4096 cached
+tokens, 16 heads, d_c 512 + d_r 64, 64-token paged blocks in a shuffled block table.
+
+value = cached-token.heads per second of step time, i.e. sum_b sum_i (L_b - s_q + i + 1) * H
+divided by the mean step time.  Several independent copies of the cache pool are
+rotated from step to step so the 256 MB Infinity Cache cannot serve the cache reads.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode cached-token·heads/s, HBM TB/s + MFMA util, µs/decode step"
+UNIT = "cached-token·heads/s"
+WORKLOADS = {"tiny-f32": "1", "v2lite-bf16": "2", "v3-bf16-sq1": "3", "v3-bf16-sq2": "3b",
+             "v2lite-int4-32k": "4", "v3-int2-128k": "5"}
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+KERNEL_SOURCES = ["mla_latent_kv_02_amd/csrc/mla_decode.hip", "mla_latent_kv_02_amd/csrc/mla_device.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v2lite-bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--num-splits", type=int, default=0, help="context partitions (0 = library plan)")
+    ap.add_argument("--rotate", type=int, default=0, help="cache pool copies to rotate (0 = enough to exceed 512 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="run warmup+steps and a 256 MiB copy for counter calibration; print no JSON")
+    return ap.parse_args()
+
+
+def algorithmic(x, bytes_per_token):
+    """Bytes and FLOPs the decode (attention) step must move / compute, and the metric's units."""
+    cfg = x.cfg
+    L = x.seq_lens.astype("int64")
+    H, s_q = cfg.H, cfg.s_q
+    qbytes = 2 if cfg.dtype == "bf16" else 4
+    cache_bytes = int(L.sum()) * bytes_per_token
+    io_bytes = len(L) * s_q * H * ((cfg.d_c + cfg.d_r) * qbytes + cfg.d_c * 4 + 4)
+    attended = sum(int((L - s_q + i + 1).sum()) for i in range(s_q))       # (query, token) pairs
+    flops = attended * H * 2 * (2 * cfg.d_c + cfg.d_r)
+    return cache_bytes + io_bytes, cache_bytes, flops, attended * H
+
+
+def cpu_baseline(x, seconds: float):
+    """Time the float64 oracle (the unabsorbed MLA definition) on a bounded sample of sequences."""
+    import oracle
+    cfg = x.cfg
+    lens = [int(L) for L in x.seq_lens]
+    if cfg.quantised:
+        c, k = oracle.dequant_cache([x.c_codes[b, :L] for b, L in enumerate(lens)],
+                                    [x.c_sz[b, :L] for b, L in enumerate(lens)],
+                                    [x.r_codes[b, :L] for b, L in enumerate(lens)],
+                                    [x.r_sz[b, :L] for b, L in enumerate(lens)], cfg.latent_group, cfg.rope_group)
+    else:
+        c = [x.c[b, :L] for b, L in enumerate(lens)]
+        k = [x.k_rope[b, :L] for b, L in enumerate(lens)]
+    done_units, t_used, nseq = 0, 0.0, 0
+    order = list(range(len(x.seq_lens)))
+    heads = list(range(cfg.H))
+    # sample: whole sequences (all heads, all query tokens) until ~`seconds` of CPU time
+    for b in order:
+        rows = [(b, i, h) for i in range(cfg.s_q) for h in heads]
+        t0 = time.perf_counter()
+        oracle.decode_unabsorbed(x.q_nope[b:b + 1], x.q_rope[b:b + 1], x.w_uk, x.w_uv, [c[b]], [k[b]],
+                                 x.seq_lens[b:b + 1], cfg.s_q, cfg.sm_scale)
+        t_used += time.perf_counter() - t0
+        L = int(x.seq_lens[b])
+        done_units += sum(L - cfg.s_q + i + 1 for i in range(cfg.s_q)) * cfg.H
+        nseq += 1
+        if t_used >= seconds:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    return {"value": done_units / t_used, "unit": UNIT, "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 unabsorbed oracle (explicit per-head K=[c W_UK^T | k_rope], V=c W_UV, softmax) "
+                      f"over {nseq} of {len(x.seq_lens)} sequences, all {cfg.H} heads; {t_used:.1f} s",
+            "seconds": round(t_used, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode shards over sequences "
+                                   "with no communication, so run one process per GPU instead",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import mla_latent_kv_02_amd as mla
+    from mla_synth import CONFIGS, SEEDS, make_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    mla.lib()
+    name = WORKLOADS[args.workload]
+    cfg = CONFIGS[name]
+    dev = torch.device("cuda:0")
+    log(f"generating {args.workload} inputs")
+    x = make_inputs(cfg, SEEDS[name])
+    log("inputs ready; uploading")
+    desc = mla.cache_desc(cfg.d_c, cfg.d_r, cfg.latent_fmt, cfg.rope_fmt, cfg.latent_group, cfg.rope_group)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    pool_bytes = x.pool.nbytes
+    rotate = args.rotate or max(3, math.ceil(512e6 / pool_bytes) + 1)
+    pools = [torch.from_numpy(x.pool).to(dev) for _ in range(rotate)]
+    bt = torch.from_numpy(x.block_table).to(dev)
+    sl = torch.from_numpy(x.seq_lens).to(dev)
+    qn = torch.from_numpy(x.q_nope).to(dt).to(dev)
+    qr = torch.from_numpy(x.q_rope).to(dt).to(dev)
+    wuk = torch.from_numpy(x.w_uk).to(dt).to(dev)
+    wuv = torch.from_numpy(x.w_uv).to(dt).to(dev)
+    max_len = int(x.seq_lens.max())
+    step = mla.DecodeStep(wuk, wuv, desc, len(x.seq_lens), cfg.s_q, max_len, cfg.sm_scale,
+                          num_splits=args.num_splits, q_lat_dtype=dt)
+    B, s_q, H = len(x.seq_lens), cfg.s_q, cfg.H
+    ql = step.q_lat.view(B, s_q, H, cfg.d_c)
+
+    for i in range(args.warmup):
+        step.run(qn, qr, pools[i % rotate], bt, sl)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps, {rotate} pool copies)")
+
+    if args.profile_run:
+        for i in range(args.steps):
+            step.run(qn, qr, pools[i % rotate], bt, sl)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)          # calibration copy: 256 MiB read + 256 MiB written
+        torch.cuda.synchronize()
+        print(f"profile run done: {args.steps} steps of {args.workload}, 1 calibration copy of 256 MiB", flush=True)
+        return
+
+    K = args.steps
+    st = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    splits, tpc = mla.decode_plan(ql, qr, pools[0], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(st)
+        mla.absorb_q(qn.view(B * s_q, H, cfg.d_n), wuk, out=step.q_lat)
+        e[1].record(st)
+        mla.decode_paged(ql, qr, pools[i % rotate], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits,
+                         out=step.o_lat, lse=step.lse, workspace=step.workspace)
+        e[2].record(st)
+        mla.out_proj(step.o_lat.view(B * s_q, H, cfg.d_c), wuv, out=step.out)
+        e[3].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    absorb_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
+    decode_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
+    proj_ms = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(K)) / K
+    gpu_ms = ev[0][0].elapsed_time(ev[K - 1][3]) / K
+    ms_per_step = max(gpu_ms, 1e-9)
+
+    bpt = mla.block_bytes(desc) // 64
+    alg_bytes, cache_bytes, flops, units = algorithmic(x, bpt)
+    value = units / (ms_per_step * 1e-3)
+    dec_s = decode_ms * 1e-3
+    gbs = alg_bytes / dec_s / 1e9
+    tflops = flops / dec_s / 1e12
+    ai = flops / alg_bytes
+    bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = "mla_decode_paged (decode_mfma_kernel + combine_kernel)" if cfg.dtype == "bf16" else \
+        "mla_decode_paged (decode_f32_kernel + combine_kernel)"
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["flops_per_launch"] = flops
+    roof["traffic"] = None
+    tfile = os.path.join(ROOT, "profiles", f"decode_traffic_{args.workload}.json")
+    if os.path.exists(tfile):
+        try:
+            tr = json.load(open(tfile))
+            if tr.get("kernel_hash") == kernel_hash():
+                roof["traffic"] = tr.get("bytes_per_launch")
+        except Exception:
+            pass
+
+    rec = {"metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": args.workload, "batch": B, "heads": H, "s_q": s_q, "d_c": cfg.d_c,
+                      "d_r": cfg.d_r, "d_n": cfg.d_n, "d_v": cfg.d_v, "cache": cfg.latent_fmt + "/" + cfg.rope_fmt,
+                      "seq_len": cfg.lens[1] if cfg.lens[0] == "fixed" else list(cfg.lens[1:]),
+                      "mean_seq_len": float(x.seq_lens.mean()), "block_tokens": 64, "splits": splits,
+                      "tiles_per_split": tpc, "pool_copies_rotated": rotate},
+           "roofline": roof,
+           "us_per_step": round(ms_per_step * 1e3, 2), "wall_us_per_step": round(wall / K * 1e6, 2),
+           "decode_us": round(decode_ms * 1e3, 2), "absorb_us": round(absorb_ms * 1e3, 2),
+           "out_proj_us": round(proj_ms * 1e3, 2), "hbm_tbps": round(gbs / 1e3, 3),
+           "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "cache_bytes": cache_bytes}
+    log(f"timed {K} steps: {ms_per_step * 1e3:.2f} us/step, decode {decode_ms * 1e3:.2f} us")
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * libmla — Multi-Head Latent Attention decode over a paged latent KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  MLA keeps one compressed latent vector c_KV per
+ * cached token plus a narrow, separately rotated RoPE key; at decode time the
+ * latent is up-projected into per-head keys and values (RAQ-MLA abstract,
+ * searcharxiv "Linchuan Xie" author page).  Because the key up-projection can
+ * be folded into the query, every head can score the same shared latent: the
+ * absorbed MQA decoding path (GQLA abstract, thelatestinai.com paper-cards
+ * page).  One decode step is therefore three calls:
+ *
+ *   mla_absorb_q      q_lat[n,h,:] = q_nope[n,h,:] . W_UK[h]             (fold W_UK into q)
+ *   mla_decode_paged  s_t = sm_scale (q_lat . c_t + q_rope . k_rope_t),
+ *                     o_lat = softmax(s) . c  over the paged cache       (shared-latent attention)
+ *   mla_out_proj      out[n,h,:] = o_lat[n,h,:] . W_UV[h]                (up-project to values)
+ *
+ * The cache may hold bf16/fp32 values or low-bit codes (INT4 latent + INT4
+ * RoPE key, or INT2 latent + INT4 RoPE key) which are unpacked and
+ * dequantised inside the attention loop, without a full-precision copy of the
+ * history (QuantMLA English abstract, arxivdaily QuantMLA page; cache-layout
+ * part of the QuantMLA podcast page).  Decoding with two query tokens per
+ * sequence (s_q = 2, causal within the pair) is supported, the multi-token
+ * prediction case named in the GQLA abstract.
+ *
+ * Conventions
+ *   - Row-major, densely packed tensors unless a stride argument says otherwise.
+ *   - W_UK is [H][d_n][d_c] (k_nope = W_UK[h] c); W_UV is [H][d_c][d_v].
+ *   - seq_lens[b] counts every cached token of sequence b INCLUDING its s_q new
+ *     query tokens; query i (0-based) attends cached tokens 0 .. L_b - s_q + i.
+ *   - lse is the natural logarithm of the softmax denominator of the scaled scores.
+ *
+ * Ownership and streams
+ *   The caller owns all memory (device pointers unless stated).  libmla never
+ *   allocates, frees or keeps pointers after a call returns.  Every compute call
+ *   is asynchronous on the caller's stream (a hipStream_t passed as void*, NULL =
+ *   the null stream); buffers must stay valid until that stream has completed.
+ *   The only process-wide state is a cached per-device CU count.
+ *
+ * Errors
+ *   Every entry point returns an mla_status (int32_t).  Arguments are validated
+ *   on the host before anything is launched, so a call that fails validation
+ *   has launched nothing and touched no device.  No C++ exception crosses the ABI.
+ */
+#ifndef LIBMLA_H
+#define LIBMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* Status codes. */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG 1  /* null pointer, non-positive size, bad enum, misaligned pointer, seq too short */
+#define MLA_ERR_UNSUPPORTED 2  /* valid combination for which no kernel exists (e.g. bf16 cache with d_c != 512) */
+#define MLA_ERR_WORKSPACE 3    /* workspace missing or smaller than mla_decode_workspace_size() */
+#define MLA_ERR_HIP 4          /* a HIP runtime call or kernel launch failed */
+
+/* Element types of q / weights / outputs. */
+#define MLA_F32 0
+#define MLA_BF16 1
+
+/* Cache element formats. */
+#define MLA_FMT_F32 0
+#define MLA_FMT_BF16 1
+#define MLA_FMT_INT4 2  /* 2 codes per byte; element 2j in the low nibble of byte j */
+#define MLA_FMT_INT2 3  /* 4 codes per byte; element 4j+k in bits 2k..2k+1 of byte j */
+
+/*
+ * Paged-cache descriptor.  A block holds block_size (= 64) consecutive tokens
+ * of one sequence.
+ *   Float formats (latent_fmt == rope_fmt, F32 or BF16): one plane of rows
+ *     [c (d_c values) | k_rope (d_r values)] per token, block = 64 rows.
+ *   Quantised formats: four planes per block, each starting 16-byte aligned:
+ *     latent codes [64][d_c*bits/8] | latent (scale, zero) fp16 pairs [64][d_c/latent_group][2] |
+ *     rope codes   [64][d_r*bits/8] | rope   (scale, zero) fp16 pairs [64][d_r/rope_group][2].
+ *   A quantised element dequantises to RNE_bf16((code - zero) * scale), with an
+ *   integer-valued fp16 zero-point and an fp16 scale per (token, group).
+ */
+typedef struct mla_cache_desc {
+  int32_t d_c;          /* latent width */
+  int32_t d_r;          /* RoPE key width */
+  int32_t block_size;   /* tokens per block; must be 64 */
+  int32_t latent_fmt;   /* MLA_FMT_* */
+  int32_t rope_fmt;     /* MLA_FMT_*; BF16/F32 must match latent_fmt; INT4 with a quantised latent */
+  int32_t latent_group; /* channels per scale/zero group of the latent (quantised only) */
+  int32_t rope_group;   /* channels per scale/zero group of the RoPE key (quantised only) */
+} mla_cache_desc;
+
+/* Bytes of one block for this descriptor, or -1 if the descriptor is invalid. */
+int64_t mla_cache_block_bytes(const mla_cache_desc* desc);
+
+/* Byte offsets of the four planes (latent codes, latent scale/zero, rope codes, rope
+ * scale/zero) inside a block; float formats report {0, -1, -1, -1}. */
+int32_t mla_cache_plane_offsets(const mla_cache_desc* desc, int64_t offsets[4]);
+
+/*
+ * mla_absorb_q: fold W_UK into the query (the absorbed MQA form, GQLA abstract).
+ *   q_lat[n][h][:] = sum_i q_nope[n, h, i] * W_UK[h][i][:]          (fp32 accumulation)
+ *   q_nope element (n, h, i) is at q_nope[n*q_stride_n + h*q_stride_h + i] (elements).
+ *   w_uk [H][d_n][d_c] of w_dtype; q_lat [N][H][d_c] of out_dtype (dense).
+ *   dtypes: q, w, out in {MLA_F32, MLA_BF16}.  bf16 weights use the MFMA kernel when
+ *   d_n % 32 == 0 and d_c % 64 == 0; every other combination runs a plain fp32 kernel.
+ */
+int32_t mla_absorb_q(const void* q_nope, int64_t q_stride_n, int64_t q_stride_h, int32_t q_dtype,
+                     const void* w_uk, int32_t w_dtype, void* q_lat, int32_t out_dtype, int32_t N,
+                     int32_t H, int32_t d_n, int32_t d_c, void* stream);
+
+/* Arguments of mla_decode_paged.  Every pointer is a device pointer except the struct itself. */
+typedef struct mla_decode_args {
+  const void* q_lat;          /* [batch][s_q][H][d_c], q_dtype; 16-byte aligned */
+  const void* q_rope;         /* [batch][s_q][H][d_r], q_dtype, already rotated */
+  int32_t q_dtype;            /* MLA_BF16 (bf16/quantised caches) or MLA_F32 (fp32 cache) */
+  const void* cache_pool;     /* num_blocks blocks of mla_cache_block_bytes(&cache) bytes, 16-byte aligned */
+  int64_t num_blocks;
+  mla_cache_desc cache;
+  const int32_t* block_table; /* [batch][block_table_stride]; entries of the first ceil(L_b/64) slots are used */
+  int32_t block_table_stride; /* >= ceil(max_seq_len / 64) */
+  const int32_t* seq_lens;    /* [batch], each in [s_q, max_seq_len] */
+  int32_t max_seq_len;        /* host-side upper bound of seq_lens, used to plan the split */
+  int32_t batch;
+  int32_t s_q;                /* 1 or 2 */
+  int32_t num_heads;
+  float sm_scale;             /* score scale, e.g. 1/sqrt(d_n + d_r) */
+  int32_t num_splits;         /* context partitions per longest sequence; 0 = automatic */
+  void* o_lat;                /* [batch][s_q][H][d_c] of o_dtype */
+  int32_t o_dtype;            /* MLA_F32 or MLA_BF16 */
+  float* lse;                 /* [batch][s_q][H] natural-log LSE, or NULL */
+  void* workspace;            /* scratch for split partials, >= mla_decode_workspace_size() bytes */
+  size_t workspace_bytes;
+} mla_decode_args;
+
+/* Workspace needed by mla_decode_paged for these arguments (0 when no split is used). */
+int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes);
+
+/* The split plan mla_decode_paged will use: partitions of the longest sequence and
+ * 64-token tiles per partition.  num_cus = compute units to plan for (0 = query the
+ * current device).  Pure host logic. */
+int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* num_splits,
+                        int32_t* tiles_per_split);
+
+/*
+ * mla_decode_paged: attention of the absorbed queries over the shared latent.
+ *   For sequence b, query i < s_q, head h, over cached tokens t <= L_b - s_q + i:
+ *     s_t  = sm_scale * (q_lat[b,i,h] . c_t + q_rope[b,i,h] . k_rope_t)
+ *     o_lat[b,i,h] = sum_t softmax(s)_t c_t,   lse[b,i,h] = log sum_t exp(s_t)
+ *   c_t and k_rope_t are read through block_table from the pool, dequantised in the
+ *   kernel for INT4/INT2 caches.  Cache slots past L_b in a sequence's last block are
+ *   never used.  Long contexts are split into partitions whose partial (o, lse) are
+ *   merged by a log-sum-exp combine; the result is deterministic for fixed arguments.
+ *   Block-table entries outside [0, num_blocks) are not dereferenced (their tokens
+ *   read as zeros); seq_lens above max_seq_len are clamped to it.
+ *   Kernels: bf16 MFMA for BF16/INT4/INT2 caches with d_c = 512, d_r = 64; a plain
+ *   fp32 kernel for F32 caches (d_c <= 1024, d_r <= 256).
+ */
+int32_t mla_decode_paged(const mla_decode_args* args, void* stream);
+
+/*
+ * mla_out_proj: up-project the latent attention output (W_UV, RAQ-MLA abstract).
+ *   out[n][h][:] = sum_j o_lat[n, h, j] * W_UV[h][j][:]      (fp32 accumulation)
+ *   o_lat element (n, h, j) at o_lat[n*o_stride_n + h*o_stride_h + j]; w_uv [H][d_c][d_v];
+ *   out [N][H][d_v] dense.  fp32 o_lat with bf16 weights is split into two bf16 terms
+ *   (hi + lo) for the MFMA so the product keeps fp32-level accuracy.
+ */
+int32_t mla_out_proj(const void* o_lat, int64_t o_stride_n, int64_t o_stride_h, int32_t o_dtype,
+                     const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, int32_t N,
+                     int32_t H, int32_t d_c, int32_t d_v, void* stream);
+
+/*
+ * mla_dequant_blocks (test/debug): materialise blocks of a paged cache as bf16.
+ *   out_bf16[k][t][0:d_c] = latent of token t of block block_ids[k], [d_c:d_c+d_r] = RoPE key,
+ *   for k < n_blocks, t < 64.  Uses the same device unpack/dequant code as the decode
+ *   kernel, so its output is bit-identical to what the decode consumes.  F32 caches are
+ *   rounded to bf16 (ties to even).  Ids outside [0, num_blocks) give zero rows.
+ */
+int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
+                           const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(int32_t status);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMLA_H */

@@ -1,0 +1,244 @@
+"""libmla for MI355X: MLA decode over a paged latent KV cache (bf16 / INT4 / INT2).
+
+Thin Python binding over the C ABI in include/libmla.h.  Every step of the
+decode runs in the library's HIP kernels; this module only checks tensors and
+passes pointers and the current HIP stream.  PyTorch provides device memory
+and streams.  Importing works without a GPU; calling needs the built
+libmla.so (``python -m mla_latent_kv_02_amd.build``) and an MI355X.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (MLA_BF16, MLA_F32, MLA_FMT_BF16, MLA_FMT_F32, MLA_FMT_INT2, MLA_FMT_INT4,  # noqa: F401
+                   CacheDesc, DecodeArgs, FMT_BY_NAME)
+
+__all__ = ["MlaError", "cache_desc", "block_bytes", "plane_offsets", "absorb_q", "decode_paged", "out_proj",
+           "dequant_blocks", "decode_workspace_size", "decode_plan", "DecodeStep", "lib"]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.load().mla_status_string(status).decode()
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.MLA_OK:
+        raise MlaError(status, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libmla operates on GPU tensors")
+
+
+def cache_desc(d_c: int = 512, d_r: int = 64, latent_fmt="bf16", rope_fmt=None, latent_group: int = 0,
+               rope_group: int = 0) -> CacheDesc:
+    lf = FMT_BY_NAME[latent_fmt] if isinstance(latent_fmt, str) else int(latent_fmt)
+    rf = lf if rope_fmt is None else (FMT_BY_NAME[rope_fmt] if isinstance(rope_fmt, str) else int(rope_fmt))
+    return CacheDesc(d_c, d_r, 64, lf, rf, latent_group, rope_group)
+
+
+def block_bytes(desc: CacheDesc) -> int:
+    return int(_lib.load().mla_cache_block_bytes(ctypes.byref(desc)))
+
+
+def plane_offsets(desc: CacheDesc):
+    off = (ctypes.c_int64 * 4)()
+    _check(_lib.load().mla_cache_plane_offsets(ctypes.byref(desc), off), "mla_cache_plane_offsets")
+    return list(off)
+
+
+def _proj(fn, name, x, w, out_dtype, out):
+    # x [N, H, K] (strided rows allowed, unit stride along K), w [H, K, M] dense
+    _need_cuda(x, w)
+    if x.dim() != 3 or w.dim() != 3 or x.shape[1] != w.shape[0] or x.shape[2] != w.shape[1]:
+        raise ValueError(f"{name}: shapes {tuple(x.shape)} x {tuple(w.shape)} do not match")
+    if x.stride(2) != 1:
+        x = x.contiguous()
+    w = w.contiguous()
+    N, H, K = x.shape
+    M = w.shape[2]
+    if out is None:
+        out = torch.empty((N, H, M), dtype=out_dtype, device=x.device)
+    if not out.is_contiguous() or out.shape != (N, H, M):
+        raise ValueError(f"{name}: out must be a dense [N, H, M] tensor")
+    st = fn(ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1), _dt(x), ctypes.c_void_p(w.data_ptr()),
+            _dt(w), ctypes.c_void_p(out.data_ptr()), _dt(out), N, H, K, M, _stream(x.device))
+    _check(st, name)
+    return out
+
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out_dtype=torch.bfloat16,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_lat[n, h, :] = q_nope[n, h, :] @ W_UK[h]; q_nope [N, H, d_n], w_uk [H, d_n, d_c]."""
+    return _proj(_lib.load().mla_absorb_q, "mla_absorb_q", q_nope, w_uk, out_dtype, out)
+
+
+def out_proj(o_lat: torch.Tensor, w_uv: torch.Tensor, out_dtype=torch.float32,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[n, h, :] = o_lat[n, h, :] @ W_UV[h]; o_lat [N, H, d_c], w_uv [H, d_c, d_v]."""
+    return _proj(_lib.load().mla_out_proj, "mla_out_proj", o_lat, w_uv, out_dtype, out)
+
+
+def _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                 o_lat, lse, workspace) -> DecodeArgs:
+    B, s_q, H, d_c = q_lat.shape
+    a = DecodeArgs()
+    a.q_lat = q_lat.data_ptr()
+    a.q_rope = q_rope.data_ptr()
+    a.q_dtype = _dt(q_lat)
+    a.cache_pool = pool.data_ptr()
+    a.num_blocks = pool.shape[0]
+    a.cache = desc
+    a.block_table = block_table.data_ptr()
+    a.block_table_stride = block_table.shape[1]
+    a.seq_lens = seq_lens.data_ptr()
+    a.max_seq_len = int(max_seq_len)
+    a.batch, a.s_q, a.num_heads = B, s_q, H
+    a.sm_scale = float(sm_scale)
+    a.num_splits = int(num_splits)
+    a.o_lat = o_lat.data_ptr() if o_lat is not None else 1 << 12
+    a.o_dtype = _dt(o_lat) if o_lat is not None else MLA_F32
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    return a
+
+
+def _check_decode_tensors(q_lat, q_rope, pool, desc, block_table, seq_lens):
+    _need_cuda(q_lat, q_rope, pool, block_table, seq_lens)
+    if q_lat.dim() != 4 or q_rope.dim() != 4 or q_lat.shape[:3] != q_rope.shape[:3]:
+        raise ValueError("q_lat [B, s_q, H, d_c] and q_rope [B, s_q, H, d_r] expected")
+    if q_lat.shape[3] != desc.d_c or q_rope.shape[3] != desc.d_r:
+        raise ValueError("q widths do not match the cache descriptor")
+    if q_lat.dtype != q_rope.dtype or not q_lat.is_contiguous() or not q_rope.is_contiguous():
+        raise ValueError("q_lat and q_rope must be dense and of one dtype")
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or not pool.is_contiguous() or pool.shape[1] != block_bytes(desc):
+        raise ValueError("pool must be a dense uint8 [num_blocks, block_bytes] tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be dense int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q_lat.shape[0],):
+        raise ValueError("seq_lens must be int32 [B]")
+
+
+def decode_workspace_size(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale,
+                          num_splits: int = 0) -> int:
+    a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                     None, None, None)
+    n = ctypes.c_size_t()
+    _check(_lib.load().mla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)), "mla_decode_workspace_size")
+    return int(n.value)
+
+
+def decode_plan(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits: int = 0,
+                num_cus: int = 0) -> Tuple[int, int]:
+    a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                     None, None, None)
+    s, t = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.load().mla_decode_plan(ctypes.byref(a), num_cus, ctypes.byref(s), ctypes.byref(t)), "mla_decode_plan")
+    return s.value, t.value
+
+
+def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, desc: CacheDesc,
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                 num_splits: int = 0, o_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 want_lse: bool = True):
+    """Absorbed-form attention over the paged latent cache.  Returns (o_lat, lse)."""
+    _check_decode_tensors(q_lat, q_rope, pool, desc, block_table, seq_lens)
+    B, s_q, H, d_c = q_lat.shape
+    if out is None:
+        out = torch.empty((B, s_q, H, d_c), dtype=o_dtype, device=q_lat.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
+    if workspace is None:
+        n = decode_workspace_size(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale,
+                                  num_splits)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q_lat.device)
+    a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                     out, lse, workspace)
+    _check(_lib.load().mla_decode_paged(ctypes.byref(a), _stream(q_lat.device)), "mla_decode_paged")
+    return out, lse
+
+
+def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor) -> torch.Tensor:
+    """bf16 [n, 64, d_c + d_r] view of cache blocks, from the decode kernel's own reader."""
+    _need_cuda(pool, block_ids)
+    if block_ids.dtype != torch.int32 or not block_ids.is_contiguous():
+        raise ValueError("block_ids must be dense int32")
+    n = block_ids.numel()
+    out = torch.empty((n, 64, desc.d_c + desc.d_r), dtype=torch.bfloat16, device=pool.device)
+    st = _lib.load().mla_dequant_blocks(ctypes.c_void_p(pool.data_ptr()), pool.shape[0], ctypes.byref(desc),
+                                        ctypes.c_void_p(block_ids.data_ptr()), n, ctypes.c_void_p(out.data_ptr()),
+                                        _stream(pool.device))
+    _check(st, "mla_dequant_blocks")
+    return out
+
+
+@dataclass
+class DecodeStep:
+    """One MLA decode step with preallocated buffers: absorb -> paged decode -> out_proj.
+
+    q_nope [B, s_q, H, d_n], q_rope [B, s_q, H, d_r] (bf16 or fp32), w_uk [H, d_n, d_c],
+    w_uv [H, d_c, d_v].  ``run`` enqueues the three library calls on the current stream
+    and returns out [B, s_q, H, d_v] (fp32).
+    """
+    w_uk: torch.Tensor
+    w_uv: torch.Tensor
+    desc: CacheDesc
+    batch: int
+    s_q: int
+    max_seq_len: int
+    sm_scale: float
+    num_splits: int = 0
+    q_lat_dtype: torch.dtype = torch.bfloat16
+
+    def __post_init__(self):
+        H, d_n, d_c = self.w_uk.shape
+        d_v = self.w_uv.shape[2]
+        dev = self.w_uk.device
+        N = self.batch * self.s_q
+        self.H, self.d_n, self.d_c, self.d_v = H, d_n, d_c, d_v
+        self.q_lat = torch.empty((N, H, d_c), dtype=self.q_lat_dtype, device=dev)
+        self.o_lat = torch.empty((self.batch, self.s_q, H, d_c), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.batch, self.s_q, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((N, H, d_v), dtype=torch.float32, device=dev)
+        self.workspace = None
+
+    def run(self, q_nope, q_rope, pool, block_table, seq_lens):
+        B, s_q, H = self.batch, self.s_q, self.H
+        absorb_q(q_nope.view(B * s_q, H, self.d_n), self.w_uk, out=self.q_lat)
+        ql = self.q_lat.view(B, s_q, H, self.d_c)
+        if self.workspace is None:
+            n = decode_workspace_size(ql, q_rope, pool, self.desc, block_table, seq_lens, self.max_seq_len,
+                                      self.sm_scale, self.num_splits)
+            self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=pool.device)
+        decode_paged(ql, q_rope, pool, self.desc, block_table, seq_lens, self.max_seq_len, self.sm_scale,
+                     self.num_splits, out=self.o_lat, lse=self.lse, workspace=self.workspace)
+        out_proj(self.o_lat.view(B * s_q, H, self.d_c), self.w_uv, out=self.out)
+        return self.out.view(B, s_q, H, self.d_v)

@@ -1,0 +1,351 @@
+// libmla host layer: argument validation, cache layout, split planning and launches.
+// Validation never touches the device, so a rejected call has no side effects.
+#include "libmla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "mla_internal.hpp"
+
+namespace {
+
+constexpr int kBlock = 64;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_dtype(int32_t d) { return d == MLA_F32 || d == MLA_BF16; }
+bool is_float_fmt(int32_t f) { return f == MLA_FMT_F32 || f == MLA_FMT_BF16; }
+bool is_quant_fmt(int32_t f) { return f == MLA_FMT_INT4 || f == MLA_FMT_INT2; }
+int fmt_bits(int32_t f) { return f == MLA_FMT_INT4 ? 4 : f == MLA_FMT_INT2 ? 2 : f == MLA_FMT_BF16 ? 16 : 32; }
+
+struct Layout {
+  int64_t block_bytes = -1;
+  int64_t off[4] = {0, -1, -1, -1};
+};
+
+// Byte layout of one block (see mla_cache_desc).  Returns false for an invalid descriptor.
+bool cache_layout(const mla_cache_desc* d, Layout* out) {
+  if (d == nullptr || d->block_size != kBlock || d->d_c <= 0 || d->d_r <= 0) return false;
+  if (is_float_fmt(d->latent_fmt)) {
+    if (d->rope_fmt != d->latent_fmt) return false;
+    out->block_bytes = (int64_t)kBlock * (d->d_c + d->d_r) * (fmt_bits(d->latent_fmt) / 8);
+    out->off[0] = 0;
+    out->off[1] = out->off[2] = out->off[3] = -1;
+    return true;
+  }
+  if (!is_quant_fmt(d->latent_fmt) || !is_quant_fmt(d->rope_fmt)) return false;
+  if (d->latent_group <= 0 || d->rope_group <= 0 || d->d_c % d->latent_group || d->d_r % d->rope_group) return false;
+  const int lb = fmt_bits(d->latent_fmt), rb = fmt_bits(d->rope_fmt);
+  if ((d->d_c * lb) % 8 || (d->d_r * rb) % 8) return false;
+  const int64_t sizes[4] = {(int64_t)kBlock * d->d_c * lb / 8, (int64_t)kBlock * (d->d_c / d->latent_group) * 4,
+                            (int64_t)kBlock * d->d_r * rb / 8, (int64_t)kBlock * (d->d_r / d->rope_group) * 4};
+  int64_t pos = 0;
+  for (int i = 0; i < 4; ++i) {
+    out->off[i] = pos;
+    pos += align_up(sizes[i], 16);
+  }
+  out->block_bytes = pos;
+  return true;
+}
+
+// Is there a decode kernel for this (valid) descriptor and query dtype?
+bool decode_supported(const mla_cache_desc* d, int32_t q_dtype) {
+  if (d->latent_fmt == MLA_FMT_F32) return q_dtype == MLA_F32 && d->d_c <= 1024 && d->d_r <= 256;
+  if (d->d_c != 512 || d->d_r != 64) return false;
+  if (d->latent_fmt == MLA_FMT_BF16) return true;
+  if (d->rope_fmt != MLA_FMT_INT4 || (d->rope_group != 32 && d->rope_group != 64)) return false;
+  if (d->latent_fmt == MLA_FMT_INT4) return d->latent_group % 16 == 0;
+  return d->latent_group % 32 == 0;  // INT2
+}
+
+int32_t validate_decode(const mla_decode_args* a, Layout* lay) {
+  if (a == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!a->q_lat || !a->q_rope || !a->cache_pool || !a->block_table || !a->seq_lens || !a->o_lat)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch <= 0 || a->num_heads <= 0 || (a->s_q != 1 && a->s_q != 2)) return MLA_ERR_INVALID_ARG;
+  if (a->max_seq_len < a->s_q || a->num_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->o_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(a->sm_scale) || a->num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if (!cache_layout(&a->cache, lay)) return MLA_ERR_INVALID_ARG;
+  if (a->block_table_stride < ceil_div(a->max_seq_len, kBlock)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(a->q_lat, 16) || !aligned(a->q_rope, 16) || !aligned(a->cache_pool, 16) || !aligned(a->o_lat, 16))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) || (a->lse && !aligned(a->lse, 4)))
+    return MLA_ERR_INVALID_ARG;
+  if (!decode_supported(&a->cache, a->q_dtype)) return MLA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)a->s_q * a->num_heads;
+  if (rows > (1 << 20) || (int64_t)a->batch * rows > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+struct Plan {
+  int rt;          // row tiles per workgroup (MFMA kernel), 0 = fp32 kernel
+  int rg;          // row groups per sequence
+  int splits;      // partitions of the longest sequence
+  int tpc;         // 64-token tiles per partition
+};
+
+Plan make_plan(const mla_decode_args* a, int cus) {
+  Plan p{};
+  const int R = a->s_q * a->num_heads;
+  int wgs_per_cu;
+  if (a->cache.latent_fmt == MLA_FMT_F32) {
+    p.rt = 0;
+    p.rg = R;
+    wgs_per_cu = 8;
+  } else {
+    p.rt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+    p.rg = (int)ceil_div(R, 16 * p.rt);
+    wgs_per_cu = p.rt == 4 ? 1 : 2;
+  }
+  const int nblk = (int)ceil_div(a->max_seq_len, kBlock);
+  int splits = a->num_splits;
+  if (splits <= 0) {
+    const int64_t target = (int64_t)cus * wgs_per_cu;
+    splits = (int)ceil_div(target, (int64_t)a->batch * p.rg);
+  }
+  splits = splits < 1 ? 1 : (splits > nblk ? nblk : splits);
+  p.tpc = (int)ceil_div(nblk, splits);
+  p.splits = (int)ceil_div(nblk, p.tpc);
+  return p;
+}
+
+int32_t device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *cus = v;
+      return MLA_OK;
+    }
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return MLA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(v, std::memory_order_relaxed);
+  *cus = v;
+  return MLA_OK;
+}
+
+size_t partial_bytes(const mla_decode_args* a, const Plan& p, size_t* lse_off) {
+  if (p.splits <= 1) {
+    *lse_off = 0;
+    return 0;
+  }
+  const int64_t units = (int64_t)a->batch * p.splits * a->s_q * a->num_heads;
+  const int64_t o_bytes = align_up(units * a->cache.d_c * 4, 256);
+  *lse_off = (size_t)o_bytes;
+  return (size_t)(o_bytes + align_up(units * 4, 256));
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+int32_t validate_proj(const void* x, int32_t xdt, const void* w, int32_t wdt, void* y, int32_t ydt, int32_t N,
+                      int32_t H, int32_t K, int32_t M, int64_t sn, int64_t sh) {
+  if (!x || !w || !y) return MLA_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || K <= 0 || M <= 0 || sn < 0 || sh < 0) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(xdt) || !valid_dtype(wdt) || !valid_dtype(ydt)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(x, xdt == MLA_F32 ? 4 : 2) || !aligned(w, wdt == MLA_F32 ? 4 : 2) || !aligned(y, ydt == MLA_F32 ? 4 : 2))
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)N * H * M > (1LL << 40)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int32_t run_proj(const void* x, int64_t sn, int64_t sh, int32_t xdt, const void* w, int32_t wdt, void* y,
+                 int32_t ydt, int32_t N, int32_t H, int32_t K, int32_t M, void* stream) {
+  int32_t s = validate_proj(x, xdt, w, wdt, y, ydt, N, H, K, M, sn, sh);
+  if (s != MLA_OK) return s;
+  mla::ProjParams p{};
+  p.X = x;
+  p.sxn = sn;
+  p.sxh = sh;
+  p.x_f32 = xdt == MLA_F32;
+  p.W = w;
+  p.w_f32 = wdt == MLA_F32;
+  p.Y = y;
+  p.y_f32 = ydt == MLA_F32;
+  p.N = N;
+  p.H = H;
+  p.K = K;
+  p.M = M;
+  p.aligned16 = aligned(x, 16) && aligned(w, 16);
+  return hip_status(mla::launch_proj(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this combination";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown mla status";
+}
+
+int64_t mla_cache_block_bytes(const mla_cache_desc* desc) {
+  Layout l;
+  return cache_layout(desc, &l) ? l.block_bytes : -1;
+}
+
+int32_t mla_cache_plane_offsets(const mla_cache_desc* desc, int64_t offsets[4]) {
+  Layout l;
+  if (offsets == nullptr || !cache_layout(desc, &l)) return MLA_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i) offsets[i] = l.off[i];
+  return MLA_OK;
+}
+
+int32_t mla_absorb_q(const void* q_nope, int64_t q_stride_n, int64_t q_stride_h, int32_t q_dtype, const void* w_uk,
+                     int32_t w_dtype, void* q_lat, int32_t out_dtype, int32_t N, int32_t H, int32_t d_n, int32_t d_c,
+                     void* stream) {
+  return run_proj(q_nope, q_stride_n, q_stride_h, q_dtype, w_uk, w_dtype, q_lat, out_dtype, N, H, d_n, d_c, stream);
+}
+
+int32_t mla_out_proj(const void* o_lat, int64_t o_stride_n, int64_t o_stride_h, int32_t o_dtype, const void* w_uv,
+                     int32_t w_dtype, void* out, int32_t out_dtype, int32_t N, int32_t H, int32_t d_c, int32_t d_v,
+                     void* stream) {
+  return run_proj(o_lat, o_stride_n, o_stride_h, o_dtype, w_uv, w_dtype, out, out_dtype, N, H, d_c, d_v, stream);
+}
+
+int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* num_splits, int32_t* tiles_per_split) {
+  Layout lay;
+  int32_t s = validate_decode(args, &lay);
+  if (s != MLA_OK) return s;
+  if (num_splits == nullptr || tiles_per_split == nullptr || num_cus < 0) return MLA_ERR_INVALID_ARG;
+  int cus = num_cus;
+  if (cus == 0) {
+    s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+  }
+  const Plan p = make_plan(args, cus);
+  *num_splits = p.splits;
+  *tiles_per_split = p.tpc;
+  return MLA_OK;
+}
+
+int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes) {
+  Layout lay;
+  int32_t s = validate_decode(args, &lay);
+  if (s != MLA_OK) return s;
+  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != MLA_OK) return s;
+  size_t lse_off = 0;
+  *bytes = partial_bytes(args, make_plan(args, cus), &lse_off);
+  return MLA_OK;
+}
+
+int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
+  Layout lay;
+  int32_t s = validate_decode(a, &lay);
+  if (s != MLA_OK) return s;
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != MLA_OK) return s;
+  const Plan plan = make_plan(a, cus);
+  size_t lse_off = 0;
+  const size_t need = partial_bytes(a, plan, &lse_off);
+  if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need || !aligned(a->workspace, 256)))
+    return MLA_ERR_WORKSPACE;
+
+  mla::DecodeParams p{};
+  p.q_lat = a->q_lat;
+  p.q_rope = a->q_rope;
+  p.q_f32 = a->q_dtype == MLA_F32;
+  p.pool = (const uint8_t*)a->cache_pool;
+  p.num_blocks = a->num_blocks;
+  p.block_bytes = lay.block_bytes;
+  p.off_lc = lay.off[0];
+  p.off_ls = lay.off[1];
+  p.off_rc = lay.off[2];
+  p.off_rs = lay.off[3];
+  p.g_lat = a->cache.latent_group > 0 ? a->cache.latent_group : 1;
+  p.g_rope = a->cache.rope_group > 0 ? a->cache.rope_group : 1;
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.seq_lens = a->seq_lens;
+  p.max_seq_len = a->max_seq_len;
+  p.B = a->batch;
+  p.s_q = a->s_q;
+  p.H = a->num_heads;
+  p.R = a->s_q * a->num_heads;
+  p.RG = plan.rg;
+  p.d_c = a->cache.d_c;
+  p.d_r = a->cache.d_r;
+  p.max_chunks = plan.splits;
+  p.tpc = plan.tpc;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  const bool split = plan.splits > 1;
+  float* part_o = split ? (float*)a->workspace : nullptr;
+  float* part_lse = split ? (float*)((char*)a->workspace + lse_off) : nullptr;
+  p.out = split ? (void*)part_o : a->o_lat;
+  p.out_bf16 = split ? 0 : (a->o_dtype == MLA_BF16);
+  p.out_lse = split ? part_lse : a->lse;
+  const int64_t units = (int64_t)a->batch * plan.splits * plan.rg;
+  if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  p.total_units = (int)units;
+  p.units_per_xcd = (int)ceil_div(units, 8);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = plan.rt == 0 ? mla::launch_decode_f32(p, st) : mla::launch_decode_mfma(p, a->cache.latent_fmt, plan.rt, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (split) {
+    mla::CombineParams c{};
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.seq_lens = a->seq_lens;
+    c.max_seq_len = a->max_seq_len;
+    c.R = p.R;
+    c.d_c = p.d_c;
+    c.max_chunks = plan.splits;
+    c.tpc = plan.tpc;
+    c.out = a->o_lat;
+    c.out_bf16 = a->o_dtype == MLA_BF16;
+    c.out_lse = a->lse;
+    e = mla::launch_combine(c, a->batch, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
+                           const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream) {
+  Layout lay;
+  if (!cache_pool || !block_ids || !out_bf16 || n_blocks <= 0 || num_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (!cache_layout(desc, &lay)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(cache_pool, 16) || !aligned(out_bf16, 16) || !aligned(block_ids, 4)) return MLA_ERR_INVALID_ARG;
+  if (desc->latent_fmt != MLA_FMT_F32 && !decode_supported(desc, MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  mla::DequantParams p{};
+  p.pool = (const uint8_t*)cache_pool;
+  p.num_blocks = num_blocks;
+  p.block_bytes = lay.block_bytes;
+  p.off_lc = lay.off[0];
+  p.off_ls = lay.off[1];
+  p.off_rc = lay.off[2];
+  p.off_rs = lay.off[3];
+  p.g_lat = desc->latent_group > 0 ? desc->latent_group : 1;
+  p.g_rope = desc->rope_group > 0 ? desc->rope_group : 1;
+  p.d_c = desc->d_c;
+  p.d_r = desc->d_r;
+  p.ids = block_ids;
+  p.n = n_blocks;
+  p.out = (uint16_t*)out_bf16;
+  return hip_status(mla::launch_dequant(p, desc->latent_fmt, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,227 @@
+// Device-side building blocks shared by the libmla kernels (gfx950 / CDNA4).
+//
+// - vector types for the bf16 MFMA operands,
+// - round-to-nearest-even fp32 -> bf16,
+// - the cache-tile reader: loads one 64-token block of a paged cache into
+//   registers (bf16 rows, or INT4/INT2 codes with their fp16 scale/zero) and
+//   later emits it as bf16 8-element pieces, dequantising codes on the way.
+//   The decode kernel and the mla_dequant_blocks kernel both use this reader,
+//   so what the debug entry point returns is exactly what attention consumes.
+//
+// Dequantisation (QuantMLA: unpack and dequantise inside attention): a code q
+// of group (scale s, integer zero-point z) becomes RNE_bf16((q - z) * s).  With
+// |q - z| <= 15 and an fp16 s the product has at most 15 significant bits, so
+// fma(q, s, -(z*s)) returns it exactly in fp32 (z*s is exact as well); the one
+// rounding is the final fp32 -> bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int BLOCK_TOKENS = 64;
+
+// Cache formats (values of MLA_FMT_*).
+constexpr int FMT_F32 = 0, FMT_BF16 = 1, FMT_INT4 = 2, FMT_INT2 = 3;
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  // round to nearest, ties to even (inputs are finite here)
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)v;
+}
+
+// Eight INT4 codes of one 32-bit word (element e at bits 4e..4e+3) -> 8 bf16 (as 4 words).
+__device__ __forceinline__ u32x4 dequant_int4x8(uint32_t w, float s, float zs) {
+  uint32_t lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 in bytes 0..3
+  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  u32x4 r;
+  r[0] = pack_bf16x2(__builtin_fmaf((float)(lo & 0xFF), s, -zs), __builtin_fmaf((float)(hi & 0xFF), s, -zs));
+  r[1] = pack_bf16x2(__builtin_fmaf((float)((lo >> 8) & 0xFF), s, -zs), __builtin_fmaf((float)((hi >> 8) & 0xFF), s, -zs));
+  r[2] = pack_bf16x2(__builtin_fmaf((float)((lo >> 16) & 0xFF), s, -zs), __builtin_fmaf((float)((hi >> 16) & 0xFF), s, -zs));
+  r[3] = pack_bf16x2(__builtin_fmaf((float)(lo >> 24), s, -zs), __builtin_fmaf((float)(hi >> 24), s, -zs));
+  return r;
+}
+
+// Eight INT2 codes of the low 16 bits of w (element e at bits 2e..2e+1) -> 8 bf16.
+__device__ __forceinline__ u32x4 dequant_int2x8(uint32_t w, float s, float zs) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float a = (float)((w >> (4 * k)) & 3u);
+    float b = (float)((w >> (4 * k + 2)) & 3u);
+    r[k] = pack_bf16x2(__builtin_fmaf(a, s, -zs), __builtin_fmaf(b, s, -zs));
+  }
+  return r;
+}
+
+// (scale, zero) fp16 pair packed in a 32-bit word -> (s, z*s) as fp32.
+__device__ __forceinline__ void scale_zero(uint32_t sz, float& s, float& zs) {
+  s = half_bits_to_f32(sz & 0xFFFFu);
+  float z = half_bits_to_f32(sz >> 16);
+  zs = z * s;  // exact: z is a small integer, s has 11 significant bits
+}
+
+// Byte offsets of the four planes of a quantised block.
+struct QuantPlanes {
+  int32_t lc, ls, rc, rs;
+};
+
+// --------------------------------------------------------------------------------------
+// Tile reader.  NT threads cooperate on one 64-token block of d_c = 512, d_r = 64.
+// load(): issue the global loads into registers (tokens >= valid are not read).
+// emit(f): call f(token, col8, u32x4 bf16x8) for every 8-element piece of the block, in
+//          the latent-then-rope column order (col8 in 0..71), zeros for tokens >= valid.
+// --------------------------------------------------------------------------------------
+template <int FMT, int NT>
+struct TileReader;
+
+// bf16 rows [c(512) | k_rope(64)] = 72 pieces of 16 bytes per token, 4608 per block.
+template <int NT>
+struct TileReader<FMT_BF16, NT> {
+  static constexpr int PIECES = BLOCK_TOKENS * 72;
+  static constexpr int PER = PIECES / NT;
+  static_assert(PIECES % NT == 0, "thread count must divide the block");
+  u32x4 v[PER];
+
+  __device__ __forceinline__ void load(const uint8_t* blk, int valid, int tid, const QuantPlanes&, int, int) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int p = tid + k * NT;
+      int tok = p / 72;
+      if (tok < valid) {
+        v[k] = __builtin_nontemporal_load((const u32x4*)(blk + (size_t)p * 16));
+      } else {
+        v[k] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void emit(F&& f, int valid, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int p = tid + k * NT;
+      f(p / 72, p % 72, v[k]);
+    }
+  }
+};
+
+// Quantised latent (INT4 or INT2) + INT4 RoPE key.
+// Latent codes are read 16 bytes at a time: 32 INT4 or 64 INT2 elements per piece.
+template <int FMT, int NT>
+struct QuantTileReader {
+  static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
+  static constexpr int LAT_BYTES = 512 * BITS / 8;              // per token
+  static constexpr int LAT_PIECES = BLOCK_TOKENS * LAT_BYTES / 16;
+  static constexpr int ELEMS = 128 / BITS;                       // elements per 16-byte piece
+  static constexpr int PIECES_PER_TOK = LAT_BYTES / 16;
+  static constexpr int PER = LAT_PIECES / NT;
+  static constexpr int ROPE_PIECES = BLOCK_TOKENS * 2;           // 64 INT4 codes = 2 pieces/token
+  static_assert(LAT_PIECES % NT == 0, "thread count must divide the latent plane");
+  static_assert(ROPE_PIECES <= NT, "one rope piece per thread at most");
+  u32x4 c[PER];
+  uint32_t sz[PER][2];   // (scale, zero) words for the piece's first and second half
+  u32x4 rc;
+  uint32_t rsz;
+
+  __device__ __forceinline__ void load(const uint8_t* blk, int valid, int tid, const QuantPlanes& pl,
+                                       int g_lat, int g_rope) {
+    const int groups = 512 / g_lat;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int p = tid + k * NT;
+      int tok = p / PIECES_PER_TOK;
+      int e0 = (p % PIECES_PER_TOK) * ELEMS;
+      if (tok < valid) {
+        c[k] = __builtin_nontemporal_load((const u32x4*)(blk + pl.lc + (size_t)p * 16));
+        const uint32_t* szp = (const uint32_t*)(blk + pl.ls) + tok * groups;
+        sz[k][0] = szp[e0 / g_lat];
+        sz[k][1] = szp[(e0 + ELEMS / 2) / g_lat];
+      } else {
+        c[k] = u32x4{0, 0, 0, 0};
+        sz[k][0] = sz[k][1] = 0;
+      }
+    }
+    if (tid < ROPE_PIECES) {
+      int tok = tid >> 1;
+      if (tok < valid) {
+        rc = __builtin_nontemporal_load((const u32x4*)(blk + pl.rc + (size_t)tid * 16));
+        const uint32_t* szp = (const uint32_t*)(blk + pl.rs) + tok * (64 / g_rope);
+        rsz = szp[((tid & 1) * 32) / g_rope];
+      } else {
+        rc = u32x4{0, 0, 0, 0};
+        rsz = 0;
+      }
+    }
+  }
+
+  template <class F>
+  __device__ __forceinline__ void emit(F&& f, int valid, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int p = tid + k * NT;
+      int tok = p / PIECES_PER_TOK;
+      int col8 = (p % PIECES_PER_TOK) * (ELEMS / 8);
+      if (tok >= valid) {
+#pragma unroll
+        for (int j = 0; j < ELEMS / 8; ++j) f(tok, col8 + j, u32x4{0, 0, 0, 0});
+        continue;
+      }
+      float s0, zs0, s1, zs1;
+      scale_zero(sz[k][0], s0, zs0);
+      scale_zero(sz[k][1], s1, zs1);
+      if (BITS == 4) {
+        // 4 words x 8 codes; first two words in the first half of the piece
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(tok, col8 + j, dequant_int4x8(c[k][j], j < 2 ? s0 : s1, j < 2 ? zs0 : zs1));
+      } else {
+        // 4 words x 16 codes; each word gives two 8-element pieces
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float s = j < 2 ? s0 : s1, zs = j < 2 ? zs0 : zs1;
+          f(tok, col8 + 2 * j, dequant_int2x8(c[k][j] & 0xFFFFu, s, zs));
+          f(tok, col8 + 2 * j + 1, dequant_int2x8(c[k][j] >> 16, s, zs));
+        }
+      }
+    }
+    if (tid < ROPE_PIECES) {
+      int tok = tid >> 1;
+      int col8 = 64 + (tid & 1) * 4;
+      if (tok >= valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(tok, col8 + j, u32x4{0, 0, 0, 0});
+      } else {
+        float s, zs;
+        scale_zero(rsz, s, zs);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(tok, col8 + j, dequant_int4x8(rc[j], s, zs));
+      }
+    }
+  }
+};
+
+template <int NT>
+struct TileReader<FMT_INT4, NT> : QuantTileReader<FMT_INT4, NT> {};
+template <int NT>
+struct TileReader<FMT_INT2, NT> : QuantTileReader<FMT_INT2, NT> {};
+
+}  // namespace mla

@@ -1,0 +1,72 @@
+// Internal interface between the libmla host layer (libmla.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Arguments of the decode kernels, resolved by the host layer.
+struct DecodeParams {
+  const void* q_lat;        // [B][R][d_c]
+  const void* q_rope;       // [B][R][d_r]
+  int q_f32;                // q dtype is fp32 (else bf16)
+  const uint8_t* pool;
+  int64_t num_blocks;
+  int64_t block_bytes;
+  int64_t off_lc, off_ls, off_rc, off_rs;  // quantised plane offsets
+  int g_lat, g_rope;        // quantisation group sizes
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  int B, s_q, H, R, RG, d_c, d_r;  // R = s_q * H rows per sequence, RG row groups
+  int max_chunks, tpc;      // partitions per sequence (upper bound) and 64-token tiles per partition
+  int total_units, units_per_xcd;
+  float scale_log2;         // sm_scale * log2(e)
+  void* out;                // partials [B*max_chunks][R][d_c] fp32, or o_lat when max_chunks == 1
+  int out_bf16;
+  float* out_lse;           // [B*max_chunks][R] or lse (may be null when writing o_lat directly)
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  int R, d_c, max_chunks, tpc;
+  void* out;
+  int out_bf16;
+  float* out_lse;
+};
+
+struct ProjParams {
+  const void* X;            // element (n, h, k) at X[n*sxn + h*sxh + k]
+  int64_t sxn, sxh;
+  int x_f32;
+  const void* W;            // [H][K][M]
+  int w_f32;
+  void* Y;                  // [N][H][M]
+  int y_f32;
+  int N, H, K, M;
+  int aligned16;            // X and W base addresses are 16-byte aligned
+};
+
+struct DequantParams {
+  const uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+  int64_t off_lc, off_ls, off_rc, off_rs;
+  int g_lat, g_rope;
+  int d_c, d_r;
+  const int32_t* ids;
+  int n;
+  uint16_t* out;            // [n][64][d_c + d_r] bf16 bits
+};
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
+hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
+hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
+hipError_t launch_proj(const ProjParams& p, hipStream_t st);
+hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
+
+}  // namespace mla

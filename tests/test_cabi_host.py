@@ -1,0 +1,122 @@
+"""CPU checks of the libmla C ABI: the library loads, exports every declared symbol, computes
+cache layouts and split plans, and rejects bad arguments before touching any device."""
+import ctypes
+
+import pytest
+
+import mla_latent_kv_02_amd as mla
+from mla_latent_kv_02_amd import _lib
+from mla_synth import CONFIGS, block_layout
+
+FAKE = 1 << 20  # an aligned, never dereferenced address for validation-only calls
+
+
+def test_library_exports_every_header_function():
+    L = mla.lib()
+    names = _lib.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mla_abi_version() == 1
+
+
+def test_block_layout_matches_generator_and_survey_sizes():
+    for name in ("1", "2", "4", "5"):
+        cfg = CONFIGS[name]
+        d = mla.cache_desc(cfg.d_c, cfg.d_r, cfg.latent_fmt, cfg.rope_fmt, cfg.latent_group, cfg.rope_group)
+        gb, goff = block_layout(cfg)
+        assert mla.block_bytes(d) == gb
+        off = mla.plane_offsets(d)
+        if cfg.quantised:
+            assert off == [goff["lc"], goff["ls"], goff["rc"], goff["rs"]]
+    assert mla.block_bytes(mla.cache_desc(512, 64, "bf16")) == 64 * 1152
+    assert mla.block_bytes(mla.cache_desc(512, 64, "int4", "int4", 64, 64)) == 20736
+    assert mla.block_bytes(mla.cache_desc(512, 64, "int2", "int4", 32, 64)) == 14592
+
+
+@pytest.mark.parametrize("bad", [dict(block_size=32), dict(d_c=0), dict(latent_fmt=9), dict(rope_fmt=0),
+                                 dict(latent_group=0), dict(latent_group=48)])
+def test_invalid_descriptors(bad):
+    d = mla.cache_desc(512, 64, "int4", "int4", 64, 64)
+    for k, v in bad.items():
+        setattr(d, k, v)
+    assert mla.block_bytes(d) == -1
+
+
+def _args(**kw):
+    a = _lib.DecodeArgs()
+    a.q_lat = a.q_rope = a.cache_pool = a.block_table = a.seq_lens = a.o_lat = FAKE
+    a.q_dtype = _lib.MLA_BF16
+    a.num_blocks = 100
+    a.cache = mla.cache_desc(512, 64, "bf16")
+    a.block_table_stride = 64
+    a.max_seq_len = 4096
+    a.batch, a.s_q, a.num_heads = 32, 1, 16
+    a.sm_scale = 0.07
+    a.o_dtype = _lib.MLA_F32
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _plan(a, cus=256):
+    s, t = ctypes.c_int32(), ctypes.c_int32()
+    st = mla.lib().mla_decode_plan(ctypes.byref(a), cus, ctypes.byref(s), ctypes.byref(t))
+    return st, s.value, t.value
+
+
+def test_split_plan_covers_the_longest_sequence():
+    for B, H, s_q, L, ns in [(32, 16, 1, 4096, 0), (64, 128, 1, 8192, 0), (64, 128, 2, 8192, 0),
+                             (16, 16, 1, 32768, 0), (4, 128, 1, 131072, 0), (1, 16, 1, 1, 0), (3, 16, 1, 700, 5),
+                             (2, 16, 2, 2, 0)]:
+        a = _args(batch=B, num_heads=H, s_q=s_q, max_seq_len=L, num_splits=ns, block_table_stride=-(-L // 64))
+        st, splits, tpc = _plan(a)
+        assert st == 0
+        nblk = -(-L // 64)
+        assert splits * tpc >= nblk and (splits - 1) * tpc < nblk
+        assert 1 <= splits <= nblk
+        if ns:
+            assert splits <= ns
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q_lat", None, 1), ("seq_lens", None, 1), ("batch", 0, 1), ("s_q", 3, 1), ("num_heads", 0, 1),
+    ("max_seq_len", 0, 1), ("q_dtype", 7, 1), ("o_dtype", 5, 1), ("num_blocks", 0, 1),
+    ("block_table_stride", 10, 1), ("q_lat", FAKE + 2, 1), ("cache_pool", FAKE + 8, 1),
+    ("num_splits", -1, 1), ("sm_scale", float("nan"), 1),
+])
+def test_decode_rejects_bad_arguments_without_a_device(field, value, status):
+    a = _args(**{field: value})
+    assert mla.lib().mla_decode_paged(ctypes.byref(a), None) == status
+    n = ctypes.c_size_t()
+    assert mla.lib().mla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == status
+
+
+def test_decode_unsupported_combinations():
+    L = mla.lib()
+    a = _args(cache=mla.cache_desc(256, 64, "bf16"))
+    assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
+    a = _args(cache=mla.cache_desc(64, 16, "f32"), q_dtype=_lib.MLA_BF16)
+    assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
+    a = _args(cache=mla.cache_desc(512, 64, "int2", "int4", 16, 64))
+    assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
+    a = _args(cache=mla.cache_desc(512, 64, "int4", "int2", 64, 64))
+    assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_projection_and_dequant_validation():
+    L = mla.lib()
+    assert L.mla_absorb_q(None, 0, 0, 1, FAKE, 1, FAKE, 1, 1, 1, 128, 512, None) == 1
+    assert L.mla_absorb_q(FAKE, 0, 0, 1, FAKE, 1, FAKE, 1, 0, 1, 128, 512, None) == 1
+    assert L.mla_out_proj(FAKE, 0, 0, 9, FAKE, 1, FAKE, 1, 1, 1, 512, 128, None) == 1
+    d = mla.cache_desc(512, 64, "int4", "int4", 64, 64)
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), None, 1, FAKE, None) == 1
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), FAKE, 0, FAKE, None) == 1
+    d2 = mla.cache_desc(256, 64, "int4", "int4", 64, 64)
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d2), FAKE, 1, FAKE, None) == 2
+
+
+def test_status_strings():
+    L = mla.lib()
+    for s in range(5):
+        assert L.mla_status_string(s).startswith(b"MLA_")

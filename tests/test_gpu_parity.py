@@ -1,0 +1,283 @@
+"""GPU parity of libmla against the float64 oracle (marked gpu; needs MI355X + built libmla.so).
+
+Stage-wise: each call's oracle is fed that call's actual inputs (e.g. the bf16 q_lat the
+decode consumed).  Bar: integer unpack/dequant bit-exact; fp32-accumulated outputs within
+max|gpu - ref| / max|ref| <= 2e-3 for bf16 inputs and <= 1e-5 for fp32 inputs.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from mla_synth import CONFIGS, make_inputs  # noqa: E402
+from tests.gpu_helpers import (bf16_exact, desc_of, dev, logical_cache, norm_err, tdtype,  # noqa: E402
+                               to_device)
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_02_amd as m
+    m.lib()
+    return m
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def assert_bf16_output(got, ref, tol):
+    """A bf16 output is one RNE rounding (relative error <= 2^-8) of an fp32 value that is
+    within tol * max|ref| of the reference: |got - ref| <= 2^-8 (|ref| + tol max|ref|) + tol max|ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    mx = np.max(np.abs(ref))
+    bound = 2.0 ** -8 * (np.abs(ref) + tol * mx) + tol * mx
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
+def _decode_stage(m, x, num_splits=0, o_dtype=torch.float32):
+    """Run mla_decode_paged on bf16-rounded (or fp32) oracle q_lat; return gpu and oracle results."""
+    cfg = x.cfg
+    t = to_device(x)
+    q_lat64 = oracle.absorb_q(x.q_nope, x.w_uk)
+    if cfg.dtype == "bf16":
+        q_lat64 = bf16_exact(q_lat64)
+    q_lat = torch.from_numpy(q_lat64).to(tdtype(cfg)).to(dev())
+    out, lse = m.decode_paged(q_lat, t["q_rope"], t["pool"], desc_of(cfg), t["block_table"], t["seq_lens"],
+                              int(x.seq_lens.max()), cfg.sm_scale, num_splits=num_splits, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    c, k = logical_cache(x)
+    ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c, k, x.seq_lens, cfg.s_q,
+                                          cfg.sm_scale)
+    return out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_lse
+
+
+# ------------------------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("name", ["2", "4", "5"])
+def test_dequant_blocks_bit_exact(mla, name):
+    cfg = CONFIGS[name]
+    x = make_inputs(cfg, 31, lens=[1, 63, 64, 65, 200], H=2)
+    _say("dequant_blocks", name)
+    t = to_device(x)
+    ids = torch.from_numpy(x.block_table.reshape(-1).copy()).to(dev())
+    got = mla.dequant_blocks(t["pool"], desc_of(cfg), ids).view(torch.int16).cpu().numpy().view(np.uint16)
+    torch.cuda.synchronize()
+    c, k = logical_cache(x)
+    nb = x.block_table.shape[1]
+    for b, L in enumerate(x.seq_lens):
+        ref = np.concatenate([c[b], k[b]], axis=1)
+        ref_bits = (ref.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        blk = got[b * nb:(b + 1) * nb].reshape(-1, cfg.d_c + cfg.d_r)[:L]
+        np.testing.assert_array_equal(blk, ref_bits)
+
+
+@pytest.mark.parametrize("fmt,bits,group", [("int4", 4, 64), ("int2", 2, 32), ("int4", 4, 16)])
+def test_dequant_every_code_zero_and_scale(mla, fmt, bits, group):
+    """Every code x every zero-point x fp16 scales (subnormal .. max) through the GPU reader."""
+    qmax = 2 ** bits - 1
+    d_c, d_r = 512, 64
+    ng = d_c // group
+    rng = np.random.default_rng(5)
+    svals = np.concatenate([np.array([0x0001, 0x0003, 0x03FF, 0x0400, 0x3C00, 0x3C01, 0x7BFF], np.uint16),
+                            rng.integers(1, 0x7BFF, 4000).astype(np.uint16)]).view(np.float16)
+    T = 64 * 4  # four blocks
+    codes = (np.arange(T * d_c).reshape(T, d_c) * 7 % (qmax + 1)).astype(np.uint8)
+    sz = np.zeros((T, ng, 2), np.float16)
+    sz[..., 0] = svals[np.arange(T * ng) % len(svals)].reshape(T, ng)
+    sz[..., 1] = (np.arange(T * ng).reshape(T, ng) % (qmax + 1)).astype(np.float16)
+    rcodes = (np.arange(T * d_r).reshape(T, d_r) % 16).astype(np.uint8)
+    rsz = np.zeros((T, 1, 2), np.float16)
+    rsz[:, 0, 0] = svals[np.arange(T) * 3 % len(svals)]
+    rsz[:, 0, 1] = (np.arange(T) % 16).astype(np.float16)
+    from mla_synth import pack_codes
+    desc = mla.cache_desc(d_c, d_r, fmt, "int4", group, 64)
+    bb = mla.block_bytes(desc)
+    off = mla.plane_offsets(desc)
+    pool = np.zeros((4, bb), np.uint8)
+    for blk in range(4):
+        sl = slice(blk * 64, blk * 64 + 64)
+        pool[blk, off[0]:off[0] + 64 * d_c * bits // 8] = pack_codes(codes[sl], bits).reshape(-1)
+        pool[blk, off[1]:off[1] + 64 * ng * 4] = sz[sl].view(np.uint8).reshape(-1)
+        pool[blk, off[2]:off[2] + 64 * 32] = pack_codes(rcodes[sl], 4).reshape(-1)
+        pool[blk, off[3]:off[3] + 64 * 4] = rsz[sl].view(np.uint8).reshape(-1)
+    _say("dequant every code", fmt, group)
+    got = mla.dequant_blocks(torch.from_numpy(pool).to(dev()), desc,
+                             torch.arange(4, dtype=torch.int32, device=dev()))
+    got = got.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, d_c + d_r)
+    ref = np.concatenate([oracle.dequant(codes, sz, group), oracle.dequant(rcodes, rsz, 64)], axis=1)
+    ref_bits = (ref.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(got, ref_bits)
+
+
+# ------------------------------------------------------------------------------------ decode stage
+
+DECODE_CASES = [
+    # (workload, lens, H override)
+    ("2", [1, 63, 64, 65, 700, 1000], None),
+    ("2", [130, 2], 32),          # s_q=1, 32 heads -> 2 row tiles
+    ("3", [64, 129, 500], 128),
+    ("3b", [2, 3, 64, 65, 300], 16),
+    ("3b", [77, 640], 128),
+    ("4", [1, 64, 333, 1030], None),
+    ("5", [65, 1200], 128),
+    ("5", [5, 100], 16),
+]
+
+
+@pytest.mark.parametrize("name,lens,H", DECODE_CASES)
+def test_decode_stage_matches_oracle(mla, name, lens, H):
+    cfg = CONFIGS[name]
+    x = make_inputs(cfg, 41, lens=lens, H=H)
+    _say("decode", name, lens, H)
+    o, lse, ref_o, ref_lse = _decode_stage(mla, x)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    e = norm_err(o, ref_o)
+    el = float(np.max(np.abs(lse - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= TOL_BF16
+    assert el <= TOL_BF16
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_decode_split_count_invariance(mla, splits):
+    cfg = CONFIGS["2"]
+    x = make_inputs(cfg, 43, lens=[1, 64, 200, 900], H=16)
+    _say("split", splits)
+    o, lse, ref_o, ref_lse = _decode_stage(mla, x, num_splits=splits)
+    assert norm_err(o, ref_o) <= TOL_BF16
+    assert float(np.max(np.abs(lse - ref_lse))) <= TOL_BF16
+
+
+def test_decode_deterministic(mla):
+    cfg = CONFIGS["3"]
+    x = make_inputs(cfg, 44, lens=[300, 1000], H=128)
+    t = to_device(x)
+    q = torch.from_numpy(bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))).to(torch.bfloat16).to(dev())
+    _say("determinism")
+    outs = []
+    for _ in range(2):
+        o, l = mla.decode_paged(q, t["q_rope"], t["pool"], desc_of(cfg), t["block_table"], t["seq_lens"],
+                                1000, cfg.sm_scale, num_splits=3)
+        outs.append((o.cpu().numpy().copy(), l.cpu().numpy().copy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_decode_bf16_output(mla):
+    cfg = CONFIGS["2"]
+    x = make_inputs(cfg, 45, lens=[100, 333], H=16)
+    _say("bf16 o_lat")
+    for splits in (1, 3):
+        o, lse, ref_o, ref_lse = _decode_stage(mla, x, num_splits=splits, o_dtype=torch.bfloat16)
+        assert_bf16_output(o, ref_o, TOL_BF16)
+
+
+def test_decode_ones_channel(mla):
+    """A latent channel that is 1 for every token gives exactly-normalised output 1 (P2 on GPU)."""
+    cfg = CONFIGS["2"]
+    y = make_inputs(cfg, 46, lens=[5, 700], H=16)
+    # rebuild the pool with the modified latent: write channel 7 = bf16(1.0) in every valid row
+    pool = y.pool.copy()
+    for b, L in enumerate(y.seq_lens):
+        for j in range(-(-L // 64)):
+            n = min(64, L - 64 * j)
+            rows = pool[y.block_table[b, j]].view(np.uint16).reshape(64, 576)
+            rows[:n, 7] = 0x3F80
+    y.pool = pool
+    y.c[:, :, 7] = np.where(np.arange(y.c.shape[1])[None, :] < y.seq_lens[:, None], 1.0, 0.0)
+    _say("ones channel")
+    o, lse, ref_o, ref_lse = _decode_stage(mla, y, num_splits=4)
+    np.testing.assert_allclose(o[..., 7], 1.0, atol=2e-6, rtol=0)
+
+
+# ------------------------------------------------------------------------------------ projections
+
+@pytest.mark.parametrize("H,N,out_dtype", [(16, 32, torch.bfloat16), (128, 64, torch.bfloat16),
+                                           (128, 128, torch.float32), (3, 5, torch.float32)])
+def test_absorb_q_matches_oracle(mla, H, N, out_dtype):
+    rng = np.random.default_rng(H * 7 + N)
+    qn = bf16_exact(rng.standard_normal((N, H, 128)))
+    wuk = bf16_exact(rng.standard_normal((H, 128, 512)) / np.sqrt(512))
+    _say("absorb", H, N, out_dtype)
+    got = mla.absorb_q(torch.from_numpy(qn).to(torch.bfloat16).to(dev()),
+                       torch.from_numpy(wuk).to(torch.bfloat16).to(dev()), out_dtype=out_dtype)
+    got = got.float().cpu().numpy()
+    ref = oracle.absorb_q(qn, wuk)
+    if out_dtype == torch.bfloat16:
+        assert_bf16_output(got, ref, TOL_F32)
+    else:
+        assert norm_err(got, ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("H,N", [(16, 32), (128, 64), (128, 128), (5, 3)])
+def test_out_proj_matches_oracle(mla, H, N):
+    rng = np.random.default_rng(H + N)
+    ol = rng.standard_normal((N, H, 512)).astype(np.float32).astype(np.float64)
+    wuv = bf16_exact(rng.standard_normal((H, 512, 128)) / np.sqrt(512))
+    _say("out_proj", H, N)
+    got = mla.out_proj(torch.from_numpy(ol).float().to(dev()), torch.from_numpy(wuv).to(torch.bfloat16).to(dev()))
+    got = got.cpu().numpy()
+    ref = oracle.out_proj(ol, wuv)
+    assert norm_err(got, ref) <= TOL_F32 * 10
+
+
+# ------------------------------------------------------------------------------------ fp32 path
+
+def test_tiny_fp32_pipeline_matches_unabsorbed(mla):
+    """The tiny fp32 workload end to end (absorb -> decode -> out_proj) vs the unabsorbed oracle."""
+    cfg = CONFIGS["1"]
+    x = make_inputs(cfg, 1)
+    t = to_device(x)
+    _say("tiny fp32 pipeline")
+    step = mla.DecodeStep(t["w_uk"], t["w_uv"], desc_of(cfg), 1, 1, int(x.seq_lens.max()), cfg.sm_scale,
+                          num_splits=2, q_lat_dtype=torch.float32)
+    out = step.run(t["q_nope"], t["q_rope"], t["pool"], t["block_table"], t["seq_lens"])
+    torch.cuda.synchronize()
+    c, k = logical_cache(x)
+    ref, ref_lse = oracle.decode_unabsorbed(x.q_nope, x.q_rope, x.w_uk, x.w_uv, c, k, x.seq_lens, 1, cfg.sm_scale)
+    assert norm_err(out.cpu().numpy(), ref) <= TOL_F32
+    assert float(np.max(np.abs(step.lse.cpu().numpy() - ref_lse))) <= TOL_F32
+
+
+@pytest.mark.parametrize("lens,s_q", [([1, 63, 64, 65, 300], 1), ([2, 64, 129], 2)])
+def test_fp32_decode_ragged(mla, lens, s_q):
+    cfg = CONFIGS["1"].with_(s_q=s_q)
+    x = make_inputs(cfg, 50, lens=lens)
+    _say("fp32 ragged", lens, s_q)
+    for splits in (1, 3):
+        o, lse, ref_o, ref_lse = _decode_stage(mla, x, num_splits=splits)
+        assert norm_err(o, ref_o) <= TOL_F32
+        assert float(np.max(np.abs(lse - ref_lse))) <= TOL_F32
+
+
+# ------------------------------------------------------------------------------------ pipeline
+
+@pytest.mark.parametrize("name,lens,H", [("2", [100, 1500], None), ("3b", [300, 70], 128), ("4", [800], None)])
+def test_pipeline_vs_unabsorbed_oracle(mla, name, lens, H):
+    """Whole decode step from q_nope against the plain (unabsorbed) MLA definition.
+
+    The absorbed path rounds q_lat to bf16 before the MFMA; that rounding alone moves the
+    output by ~2^-9 relative per q_lat element, so the end-to-end bound is 4e-3 here
+    (each stage separately meets 2e-3, see the stage tests)."""
+    cfg = CONFIGS[name]
+    x = make_inputs(cfg, 60, lens=lens, H=H)
+    t = to_device(x)
+    _say("pipeline", name, lens, H)
+    step = mla.DecodeStep(t["w_uk"], t["w_uv"], desc_of(x.cfg), len(lens), x.cfg.s_q, int(x.seq_lens.max()),
+                          x.cfg.sm_scale)
+    out = step.run(t["q_nope"], t["q_rope"], t["pool"], t["block_table"], t["seq_lens"]).cpu().numpy()
+    c, k = logical_cache(x)
+    ref, _ = oracle.decode_unabsorbed(x.q_nope, x.q_rope, x.w_uk, x.w_uv, c, k, x.seq_lens, x.cfg.s_q,
+                                      x.cfg.sm_scale)
+    e = norm_err(out, ref)
+    print(f"  pipeline err {e:.3e}", flush=True)
+    assert e <= 4e-3
