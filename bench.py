@@ -89,10 +89,8 @@ def cpu_baseline(x, seconds: float):
         k = [x.k_rope[b, :L] for b, L in enumerate(lens)]
     done_units, t_used, nseq = 0, 0.0, 0
     order = list(range(len(x.seq_lens)))
-    heads = list(range(cfg.H))
     # sample: whole sequences (all heads, all query tokens) until ~`seconds` of CPU time
-    for b in order:
-        rows = [(b, i, h) for i in range(cfg.s_q) for h in heads]
+    for b in order * 1000:
         t0 = time.perf_counter()
         oracle.decode_unabsorbed(x.q_nope[b:b + 1], x.q_rope[b:b + 1], x.w_uk, x.w_uv, [c[b]], [k[b]],
                                  x.seq_lens[b:b + 1], cfg.s_q, cfg.sm_scale)
@@ -108,8 +106,8 @@ def cpu_baseline(x, seconds: float):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     return {"value": done_units / t_used, "unit": UNIT, "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 unabsorbed oracle (explicit per-head K=[c W_UK^T | k_rope], V=c W_UV, softmax) "
-                      f"over {nseq} of {len(x.seq_lens)} sequences, all {cfg.H} heads; {t_used:.1f} s",
+            "sample": f"float64 unabsorbed oracle (explicit per-head K=[c W_UK^T | k_rope], V=c W_UV, softmax), "
+                      f"{nseq} sequence passes over the batch of {len(x.seq_lens)}, all {cfg.H} heads; {t_used:.1f} s",
             "seconds": round(t_used, 2)}
 
 
@@ -147,8 +145,9 @@ def main():
     wuk = torch.from_numpy(x.w_uk).to(dt).to(dev)
     wuv = torch.from_numpy(x.w_uv).to(dt).to(dev)
     max_len = int(x.seq_lens.max())
+    total_len = int(x.seq_lens.astype("int64").sum())
     step = mla.DecodeStep(wuk, wuv, desc, len(x.seq_lens), cfg.s_q, max_len, cfg.sm_scale,
-                          num_splits=args.num_splits, q_lat_dtype=dt)
+                          num_splits=args.num_splits, q_lat_dtype=dt, total_seq_len=total_len)
     B, s_q, H = len(x.seq_lens), cfg.s_q, cfg.H
     ql = step.q_lat.view(B, s_q, H, cfg.d_c)
 
@@ -170,7 +169,8 @@ def main():
     K = args.steps
     st = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    splits, tpc = mla.decode_plan(ql, qr, pools[0], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits)
+    splits, tpc = mla.decode_plan(ql, qr, pools[0], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits,
+                                  total_seq_len=total_len)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -179,7 +179,7 @@ def main():
         mla.absorb_q(qn.view(B * s_q, H, cfg.d_n), wuk, out=step.q_lat)
         e[1].record(st)
         mla.decode_paged(ql, qr, pools[i % rotate], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits,
-                         out=step.o_lat, lse=step.lse, workspace=step.workspace)
+                         out=step.o_lat, lse=step.lse, workspace=step.workspace, total_seq_len=total_len)
         e[2].record(st)
         mla.out_proj(step.o_lat.view(B * s_q, H, cfg.d_c), wuv, out=step.out)
         e[3].record(st)

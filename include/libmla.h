@@ -123,6 +123,7 @@ typedef struct mla_decode_args {
   int32_t block_table_stride; /* >= ceil(max_seq_len / 64) */
   const int32_t* seq_lens;    /* [batch], each in [s_q, max_seq_len] */
   int32_t max_seq_len;        /* host-side upper bound of seq_lens, used to plan the split */
+  int64_t total_seq_len;      /* optional host-side sum of seq_lens (0 = unknown); balances the plan for ragged batches */
   int32_t batch;
   int32_t s_q;                /* 1 or 2 */
   int32_t num_heads;

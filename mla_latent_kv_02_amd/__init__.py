@@ -106,7 +106,7 @@ def out_proj(o_lat: torch.Tensor, w_uv: torch.Tensor, out_dtype=torch.float32,
 
 
 def _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
-                 o_lat, lse, workspace) -> DecodeArgs:
+                 o_lat, lse, workspace, total_seq_len=0) -> DecodeArgs:
     B, s_q, H, d_c = q_lat.shape
     a = DecodeArgs()
     a.q_lat = q_lat.data_ptr()
@@ -119,6 +119,7 @@ def _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, 
     a.block_table_stride = block_table.shape[1]
     a.seq_lens = seq_lens.data_ptr()
     a.max_seq_len = int(max_seq_len)
+    a.total_seq_len = int(total_seq_len)
     a.batch, a.s_q, a.num_heads = B, s_q, H
     a.sm_scale = float(sm_scale)
     a.num_splits = int(num_splits)
@@ -147,18 +148,18 @@ def _check_decode_tensors(q_lat, q_rope, pool, desc, block_table, seq_lens):
 
 
 def decode_workspace_size(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale,
-                          num_splits: int = 0) -> int:
+                          num_splits: int = 0, total_seq_len: int = 0) -> int:
     a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
-                     None, None, None)
+                     None, None, None, total_seq_len)
     n = ctypes.c_size_t()
     _check(_lib.load().mla_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)), "mla_decode_workspace_size")
     return int(n.value)
 
 
 def decode_plan(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits: int = 0,
-                num_cus: int = 0) -> Tuple[int, int]:
+                num_cus: int = 0, total_seq_len: int = 0) -> Tuple[int, int]:
     a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
-                     None, None, None)
+                     None, None, None, total_seq_len)
     s, t = ctypes.c_int32(), ctypes.c_int32()
     _check(_lib.load().mla_decode_plan(ctypes.byref(a), num_cus, ctypes.byref(s), ctypes.byref(t)), "mla_decode_plan")
     return s.value, t.value
@@ -168,7 +169,7 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, 
                  block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
                  num_splits: int = 0, o_dtype=torch.float32, out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 want_lse: bool = True):
+                 want_lse: bool = True, total_seq_len: int = 0):
     """Absorbed-form attention over the paged latent cache.  Returns (o_lat, lse)."""
     _check_decode_tensors(q_lat, q_rope, pool, desc, block_table, seq_lens)
     B, s_q, H, d_c = q_lat.shape
@@ -178,10 +179,10 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, 
         lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
     if workspace is None:
         n = decode_workspace_size(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale,
-                                  num_splits)
+                                  num_splits, total_seq_len)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q_lat.device)
     a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
-                     out, lse, workspace)
+                     out, lse, workspace, total_seq_len)
     _check(_lib.load().mla_decode_paged(ctypes.byref(a), _stream(q_lat.device)), "mla_decode_paged")
     return out, lse
 
@@ -217,6 +218,7 @@ class DecodeStep:
     sm_scale: float
     num_splits: int = 0
     q_lat_dtype: torch.dtype = torch.bfloat16
+    total_seq_len: int = 0
 
     def __post_init__(self):
         H, d_n, d_c = self.w_uk.shape
@@ -236,9 +238,10 @@ class DecodeStep:
         ql = self.q_lat.view(B, s_q, H, self.d_c)
         if self.workspace is None:
             n = decode_workspace_size(ql, q_rope, pool, self.desc, block_table, seq_lens, self.max_seq_len,
-                                      self.sm_scale, self.num_splits)
+                                      self.sm_scale, self.num_splits, self.total_seq_len)
             self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=pool.device)
         decode_paged(ql, q_rope, pool, self.desc, block_table, seq_lens, self.max_seq_len, self.sm_scale,
-                     self.num_splits, out=self.o_lat, lse=self.lse, workspace=self.workspace)
+                     self.num_splits, out=self.o_lat, lse=self.lse, workspace=self.workspace,
+                     total_seq_len=self.total_seq_len)
         out_proj(self.o_lat.view(B * s_q, H, self.d_c), self.w_uv, out=self.out)
         return self.out.view(B, s_q, H, self.d_v)

@@ -24,7 +24,7 @@ class CacheDesc(ctypes.Structure):
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("q_lat", c_void_p), ("q_rope", c_void_p), ("q_dtype", c_int32), ("cache_pool", c_void_p),
                 ("num_blocks", c_int64), ("cache", CacheDesc), ("block_table", c_void_p),
-                ("block_table_stride", c_int32), ("seq_lens", c_void_p), ("max_seq_len", c_int32),
+                ("block_table_stride", c_int32), ("seq_lens", c_void_p), ("max_seq_len", c_int32), ("total_seq_len", c_int64),
                 ("batch", c_int32), ("s_q", c_int32), ("num_heads", c_int32), ("sm_scale", c_float),
                 ("num_splits", c_int32), ("o_lat", c_void_p), ("o_dtype", c_int32), ("lse", c_void_p),
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t)]

@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kBlock = 64;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxTilesPerSplit = 256;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -61,7 +62,7 @@ bool decode_supported(const mla_cache_desc* d, int32_t q_dtype) {
   if (d->d_c != 512 || d->d_r != 64) return false;
   if (d->latent_fmt == MLA_FMT_BF16) return true;
   if (d->rope_fmt != MLA_FMT_INT4 || (d->rope_group != 32 && d->rope_group != 64)) return false;
-  if (d->latent_fmt == MLA_FMT_INT4) return d->latent_group % 16 == 0;
+  if (d->latent_fmt == MLA_FMT_INT4) return d->latent_group % 32 == 0;
   return d->latent_group % 32 == 0;  // INT2
 }
 
@@ -95,25 +96,31 @@ struct Plan {
 Plan make_plan(const mla_decode_args* a, int cus) {
   Plan p{};
   const int R = a->s_q * a->num_heads;
-  int wgs_per_cu;
+  int64_t target;  // workgroups to aim for
   if (a->cache.latent_fmt == MLA_FMT_F32) {
     p.rt = 0;
     p.rg = R;
-    wgs_per_cu = 8;
+    target = (int64_t)cus * 8;
   } else {
     p.rt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
     p.rg = (int)ceil_div(R, 16 * p.rt);
-    wgs_per_cu = p.rt == 4 ? 1 : 2;
+    target = (int64_t)cus * 2;  // one 512-thread workgroup per CU at a time, two rounds
   }
   const int nblk = (int)ceil_div(a->max_seq_len, kBlock);
-  int splits = a->num_splits;
-  if (splits <= 0) {
-    const int64_t target = (int64_t)cus * wgs_per_cu;
-    splits = (int)ceil_div(target, (int64_t)a->batch * p.rg);
+  int tpc;
+  if (a->num_splits > 0) {
+    tpc = (int)ceil_div(nblk, a->num_splits < nblk ? a->num_splits : nblk);
+  } else if (a->total_seq_len > 0) {
+    // balance by total work: blocks of all sequences x row groups spread over the target
+    const int64_t blocks = ceil_div(a->total_seq_len, kBlock) + a->batch;  // + partial last blocks
+    tpc = (int)ceil_div(blocks * p.rg, target);
+  } else {
+    tpc = (int)ceil_div((int64_t)nblk * a->batch * p.rg, target);
   }
-  splits = splits < 1 ? 1 : (splits > nblk ? nblk : splits);
-  p.tpc = (int)ceil_div(nblk, splits);
-  p.splits = (int)ceil_div(nblk, p.tpc);
+  tpc = tpc < 1 ? 1 : (tpc > nblk ? nblk : tpc);
+  if (p.rt > 0 && tpc > kMaxTilesPerSplit) tpc = kMaxTilesPerSplit;  // the MFMA kernel stages block ids in LDS
+  p.tpc = tpc;
+  p.splits = (int)ceil_div(nblk, tpc);
   return p;
 }
 

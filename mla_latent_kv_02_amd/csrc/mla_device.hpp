@@ -32,15 +32,15 @@ constexpr int BLOCK_TOKENS = 64;
 // Cache formats (values of MLA_FMT_*).
 constexpr int FMT_F32 = 0, FMT_BF16 = 1, FMT_INT4 = 2, FMT_INT2 = 3;
 
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  // round to nearest, ties to even (inputs are finite here)
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

@@ -80,7 +80,7 @@ def test_dequant_blocks_bit_exact(mla, name):
         np.testing.assert_array_equal(blk, ref_bits)
 
 
-@pytest.mark.parametrize("fmt,bits,group", [("int4", 4, 64), ("int2", 2, 32), ("int4", 4, 16)])
+@pytest.mark.parametrize("fmt,bits,group", [("int4", 4, 64), ("int2", 2, 32), ("int4", 4, 32), ("int2", 2, 64)])
 def test_dequant_every_code_zero_and_scale(mla, fmt, bits, group):
     """Every code x every zero-point x fp16 scales (subnormal .. max) through the GPU reader."""
     qmax = 2 ** bits - 1
