@@ -245,3 +245,17 @@ class DecodeStep:
                      total_seq_len=self.total_seq_len)
         out_proj(self.o_lat.view(B * s_q, H, self.d_c), self.w_uv, out=self.out)
         return self.out.view(B, s_q, H, self.d_v)
+
+    def capture(self, q_nope, q_rope, pool, block_table, seq_lens) -> "torch.cuda.CUDAGraph":
+        """Record one step on these tensors into a HIP graph; ``graph.replay()`` re-runs it.
+
+        The three library calls only launch kernels (no allocation, no memset), so the
+        captured step is the same work as ``run``.  Buffers are the step's own and must
+        not be freed while the graph is alive.
+        """
+        self.run(q_nope, q_rope, pool, block_table, seq_lens)  # sizes the workspace outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run(q_nope, q_rope, pool, block_table, seq_lens)
+        return g

@@ -104,16 +104,15 @@ Plan make_plan(const mla_decode_args* a, int cus) {
   } else {
     p.rt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
     p.rg = (int)ceil_div(R, 16 * p.rt);
-    target = (int64_t)cus * 2;  // one 512-thread workgroup per CU at a time, two rounds
+    target = (int64_t)cus;  // one 512-thread workgroup per CU: a single round of equal partitions
   }
   const int nblk = (int)ceil_div(a->max_seq_len, kBlock);
   int tpc;
   if (a->num_splits > 0) {
     tpc = (int)ceil_div(nblk, a->num_splits < nblk ? a->num_splits : nblk);
   } else if (a->total_seq_len > 0) {
-    // balance by total work: blocks of all sequences x row groups spread over the target
-    const int64_t blocks = ceil_div(a->total_seq_len, kBlock) + a->batch;  // + partial last blocks
-    tpc = (int)ceil_div(blocks * p.rg, target);
+    // balance by total work: the batch's blocks x row groups spread over the target
+    tpc = (int)ceil_div(ceil_div(a->total_seq_len, kBlock) * p.rg, target);
   } else {
     tpc = (int)ceil_div((int64_t)nblk * a->batch * p.rg, target);
   }

@@ -3,8 +3,8 @@
 //   value up-projection out[n,h,:]  = o_lat[n,h,:] . W_UV[h]    (RAQ-MLA abstract: latent up-projected)
 // Both are Y[n][h][:] = X[n][h][:] . W[h] with W [H][K][M] row-major.  At decode batch
 // sizes (N = batch * s_q rows) this is a latency-bound read of W, so the work is cut
-// fine: one workgroup per (head, 16 output columns), the K reduction split over the 4
-// wavefronts and merged through LDS.  bf16 weights use v_mfma_f32_16x16x32_bf16 with
+// fine: one workgroup per (head, 16 output columns), the K reduction spread over up to 8
+// wavefronts (k-step j on wavefront j % NW) and merged through LDS.  bf16 weights use v_mfma_f32_16x16x32_bf16 with
 // W^T operands read by ds_read_b64_tr_b16; fp32 X is split into hi + lo bf16 terms so
 // the product keeps ~16 mantissa bits of X.  Other dtype combinations run a plain fp32 loop.
 #include <hip/hip_runtime.h>
@@ -16,8 +16,11 @@ namespace mla {
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_p;
 
-constexpr int PJ_NT = 256;
-constexpr int PJ_MT = 8;  // 16-row tiles per pass (128 rows)
+constexpr int PJ_NW = 8;    // at most 8 wavefronts; k-step j of 32 belongs to wavefront j % NW
+constexpr int PJ_KS = 4;    // at most 4 k-steps per wavefront (K <= 1024)
+
+template <bool XF32>
+constexpr int pj_mt() { return XF32 ? 4 : 8; }  // 16-row tiles per pass
 
 __device__ __forceinline__ void split_hi_lo(const f32x4& a, const f32x4& b, u32x4& vh, u32x4& vl) {
 #pragma unroll
@@ -31,66 +34,86 @@ __device__ __forceinline__ void split_hi_lo(const f32x4& a, const f32x4& b, u32x
   }
 }
 
-// grid (M/16, H); K % 128 == 0, K <= 1024
+// grid (M/16, H), NW = min(8, K/32) wavefronts; K % 32 == 0, K <= 1024.  Dynamic LDS:
+// W tile [K][16] bf16, then (NW - 1) x PJ_MT x 64 partial sums.  Every X load of a wavefront
+// (its k-steps, all row tiles of the pass) is issued before the W tile is waited for.
 template <bool XF32, bool YF32>
-__global__ __launch_bounds__(PJ_NT) void proj_mfma_kernel(ProjParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ws[1024 * 16];      // [K][16]
-  __shared__ __attribute__((aligned(16))) f32x4 part[3][PJ_MT][64];  // partial sums of waves 1..3
+__global__ __launch_bounds__(PJ_NW * 64) void proj_mfma_kernel(ProjParams p) {
+  constexpr int PJ_MT = pj_mt<XF32>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t pj_lds[];
+  const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int h = blockIdx.y;
   const int c0 = blockIdx.x * 16;
   const int K = p.K, M = p.M, N = p.N;
+  bf16_t* Ws = (bf16_t*)pj_lds;                                   // [K][16]
+  f32x4* part = (f32x4*)(pj_lds + (size_t)K * 32);                 // [NW-1][PJ_MT][64]
+  const int nks = (K / 32 - w + NW - 1) / NW;  // k-steps w, w + NW, ...
   const bf16_t* W = (const bf16_t*)p.W + (size_t)h * K * M + c0;
-  for (int q = tid; q < K * 2; q += PJ_NT) {
-    const int k = q >> 1, piece = q & 1;
-    *(u32x4*)&Ws[k * 16 + piece * 8] = *(const u32x4*)(W + (size_t)k * M + piece * 8);
-  }
-  const int KW = K / 4;  // k range of this wavefront
-  const int kb = w * KW;
-  __syncthreads();
   for (int nb = 0; nb < N; nb += 16 * PJ_MT) {
     const int mts = min(PJ_MT, (N - nb + 15) / 16);
+    // X operands of this wavefront, loaded up front
+    constexpr int XV = XF32 ? 2 : 1;
+    u32x4 xr[PJ_KS][PJ_MT][XV];
+#pragma unroll
+    for (int ks = 0; ks < PJ_KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < PJ_MT; ++mt) {
+        const int n = nb + mt * 16 + lr;
+        const bool ok = ks < nks && mt < mts && n < N;
+        const size_t xo = (size_t)(ok ? n : 0) * p.sxn + (size_t)h * p.sxh + (w + NW * ks) * 32 + lg * 8;
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+          if (XF32)
+            xr[ks][mt][v] = ok ? *(const u32x4*)((const float*)p.X + xo + 4 * v) : u32x4{0, 0, 0, 0};
+          else
+            xr[ks][mt][v] = ok ? *(const u32x4*)((const bf16_t*)p.X + xo) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    if (nb == 0) {
+      for (int q = tid; q < K * 2; q += NW * 64) {
+        const int k = q >> 1, piece = q & 1;
+        *(u32x4*)&Ws[k * 16 + piece * 8] = *(const u32x4*)(W + (size_t)k * M + piece * 8);
+      }
+      __syncthreads();
+    }
     f32x4 acc[PJ_MT];
 #pragma unroll
     for (int mt = 0; mt < PJ_MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = kb; kk < kb + KW; kk += 32) {
-      const bf16_t* wb = &Ws[(kk + lg * 8 + (lr >> 2)) * 16 + (lr & 3) * 4];
+#pragma unroll
+    for (int ks = 0; ks < PJ_KS; ++ks) {
+      if (ks >= nks) break;
+      const bf16_t* wb = &Ws[((w + NW * ks) * 32 + lg * 8 + (lr >> 2)) * 16 + (lr & 3) * 4];
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)wb);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p*)(wb + 4 * 16));
       const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int mt = 0; mt < PJ_MT; ++mt) {
         if (mt >= mts) break;
-        const int n = nb + mt * 16 + lr;
-        const size_t xo = (size_t)n * p.sxn + (size_t)h * p.sxh + kk + lg * 8;
         if (!XF32) {
-          const u32x4 v = n < N ? *(const u32x4*)((const bf16_t*)p.X + xo) : u32x4{0, 0, 0, 0};
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), bv, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[ks][mt][0]), bv, acc[mt], 0, 0, 0);
         } else {
-          f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-          if (n < N) {
-            a = *(const f32x4*)((const float*)p.X + xo);
-            b = *(const f32x4*)((const float*)p.X + xo + 4);
-          }
           u32x4 vh, vl;
-          split_hi_lo(a, b, vh, vl);
+          split_hi_lo(__builtin_bit_cast(f32x4, xr[ks][mt][0]), __builtin_bit_cast(f32x4, xr[ks][mt][XV - 1]), vh, vl);
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vh), bv, acc[mt], 0, 0, 0);
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vl), bv, acc[mt], 0, 0, 0);
         }
       }
     }
-    // merge the four k ranges: waves 1..3 hand their sums to wave 0
+    // merge the k ranges: waves 1..NW-1 hand their sums to wave 0
     if (w > 0) {
 #pragma unroll
       for (int mt = 0; mt < PJ_MT; ++mt)
-        if (mt < mts) part[w - 1][mt][lane] = acc[mt];
+        if (mt < mts) part[((w - 1) * PJ_MT + mt) * 64 + lane] = acc[mt];
     }
     __syncthreads();
     if (w == 0) {
 #pragma unroll
       for (int mt = 0; mt < PJ_MT; ++mt) {
         if (mt >= mts) break;
-        const f32x4 v = acc[mt] + part[0][mt][lane] + part[1][mt][lane] + part[2][mt][lane];
+        f32x4 v = acc[mt];
+        for (int j = 0; j < NW - 1; ++j) v += part[(j * PJ_MT + mt) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = nb + mt * 16 + lg * 4 + i;
@@ -130,26 +153,30 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjParams p) {
     ((uint16_t*)p.Y)[idx] = (uint16_t)f32_to_bf16_bits(acc);
 }
 
+template <bool XF32, bool YF32>
+static hipError_t launch_proj_mfma(const ProjParams& p, hipStream_t st) {
+  const int nw = p.K / 32 < PJ_NW ? p.K / 32 : PJ_NW;
+  const size_t lds = (size_t)p.K * 32 + (size_t)(nw - 1) * pj_mt<XF32>() * 64 * sizeof(f32x4);
+  static bool attr_set = false;  // raise the dynamic-LDS limit once (max use 32 KB + 57 KB)
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)proj_mfma_kernel<XF32, YF32>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((proj_mfma_kernel<XF32, YF32>), dim3(p.M / 16, p.H), dim3(nw * 64), lds, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
-  const bool mfma = p.aligned16 && !p.w_f32 && p.K % 128 == 0 && p.K <= 1024 && p.M % 16 == 0 &&
+  const bool mfma = p.aligned16 && !p.w_f32 && p.K % 32 == 0 && p.K <= 1024 && p.M % 16 == 0 &&
                     (p.sxn % 8 == 0) && (p.sxh % 8 == 0);
   if (mfma) {
-    const dim3 grid(p.M / 16, p.H);
-    if (p.x_f32) {
-      if (p.y_f32)
-        hipLaunchKernelGGL((proj_mfma_kernel<true, true>), grid, dim3(PJ_NT), 0, st, p);
-      else
-        hipLaunchKernelGGL((proj_mfma_kernel<true, false>), grid, dim3(PJ_NT), 0, st, p);
-    } else {
-      if (p.y_f32)
-        hipLaunchKernelGGL((proj_mfma_kernel<false, true>), grid, dim3(PJ_NT), 0, st, p);
-      else
-        hipLaunchKernelGGL((proj_mfma_kernel<false, false>), grid, dim3(PJ_NT), 0, st, p);
-    }
-  } else {
-    const size_t total = (size_t)p.N * p.H * p.M;
-    hipLaunchKernelGGL(proj_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p);
+    if (p.x_f32) return p.y_f32 ? launch_proj_mfma<true, true>(p, st) : launch_proj_mfma<true, false>(p, st);
+    return p.y_f32 ? launch_proj_mfma<false, true>(p, st) : launch_proj_mfma<false, false>(p, st);
   }
+  const size_t total = (size_t)p.N * p.H * p.M;
+  hipLaunchKernelGGL(proj_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -281,3 +281,23 @@ def test_pipeline_vs_unabsorbed_oracle(mla, name, lens, H):
     e = norm_err(out, ref)
     print(f"  pipeline err {e:.3e}", flush=True)
     assert e <= 4e-3
+
+
+def test_graph_replays_match_eager(mla):
+    """The whole step captured in a HIP graph: every replay (with eager work and a sync in
+    between) reproduces the eager result bit for bit."""
+    cfg = CONFIGS["2"]
+    x = make_inputs(cfg, 70, lens=[300, 1500], H=16)
+    t = to_device(x)
+    _say("graph replay")
+    step = mla.DecodeStep(t["w_uk"], t["w_uv"], desc_of(cfg), 2, 1, 1500, cfg.sm_scale, num_splits=4)
+    eager = step.run(t["q_nope"], t["q_rope"], t["pool"], t["block_table"], t["seq_lens"]).clone()
+    g = step.capture(t["q_nope"], t["q_rope"], t["pool"], t["block_table"], t["seq_lens"])
+    for k in range(4):
+        step.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out.view_as(eager), eager), k
+        junk = torch.randn(1 << 20, device=dev()).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
