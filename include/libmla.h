@@ -128,7 +128,9 @@ typedef struct mla_decode_args {
   int32_t s_q;                /* 1 or 2 */
   int32_t num_heads;
   float sm_scale;             /* score scale, e.g. 1/sqrt(d_n + d_r) */
-  int32_t num_splits;         /* context partitions per longest sequence; 0 = automatic */
+  int32_t num_splits;         /* fewer than 96 rows (s_q * H): context partitions per longest
+                                 sequence; 96 or more rows: num_splits * batch block ranges.
+                                 0 = automatic */
   void* o_lat;                /* [batch][s_q][H][d_c] of o_dtype */
   int32_t o_dtype;            /* MLA_F32 or MLA_BF16 */
   float* lse;                 /* [batch][s_q][H] natural-log LSE, or NULL */
@@ -136,12 +138,17 @@ typedef struct mla_decode_args {
   size_t workspace_bytes;
 } mla_decode_args;
 
-/* Workspace needed by mla_decode_paged for these arguments (0 when no split is used). */
+/* Workspace needed by mla_decode_paged for these arguments (0 when no split is used).
+ * Device memory, 256-byte aligned, owned by the caller; its contents need no initialisation
+ * and are scratch between calls (calls that overlap on one workspace race). */
 int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes);
 
-/* The split plan mla_decode_paged will use: partitions of the longest sequence and
- * 64-token tiles per partition.  num_cus = compute units to plan for (0 = query the
- * current device).  Pure host logic. */
+/* The work split mla_decode_paged will use.  Fewer than 96 query rows per sequence
+ * (s_q * num_heads): *num_splits partitions of the longest sequence of *tiles_per_split
+ * 64-token blocks each.  96 rows or more: the batch's blocks, sequence after sequence, cut
+ * into *num_splits equal ranges (one workgroup per range and 128-row group) of at most
+ * *tiles_per_split blocks.  num_cus = compute units to plan for (0 = query the current
+ * device).  Pure host logic. */
 int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* num_splits,
                         int32_t* tiles_per_split);
 
@@ -154,8 +161,9 @@ int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* n
  *   kernel for INT4/INT2 caches.  Cache slots past L_b in a sequence's last block are
  *   never used.  Long contexts are split into partitions whose partial (o, lse) are
  *   merged by a log-sum-exp combine; the result is deterministic for fixed arguments.
- *   Block-table entries outside [0, num_blocks) are not dereferenced (their tokens
- *   read as zeros); seq_lens above max_seq_len are clamped to it.
+ *   Block-table entries outside [0, num_blocks) are not dereferenced: their tokens take
+ *   no part in the softmax.  seq_lens above max_seq_len are clamped to it; a sequence of
+ *   length 0 gets o_lat = 0 and lse = -inf.
  *   Kernels: bf16 MFMA for BF16/INT4/INT2 caches with d_c = 512, d_r = 64; a plain
  *   fp32 kernel for F32 caches (d_c <= 1024, d_r <= 256).
  */

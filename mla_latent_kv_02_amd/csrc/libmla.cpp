@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -87,15 +88,34 @@ int32_t validate_decode(const mla_decode_args* a, Layout* lay) {
 }
 
 struct Plan {
-  int rt;          // row tiles per workgroup (MFMA kernel), 0 = fp32 kernel
+  bool rows;       // row-owner kernel over balanced block ranges
+  int rt;          // row tiles per workgroup (partition MFMA kernel), 0 = fp32 kernel
   int rg;          // row groups per sequence
-  int splits;      // partitions of the longest sequence
-  int tpc;         // 64-token tiles per partition
+  int splits;      // partitions of the longest sequence, or block ranges (rows)
+  int tpc;         // 64-token tiles per partition, or an upper bound of blocks per range (rows)
 };
+
+constexpr int kRowsMinRows = 96;        // query rows per sequence from which the row-owner kernel runs
+constexpr int kRowsPerGroup = 128;      // its rows per workgroup
+constexpr int kRowsMaxBatch = 8192;     // sequences it tabulates in LDS
+constexpr int kRowsMaxRangeBlocks = 256;
 
 Plan make_plan(const mla_decode_args* a, int cus) {
   Plan p{};
   const int R = a->s_q * a->num_heads;
+  if (a->cache.latent_fmt != MLA_FMT_F32 && R >= kRowsMinRows && a->batch <= kRowsMaxBatch) {
+    // the batch's blocks, sequence after sequence, cut into equal ranges: one workgroup per
+    // (range, row group), a single round over the CUs unless the ranges would get too long
+    p.rows = true;
+    p.rg = (int)ceil_div(R, kRowsPerGroup);
+    const int64_t bound = (int64_t)a->batch * ceil_div(a->max_seq_len, kBlock);  // blocks, at most
+    int64_t n = a->num_splits > 0 ? (int64_t)a->num_splits * a->batch : std::max<int64_t>(1, cus / p.rg);
+    n = std::max<int64_t>(n, ceil_div(bound, kRowsMaxRangeBlocks));
+    n = std::min<int64_t>(n, bound);
+    p.splits = (int)n;
+    p.tpc = (int)ceil_div(bound, n);
+    return p;
+  }
   int64_t target;  // workgroups to aim for
   if (a->cache.latent_fmt == MLA_FMT_F32) {
     p.rt = 0;
@@ -141,7 +161,18 @@ int32_t device_cus(int* cus) {
   return MLA_OK;
 }
 
+// Workspace layout.  Row-owner kernel: meta [B + 2] int32, then partial o and lse of the
+// slots b + i (B + ranges - 1 of them).  Partition kernels: partial o, then lse.
+size_t rows_meta_bytes(const mla_decode_args* a) { return (size_t)align_up(((int64_t)a->batch + 2) * 4, 256); }
+
 size_t partial_bytes(const mla_decode_args* a, const Plan& p, size_t* lse_off) {
+  if (p.rows) {
+    const int64_t slots = (int64_t)a->batch + p.splits - 1;
+    const int64_t rows = slots * a->s_q * a->num_heads;
+    const int64_t o_bytes = align_up(rows * a->cache.d_c * 4, 256);
+    *lse_off = rows_meta_bytes(a) + (size_t)o_bytes;
+    return *lse_off + (size_t)align_up(rows * 4, 256);
+  }
   if (p.splits <= 1) {
     *lse_off = 0;
     return 0;
@@ -269,6 +300,62 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need || !aligned(a->workspace, 256)))
     return MLA_ERR_WORKSPACE;
 
+  hipStream_t st = (hipStream_t)stream;
+  if (plan.rows) {
+    mla::RowsParams r{};
+    r.q_lat = a->q_lat;
+    r.q_rope = a->q_rope;
+    r.q_f32 = a->q_dtype == MLA_F32;
+    r.pool = (const uint8_t*)a->cache_pool;
+    r.num_blocks = a->num_blocks;
+    r.block_bytes = lay.block_bytes;
+    r.off_lc = lay.off[0];
+    r.off_ls = lay.off[1];
+    r.off_rc = lay.off[2];
+    r.off_rs = lay.off[3];
+    r.g_lat = a->cache.latent_group > 0 ? a->cache.latent_group : 1;
+    r.g_rope = a->cache.rope_group > 0 ? a->cache.rope_group : 1;
+    r.block_table = a->block_table;
+    r.bt_stride = a->block_table_stride;
+    r.seq_lens = a->seq_lens;
+    r.max_seq_len = a->max_seq_len;
+    r.B = a->batch;
+    r.s_q = a->s_q;
+    r.H = a->num_heads;
+    r.R = a->s_q * a->num_heads;
+    r.RG = plan.rg;
+    r.n_ranges = plan.splits;
+    const int64_t units = (int64_t)plan.splits * plan.rg;
+    if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+    r.total_units = (int)units;
+    r.units_per_xcd = (int)ceil_div(units, 8);
+    r.scale_log2 = a->sm_scale * 1.4426950408889634f;
+    r.out = a->o_lat;
+    r.out_bf16 = a->o_dtype == MLA_BF16;
+    r.out_lse = a->lse;
+    r.meta = (int32_t*)a->workspace;
+    r.part_o = (float*)((char*)a->workspace + rows_meta_bytes(a));
+    r.part_lse = (float*)((char*)a->workspace + lse_off);
+    hipError_t e = mla::launch_decode_rows(r, a->cache.latent_fmt, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    if (plan.splits > 1) {
+      mla::CombineParams c{};
+      c.part_o = r.part_o;
+      c.part_lse = r.part_lse;
+      c.seq_lens = a->seq_lens;
+      c.max_seq_len = a->max_seq_len;
+      c.R = r.R;
+      c.d_c = a->cache.d_c;
+      c.meta = r.meta;
+      c.out = a->o_lat;
+      c.out_bf16 = a->o_dtype == MLA_BF16;
+      c.out_lse = a->lse;
+      e = mla::launch_combine(c, a->batch, st);
+      if (e != hipSuccess) return MLA_ERR_HIP;
+    }
+    return MLA_OK;
+  }
+
   mla::DecodeParams p{};
   p.q_lat = a->q_lat;
   p.q_rope = a->q_rope;
@@ -307,7 +394,6 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.total_units = (int)units;
   p.units_per_xcd = (int)ceil_div(units, 8);
 
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e = plan.rt == 0 ? mla::launch_decode_f32(p, st) : mla::launch_decode_mfma(p, a->cache.latent_fmt, plan.rt, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (split) {

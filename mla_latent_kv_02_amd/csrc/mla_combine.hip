@@ -104,13 +104,24 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   const int tid = threadIdx.x;
   const int R = p.R;
   const int b = blockIdx.x / R, r = blockIdx.x % R;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
-  int nch = (nblk + p.tpc - 1) / p.tpc;
-  nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
-  const size_t u0 = (size_t)b * p.max_chunks;
   const float NEG_INF = -__builtin_inff();
+  int nch;
+  size_t u0;
+  if (p.meta == nullptr) {
+    int L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    nch = (nblk + p.tpc - 1) / p.tpc;
+    nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
+    u0 = (size_t)b * p.max_chunks;
+  } else {
+    const int per = p.meta[0], first = p.meta[1 + b], nblk = p.meta[2 + b] - first;
+    if (nblk <= 0) return;  // empty sequence: written by the decode kernel
+    const int i0 = first / per, i1 = (first + nblk - 1) / per;
+    if (i0 == i1) return;  // one range held the whole sequence and wrote its result
+    nch = i1 - i0 + 1;
+    u0 = (size_t)b + i0;
+  }
   // max of the partition LSEs
   float m = NEG_INF;
   for (int c = tid; c < nch; c += 128) m = fmaxf(m, p.part_lse[(u0 + c) * R + r]);

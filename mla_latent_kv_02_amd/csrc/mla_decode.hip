@@ -26,39 +26,26 @@
 // Partials (o, lse) of the partitions are merged by combine_kernel.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
+#include "mla_stage.hpp"
 
 namespace mla {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 constexpr int NT = 512;                // threads per workgroup (8 waves)
-constexpr int ST_TOK = 32;             // tokens per stage
-constexpr int ST_PIECES = ST_TOK * 72; // 16-byte pieces per bf16 stage
-constexpr int ST_ELEMS = ST_TOK * 576;
 constexpr int PROW = ST_TOK + 8;       // bf16 elements per LDS P row
 constexpr int MAX_TPC = 256;           // paged blocks per partition (host planner caps it)
 
-// s_waitcnt immediate: wait until at most n vector-memory operations are outstanding
-__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8); }
-
-// All LDS traffic of this wave is complete, then workgroup barrier.  The memory
-// clobber keeps the compiler from moving memory operations across it, without
-// the release fence that would also wait for the in-flight LDS DMA of later stages.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Stage layout: token row t holds its 72 pieces (8 bf16 each) in 9 groups of 8; piece c sits
-// at physical piece c ^ sw(t), an XOR inside its group.  Rows are 288 dwords apart (32 mod 64
-// banks).  gfx950 serves a 16-byte LDS access 16 lanes per cycle, a lane set being (lane bit 5,
-// parity of lane bits 2..4), and ds_read_b64_tr_b16 32 consecutive lanes per cycle.  sw() is
-// the XOR pattern under which all four access patterns of a stage fill 64 distinct banks per
-// cycle: the score operand reads (16 tokens x 4 consecutive pieces per wave), the transposed
-// P.C operand reads, and the dequantised latent and RoPE piece stores of the quantised formats.
-__device__ __forceinline__ int sw(int t) { return (t & 2) | ((t >> 1) & 4) | ((t >> 4) & 1); }
-// bf16 element offset of (token t, latent/rope column d) in a stage
-__device__ __forceinline__ int st_off(int t, int d) { return t * 576 + (((d >> 3) ^ sw(t)) << 3) + (d & 7); }
+// 16-byte LDS store written as inline asm.  The compiler's wait insertion cannot tell
+// which ring slot an LDS store touches once the ring loop's back edge merges its state,
+// and would otherwise wait for every DMA in flight (vmcnt(0)) before the store.  The store
+// only writes the bf16 stage, which no DMA targets; the next lds_barrier() waits for it.
+__device__ __forceinline__ void lds_store16(bf16_t* dst, const u32x4& v) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void*)dst;
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 
 __device__ __forceinline__ void dma16(const void* src, lds_void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -120,6 +107,7 @@ template <int FMT>
 struct QuantProducer {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
   static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
+  static constexpr int PPT = LB / 16;              // latent code pieces (16 B) per token
   // code stage capacity in 16-byte slots: INT4 waves 0-3 issue 2 instructions, waves 4-7 one
   static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;
   static constexpr int LOADS_HI = 1;
@@ -144,15 +132,12 @@ struct QuantProducer {
       int p = slot < n_all ? slot : slot - n_all;
       const uint8_t* src;
       if (p < n_lc) {
-        // latent code pieces are stored swizzled: slot t*PPT + (k ^ (t & 7)) holds piece k of token t
-        constexpr int PPT = LB / 16;
-        const int t = p / PPT;
-        const int k = (p % PPT) ^ (t & 7);
-        src = lc + (t * PPT + k) * 16;
+        // latent code pieces are stored piece-major: slot k * 32 + t holds piece k of token t
+        src = lc + ((p % ST_TOK) * PPT + p / ST_TOK) * 16;
       } else if ((p -= n_lc) < n_ls) {
         src = ls + p * 16;
       } else if ((p -= n_ls) < n_rc) {
-        src = rc + p * 16;
+        src = rc + ((p % ST_TOK) * 2 + p / ST_TOK) * 16;   // rope code halves, also piece-major
       } else {
         src = rs + (p - n_rc) * 16;
       }
@@ -160,61 +145,59 @@ struct QuantProducer {
     }
   }
 
-  // codes -> swizzled bf16 stage; tokens >= valid become zeros
-  __device__ __forceinline__ static void dequant(const uint8_t* cstage, int valid, int groups, int rgroups, bf16_t* stage, int tid) {
-    const int g_lat = 512 / groups;
-    const uint8_t* lc = cstage;
-    const uint32_t* ls = (const uint32_t*)(cstage + ST_TOK * LB);
-    const uint8_t* rc = cstage + ST_TOK * LB + ST_TOK * groups * 4;
-    const uint32_t* rs = (const uint32_t*)(rc + ST_TOK * 32);
-    constexpr int ELEMS = 128 / BITS;          // elements per 16-byte code piece
-    constexpr int PPT = LB / 16;               // latent pieces per token
-    constexpr int NLP = ST_TOK * PPT;          // latent pieces per stage
-    // Thread mapping: 8 consecutive lanes take 8 consecutive tokens and the same code piece k,
-    // so the swizzled code reads and the swizzled bf16 writes both spread over all banks.
-    for (int q = tid; q < NLP + 2 * ST_TOK; q += NT) {
-      if (q < NLP) {
-        const int g = q >> 3;
-        const int t = (q & 7) + 8 * (g & 3);
-        const int k = g >> 2;
-        const int e0 = k * ELEMS;
-        if (t >= valid) {
+  // Per-thread dequantisation work, fixed for the whole partition.  Thread q owns latent
+  // chunk kk = q / 32 (32 elements, inside one quantisation group since groups are multiples
+  // of 32) of token t = q mod 32: a wavefront's code reads are contiguous and its swizzled
+  // bf16 stores spread over all banks.  Threads 0..255 also own 8 RoPE elements
+  // (token rt, elements 8 ri .. 8 ri + 7).
+  struct Work {
+    int t, code, sz, dst;       // latent: token, code byte offset, scale byte offset, stage element
+    int rt, rcode, rsz, rdst;   // rope (tid < 256)
+  };
+  __device__ __forceinline__ static Work plan(int groups, int rgroups, int tid) {
+    Work w;
+    w.t = tid & 31;
+    const int kk = tid >> 5;                      // 0..15
+    const int cpiece = (kk * 32 * BITS) / 128;    // 16-byte code piece holding the chunk
+    const int cbyte = ((kk * 32 * BITS) / 8) & 15;
+    w.code = (cpiece * ST_TOK + w.t) * 16 + cbyte;
+    w.sz = ST_TOK * LB + (w.t * groups + (kk * 32) / (512 / groups)) * 4;
+    w.dst = st_off(w.t, kk * 32);
+    w.rt = tid & 31;
+    const int ri = (tid >> 5) & 7;
+    w.rcode = ST_TOK * LB + ST_TOK * groups * 4 + ((ri >> 2) * ST_TOK + w.rt) * 16 + (ri & 3) * 4;
+    w.rsz = ST_TOK * LB + ST_TOK * groups * 4 + ST_TOK * 32 + (w.rt * rgroups + (ri * 8) / (64 / rgroups)) * 4;
+    w.rdst = st_off(w.rt, 512 + ri * 8);
+    return w;
+  }
+
+  // codes -> swizzled bf16 stage; tokens >= valid become zeros (scale and zero-point 0)
+  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, const Work& w, bf16_t* stage,
+                                                 int tid) {
+    uint32_t sz = *(const uint32_t*)(cst + w.sz);
+    sz = w.t < valid ? sz : 0u;
+    float s, zs;
+    scale_zero(sz, s, zs);
+    // element 32 kk + 8 j sits at physical piece (4 kk + j) ^ sw(t) = (base piece) ^ j
+    const int row = w.t * 576;
+    const int p0 = (w.dst - row) >> 3;
+    if constexpr (BITS == 4) {
+      const u32x4 c = *(const u32x4*)(cst + w.code);
 #pragma unroll
-          for (int j = 0; j < ELEMS / 8; ++j) *(u32x4*)&stage[st_off(t, e0 + 8 * j)] = u32x4{0, 0, 0, 0};
-          continue;
-        }
-        const u32x4 c = *(const u32x4*)(lc + (t * PPT + (k ^ (t & 7))) * 16);
-        float s0, zs0, s1, zs1;
-        scale_zero(ls[t * groups + e0 / g_lat], s0, zs0);
-        scale_zero(ls[t * groups + (e0 + ELEMS / 2) / g_lat], s1, zs1);
-        if (BITS == 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *(u32x4*)&stage[st_off(t, e0 + 8 * j)] = dequant_int4x8(c[j], j < 2 ? s0 : s1, j < 2 ? zs0 : zs1);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float s = j < 2 ? s0 : s1, zs = j < 2 ? zs0 : zs1;
-            *(u32x4*)&stage[st_off(t, e0 + 16 * j)] = dequant_int2x8(c[j] & 0xFFFFu, s, zs);
-            *(u32x4*)&stage[st_off(t, e0 + 16 * j + 8)] = dequant_int2x8(c[j] >> 16, s, zs);
-          }
-        }
-      } else {
-        const int r = q - NLP;
-        const int t = r & 31;
-        const int hr = r >> 5;
-        const int e0 = 512 + hr * 32;
-        if (t >= valid) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) *(u32x4*)&stage[st_off(t, e0 + 8 * j)] = u32x4{0, 0, 0, 0};
-          continue;
-        }
-        const u32x4 c = *(const u32x4*)(rc + (t * 2 + hr) * 16);
-        float s, zs;
-        scale_zero(rs[t * rgroups + (hr * 32) / (64 / rgroups)], s, zs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4*)&stage[st_off(t, e0 + 8 * j)] = dequant_int4x8(c[j], s, zs);
-      }
+      for (int j = 0; j < 4; ++j) lds_store16(&stage[row + ((p0 ^ j) << 3)], dequant_int4x8(c[j], s, zs));
+    } else {
+      const uint2 c = *(const uint2*)(cst + w.code);
+      lds_store16(&stage[row + ((p0 ^ 0) << 3)], dequant_int2x8(c.x & 0xFFFFu, s, zs));
+      lds_store16(&stage[row + ((p0 ^ 1) << 3)], dequant_int2x8(c.x >> 16, s, zs));
+      lds_store16(&stage[row + ((p0 ^ 2) << 3)], dequant_int2x8(c.y & 0xFFFFu, s, zs));
+      lds_store16(&stage[row + ((p0 ^ 3) << 3)], dequant_int2x8(c.y >> 16, s, zs));
+    }
+    if (tid < 256) {
+      uint32_t rsz = *(const uint32_t*)(cst + w.rsz);
+      rsz = w.rt < valid ? rsz : 0u;
+      float rsc, rzs;
+      scale_zero(rsz, rsc, rzs);
+      lds_store16(&stage[w.rdst], dequant_int4x8(*(const uint32_t*)(cst + w.rcode), rsc, rzs));
     }
   }
 };
@@ -235,18 +218,26 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   using QP = QuantProducer<FMT == FMT_BF16 ? FMT_INT4 : FMT>;
   constexpr int CBYTES = QUANT ? QP::SLOTS * 16 : 16;
 
-  // bf16 path: 4 bf16 stages.  quantised path: 4 code stages + 2 bf16 stages.
+  // bf16 path: a 4-deep ring of bf16 stages.  Quantised path: an 8-deep ring of code stages
+  // and one bf16 stage that every step dequantises into.  Distinct arrays let the compiler
+  // see that reading one ring slot does not depend on the DMA into another.
+  constexpr int DEPTH = QUANT ? 8 : 4;
   __shared__ __attribute__((aligned(16))) bf16_t S0[ST_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t S1[ST_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t S1[QUANT ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t S2[QUANT ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t S3[QUANT ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t C0[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C1[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C2[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C3[CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C4[CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C5[CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C6[CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C7[CBYTES];
   __shared__ __attribute__((aligned(16))) bf16_t Ps[ROWS * PROW];
   __shared__ float red[2][ROWS];
-  __shared__ float redl[2][ROWS];
+  __shared__ float redl[2][ROWS];   // row sums of the bf16-rounded P (normalise o)
+  __shared__ float redx[2][ROWS];   // row sums of the unrounded P (lse)
   __shared__ float mfin[ROWS];
   __shared__ __attribute__((aligned(16))) float alpha[ROWS];
   __shared__ int bids[MAX_TPC];
@@ -292,7 +283,7 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   }
 
   const float NEG_INF = -__builtin_inff();
-  float m_s = NEG_INF, l_s = 0.f;
+  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
   f32x4 acc[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -330,37 +321,57 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
     else
       Prod::issue(blk + half * ST_TOK * 1152, valid, st, tid);
   };
-  // wait until stage s has landed, given how many later stages were issued after it
+  // wait until a stage has landed, given how many later stages were issued after it
+  // (each loader wave issues a fixed number of DMA instructions per stage)
   auto wait_stage = [&](int later) {
     constexpr int LA = QUANT ? QP::LOADS_LO : Producer<FMT_BF16>::LOADS_LO;
     constexpr int LB = QUANT ? QP::LOADS_HI : Producer<FMT_BF16>::LOADS_HI;
-    if (w < 4) {
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LA));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LA));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else {
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LB));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LB));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int n = w < 4 ? LA : LB;
+    auto wait_n = [&](auto K) {
+      if (n == LA) __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * LA));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * LB));
+    };
+    switch (later) {
+      case 0: wait_n(std::integral_constant<int, 0>{}); break;
+      case 1: wait_n(std::integral_constant<int, 1>{}); break;
+      case 2: wait_n(std::integral_constant<int, 2>{}); break;
+      case 3: wait_n(std::integral_constant<int, 3>{}); break;
+      case 4: wait_n(std::integral_constant<int, 4>{}); break;
+      case 5: wait_n(std::integral_constant<int, 5>{}); break;
+      default: wait_n(std::integral_constant<int, 6>{}); break;
     }
   };
+  static_assert(DEPTH - 2 <= 6, "wait_stage covers at most 6 later stages");
 
-  // prologue: stages 0, 1, 2 in flight; stage 0 landed
-  if (0 < nst) issue(0, S0, C0);
-  if (1 < nst) issue(1, S1, C1);
-  if (2 < nst) issue(2, QUANT ? S0 : S2, C2);
-  wait_stage(min(nst - 1, 2));
+  const typename QP::Work dq = QP::plan(groups, rgroups, tid);
+
+  // prologue: stages 0 .. DEPTH-2 in flight; stage 0 landed
+  if constexpr (QUANT) {
+    if (0 < nst) issue(0, S0, C0);
+    if (1 < nst) issue(1, S0, C1);
+    if (2 < nst) issue(2, S0, C2);
+    if (3 < nst) issue(3, S0, C3);
+    if (4 < nst) issue(4, S0, C4);
+    if (5 < nst) issue(5, S0, C5);
+    if (6 < nst) issue(6, S0, C6);
+  } else {
+    if (0 < nst) issue(0, S0, C0);
+    if (1 < nst) issue(1, S1, C0);
+    if (2 < nst) issue(2, S2, C0);
+  }
+  wait_stage(min(nst - 1, DEPTH - 2));
   lds_barrier();
 
-  // one stage: KS = bf16 stage read by the MFMAs, NXT/CNXT = ring slot refilled with stage s+3
+  // one stage: KS = bf16 stage read by the MFMAs, CCUR = its code stage (quantised formats),
+  // NXT/CNXT = ring slot refilled with stage s + DEPTH - 1
   auto step = [&](int s, bf16_t* KS, uint8_t* CCUR, bf16_t* NXT, uint8_t* CNXT) {
     // stage s has landed and every wave is done with stage s-1 (barrier at the end of the
-    // previous step), so the ring slot of stage s-1 can take stage s+3
-    if (s + 3 < nst) issue(s + 3, NXT, CNXT);
+    // previous step), so the ring slot of stage s-1 can take stage s + DEPTH - 1
+    if (s + DEPTH - 1 < nst) issue(s + DEPTH - 1, NXT, CNXT);
     int half_unused, valid;
     stage_src(s, half_unused, valid);
     if constexpr (QUANT) {
-      Prod::dequant(CCUR, valid, groups, rgroups, KS, tid);
+      QP::dequant(CCUR, valid, dq, KS, tid);
       lds_barrier();
     } else if (valid < ST_TOK) {
       // rows past the sequence end were filled from a dummy address: zero them
@@ -396,7 +407,9 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       const int tok0 = T0 + s * ST_TOK + sc_tt * 16 + lg * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = tok0 + i <= lim_s ? sv[i] * p.scale_log2 : NEG_INF;
+        // tokens past the causal limit, and tokens of an out-of-range block (valid = 0), are skipped
+        const bool ok = tok0 + i <= lim_s && sc_tt * 16 + lg * 4 + i < valid;
+        const float x = ok ? sv[i] * p.scale_log2 : NEG_INF;
         sv[i] = x;
         mx = fmaxf(mx, x);
       }
@@ -408,17 +421,25 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
     // ---- running max, P for the scored tile; the scorers of token tile 0 publish the
     // rescale factor of their rows, every wave then rescales the output rows it owns
     if (scorer) {
-      const float mn = fmaxf(m_s, fmaxf(red[0][row_s], red[1][row_s]));
+      // The reference maximum m only moves when the stage maximum exceeds it by more than
+      // RESCALE_SLACK (log2 units), so P = exp2(x - m) stays below 2^RESCALE_SLACK and the
+      // accumulators are rescaled only on such a move, rare after a partition's first stages.
+      // The final division by the row sum cancels the choice of m.
+      const float mt = fmaxf(red[0][row_s], red[1][row_s]);
+      const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
       const float mu = mn == NEG_INF ? 0.f : mn;
-      const float al = __builtin_amdgcn_exp2f(m_s - mu);
+      const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
       l_s *= al;
+      l_x *= al;
       m_s = mn;
       if (sc_tt == 0 && lg == 0) alpha[row_s] = al;
       uint32_t pb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pb[i] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sv[i] - mu));
+        const float pf = __builtin_amdgcn_exp2f(sv[i] - mu);
+        pb[i] = f32_to_bf16_bits(pf);
         l_s += bf16_bits_to_f32(pb[i]);
+        l_x += pf;
       }
       *(uint2*)&Ps[row_s * PROW + sc_tt * 16 + lg * 4] = uint2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
     }
@@ -457,7 +478,7 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       }
     }
     // stage s+1 landed, and nobody reads stage s any more
-    wait_stage(min(nst - 2 - s, 2));
+    wait_stage(min(nst - 2 - s, DEPTH - 2));
     lds_barrier();
   };
 
@@ -469,19 +490,25 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       if (s + 3 < nst) step(s + 3, S3, C3, S2, C2);
     }
   } else {
-    for (int s = 0; s < nst; s += 4) {
-      step(s, S0, C0, S0, C3);
-      if (s + 1 < nst) step(s + 1, S1, C1, S0, C0);
+    for (int s = 0; s < nst; s += 8) {
+      step(s, S0, C0, S0, C7);
+      if (s + 1 < nst) step(s + 1, S0, C1, S0, C0);
       if (s + 2 < nst) step(s + 2, S0, C2, S0, C1);
-      if (s + 3 < nst) step(s + 3, S1, C3, S0, C2);
+      if (s + 3 < nst) step(s + 3, S0, C3, S0, C2);
+      if (s + 4 < nst) step(s + 4, S0, C4, S0, C3);
+      if (s + 5 < nst) step(s + 5, S0, C5, S0, C4);
+      if (s + 6 < nst) step(s + 6, S0, C6, S0, C5);
+      if (s + 7 < nst) step(s + 7, S0, C7, S0, C6);
     }
   }
 
   // ---- finish: row sums over lanes and token tiles, normalise, write
   if (scorer) {
     l_s = wave_sum_16_32(l_s);
+    l_x = wave_sum_16_32(l_x);
     if (lg == 0) {
       redl[sc_tt][row_s] = l_s;
+      redx[sc_tt][row_s] = l_x;
       if (sc_tt == 0) mfin[row_s] = m_s;
     }
   }
@@ -510,7 +537,7 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
     }
   }
   if (p.out_lse != nullptr && tid < ROWS && r0 + tid < R) {
-    const float lt = redl[0][tid] + redl[1][tid];
+    const float lt = redx[0][tid] + redx[1][tid];
     p.out_lse[unit_row0 + r0 + tid] = lt > 0.f ? (mfin[tid] + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
   }
 }

@@ -1,0 +1,617 @@
+// MLA decode for many query rows per sequence (H * s_q >= 96, e.g. 128 heads): the absorbed-MQA
+// attention step with each wavefront owning whole query rows (gfx950).
+//
+// Every head scores the same cached rows [c (512) | k_rope (64)] (GQLA abstract: absorbed MQA
+// decoding path), the softmax-weighted sum is taken over the latent itself (RAQ-MLA abstract:
+// the latent supplies the values), and INT4/INT2 caches are unpacked and dequantised inside
+// the loop (QuantMLA English abstract: native low-bit attention kernel).
+//
+// Workgroup = 4 wavefronts (one per SIMD, up to 512 registers each) and 128 query rows; wave
+// w owns rows 32w .. 32w+31 end to end:
+//   * scores S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K fragments from the LDS stage, Q^T
+//     for both 16-row tiles held in registers; each K fragment feeds two MFMAs;
+//   * softmax in registers: the 32 scores of a row sit in 4 lane groups, so a row maximum is
+//     two cross-lane steps; the running maximum moves only when a stage exceeds it by more
+//     than RESCALE_SLACK (log2 units), so rescaling the accumulators is rare;
+//   * O^T += V^T . P^T: the score accumulators are already the P^T operand once the token
+//     order inside the 32-token step is taken as (4 tokens of tile 0, 4 of tile 1) per lane
+//     group, and V^T fragments come from the token-major stage with ds_read_b64_tr_b16 in the
+//     same order; each V^T fragment feeds two MFMAs; O^T (32 rows x 512) stays in AGPRs.
+// There is no cross-wave dependency inside a step: one barrier per 32-token stage guards the
+// ring of LDS stages.
+//
+// Stages stream HBM -> LDS with global_load_lds_dwordx4 (bf16: a 4-deep ring, three stages
+// in flight; INT4/INT2: a ring of code stages, dequantised one step ahead into a second bf16
+// stage).  The DMA is written as inline asm: the compiler then never inserts waits for it,
+// and each step waits with an explicit vmcnt for exactly the stage it needs.
+//
+// Work balance: the batch's cache blocks, sequence after sequence, are cut into n_ranges equal
+// ranges (one workgroup per range and row group); a range may cover several sequences, and a
+// sequence cut by range boundaries leaves partials that combine_kernel merges.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "mla_device.hpp"
+#include "mla_internal.hpp"
+#include "mla_stage.hpp"
+
+namespace mla {
+namespace rows {
+
+constexpr int NT = 512;                  // 8 wavefronts, two per SIMD
+constexpr int ROWS = 128;                // query rows per workgroup
+constexpr int MAX_RANGE_BLOCKS = 256;    // cache blocks per range (host planner guarantees it)
+constexpr int MAX_ST = 2 * MAX_RANGE_BLOCKS;
+constexpr int ST_BYTES = ST_ELEMS * 2;   // one bf16 stage
+
+// 16 bytes per lane HBM -> LDS; lane i writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).
+// One wait state between the M0 write and the DMA that reads it.
+// The kernel makes no other use of M0.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(src)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
+__device__ __forceinline__ bf16x8 load_q8(const void* base, size_t elem_off, bool f32) {
+  if (!f32) return __builtin_bit_cast(bf16x8, *(const u32x4*)((const bf16_t*)base + elem_off));
+  const float* f = (const float*)base + elem_off;
+  const f32x4 a = *(const f32x4*)f;
+  const f32x4 b = *(const f32x4*)(f + 4);
+  u32x4 r;
+  r[0] = pack_bf16x2(a[0], a[1]);
+  r[1] = pack_bf16x2(a[2], a[3]);
+  r[2] = pack_bf16x2(b[0], b[1]);
+  r[3] = pack_bf16x2(b[2], b[3]);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// ----------------------------------------------------------------------------------------
+// Stage producers: every wave issues a fixed number of DMA instructions per stage, so its
+// count of outstanding stage loads is known exactly.
+// ----------------------------------------------------------------------------------------
+
+// bf16 rows: a half block is 32 tokens x 72 pieces = 2304 pieces; waves 0-3 issue 5 DMA
+// instructions, waves 4-7 issue 4.  Slot k of the stage receives (token k / 72, logical piece
+// (k mod 72) ^ sw(token)); tokens >= valid read the half block's first piece instead (and are
+// zeroed before use).
+struct BfProducer {
+  static constexpr int LOADS_LO = 5, LOADS_HI = 4;
+  __device__ __forceinline__ static void issue(const uint8_t* half, int valid, uint32_t stage, int tid) {
+    // recomputed per stage: keeping the per-slot offsets live across the loop costs registers
+    asm volatile("" : "+v"(tid));
+    const int wbase = tid & ~63;
+#pragma unroll
+    for (int i = 0; i < LOADS_LO; ++i) {
+      if (i == LOADS_HI && tid >= 256) break;
+      const int slot = i * NT + tid;
+      const int t = slot / 72;
+      const int c = (slot - t * 72) ^ sw(t);
+      const uint8_t* src = t < valid ? half + t * 1152 + c * 16 : half;
+      dma16(src, stage + (uint32_t)(i * NT + wbase) * 16);
+    }
+  }
+};
+
+// Quantised latent (INT4 or INT2) + INT4 rope: the four code planes of a half block are copied
+// into a code stage [lc | ls | rc | rs] of SLOTS 16-byte slots; latent and rope code pieces are
+// stored piece-major (slot k * 32 + t holds piece k of token t), scale planes as they are.
+template <int FMT>
+struct QuantStage {
+  static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
+  static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
+  static constexpr int PPT = LB / 16;              // latent code pieces per token
+  // waves 0-3 issue LOADS_LO DMA instructions per stage, waves 4-7 LOADS_HI
+  static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;
+  static constexpr int LOADS_HI = 1;
+  static constexpr int SLOTS = FMT == FMT_INT4 ? 768 : 512;   // INT4: 648 used, INT2: 456
+  static constexpr int DEPTH = FMT == FMT_INT4 ? 6 : 8;   // code ring slots
+
+  __device__ __forceinline__ static void issue(const uint8_t* blk, int half, const QuantPlanes& pl, int groups,
+                                               int rgroups, uint32_t cstage, int tid) {
+    asm volatile("" : "+v"(tid));   // recomputed per stage, as for bf16 stages
+    const int n_lc = ST_TOK * LB / 16;
+    const int n_ls = ST_TOK * groups * 4 / 16;
+    const int n_rc = ST_TOK * 32 / 16;
+    const int n_rs = (ST_TOK * rgroups * 4 + 15) / 16;
+    const int n_all = n_lc + n_ls + n_rc + n_rs;
+    const uint8_t* lc = blk + pl.lc + half * ST_TOK * LB;
+    const uint8_t* ls = blk + pl.ls + half * ST_TOK * groups * 4;
+    const uint8_t* rc = blk + pl.rc + half * ST_TOK * 32;
+    const uint8_t* rs = blk + pl.rs + half * ST_TOK * rgroups * 4;
+    const int wbase = tid & ~63;
+#pragma unroll
+    for (int i = 0; i < LOADS_LO; ++i) {
+      if (i == LOADS_HI && tid >= 256) break;
+      const int slot = i * NT + tid;
+      int p = slot < n_all ? slot : slot - n_all;   // padding slots re-load a real piece
+      const uint8_t* src;
+      if (p < n_lc) {
+        src = lc + ((p % ST_TOK) * PPT + p / ST_TOK) * 16;
+      } else if ((p -= n_lc) < n_ls) {
+        src = ls + p * 16;
+      } else if ((p -= n_ls) < n_rc) {
+        src = rc + ((p % ST_TOK) * 2 + p / ST_TOK) * 16;
+      } else {
+        src = rs + (p - n_rc) * 16;
+      }
+      dma16(src, cstage + (uint32_t)(i * NT + wbase) * 16);
+    }
+  }
+
+  // Thread q dequantises latent chunk kk = q / 32 (32 elements, inside one quantisation group
+  // since groups are multiples of 32) of token t = q mod 32; threads q < 256 also dequantise
+  // RoPE elements 8 ri .. 8 ri + 7 (ri = q / 32) of token t.  Offsets are fixed per thread.
+  struct Work {
+    int t, code, sz, rcode, rsz;
+  };
+  __device__ __forceinline__ static Work plan(int groups, int rgroups, int tid) {
+    Work w;
+    w.t = tid & 31;
+    const int kk = tid >> 5;
+    const int cpiece = (kk * 32 * BITS) / 128, cbyte = ((kk * 32 * BITS) / 8) & 15;
+    w.code = (cpiece * ST_TOK + w.t) * 16 + cbyte;
+    w.sz = ST_TOK * LB + (w.t * groups + (kk * 32) / (512 / groups)) * 4;
+    const int ri = kk & 7;
+    const int rbase = ST_TOK * LB + ST_TOK * groups * 4;
+    w.rcode = rbase + ((ri >> 2) * ST_TOK + w.t) * 16 + (ri & 3) * 4;
+    w.rsz = rbase + ST_TOK * 32 + (w.t * rgroups + (ri * 8) / (64 / rgroups)) * 4;
+    return w;
+  }
+
+  // codes -> swizzled bf16 stage; tokens >= valid become zeros (scale and zero-point 0).
+  // Element 32 k + 8 j of token t sits at physical piece (4 k + j) ^ sw(t) = p0 ^ j.
+  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, const Work& w, bf16_t* stage,
+                                                 int tid) {
+    const bool ok = w.t < valid;
+    const int row = w.t * 576;
+    const int kk = tid >> 5;
+    uint32_t sz = *(const uint32_t*)(cst + w.sz);
+    sz = ok ? sz : 0u;
+    float s, zs;
+    scale_zero(sz, s, zs);
+    const int p0 = (4 * kk) ^ sw(w.t);
+    if constexpr (BITS == 4) {
+      const u32x4 c = *(const u32x4*)(cst + w.code);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
+    } else {
+      const uint2 c = *(const uint2*)(cst + w.code);
+      *(u32x4*)&stage[row + ((p0 ^ 0) << 3)] = dequant_int2x8(c.x & 0xFFFFu, s, zs);
+      *(u32x4*)&stage[row + ((p0 ^ 1) << 3)] = dequant_int2x8(c.x >> 16, s, zs);
+      *(u32x4*)&stage[row + ((p0 ^ 2) << 3)] = dequant_int2x8(c.y & 0xFFFFu, s, zs);
+      *(u32x4*)&stage[row + ((p0 ^ 3) << 3)] = dequant_int2x8(c.y >> 16, s, zs);
+    }
+    if (tid < 256) {
+      uint32_t rsz = *(const uint32_t*)(cst + w.rsz);
+      rsz = ok ? rsz : 0u;
+      float rsc, rzs;
+      scale_zero(rsz, rsc, rzs);
+      *(u32x4*)&stage[st_off(w.t, 512 + (kk & 7) * 8)] = dequant_int4x8(*(const uint32_t*)(cst + w.rcode), rsc, rzs);
+    }
+  }
+};
+
+// Stage table entry flags (st_info): sequence index in bits 0..19, valid tokens in 20..25.
+constexpr int INFO_START = 1 << 26;   // first stage of a piece (a sequence's blocks inside one range)
+constexpr int INFO_END = 1 << 27;     // last stage of a piece
+constexpr int INFO_WHOLE = 1 << 28;   // the piece is the whole sequence
+
+// ----------------------------------------------------------------------------------------
+// The kernel
+// ----------------------------------------------------------------------------------------
+template <int FMT, bool QF32>
+__global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
+  constexpr bool QUANT = FMT != FMT_BF16;
+  using QS = QuantStage<FMT == FMT_BF16 ? FMT_INT4 : FMT>;
+  // bf16: 4 ring stages.  Quantised: 2 bf16 stages + DEPTH code stages.
+  constexpr int DEPTH = QUANT ? QS::DEPTH : 4;
+  constexpr int CBYTES = QS::SLOTS * 16;
+  constexpr int SMEM = QUANT ? 2 * ST_BYTES + DEPTH * CBYTES : 4 * ST_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ int st_bid[MAX_ST];
+  __shared__ int st_tok[MAX_ST];
+  __shared__ int st_info[MAX_ST];
+  __shared__ int st_len[MAX_ST];
+  __shared__ int sh_scan[NT / 64 + 1];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const float NEG_INF = -__builtin_inff();
+
+  // unit of work; consecutive units sit on one XCD (workgroups are dealt round-robin to 8 XCDs)
+  const int u = (int)(blockIdx.x & 7) * p.units_per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= p.total_units) return;
+  const int rg = u % p.RG;
+  const int range = u / p.RG;
+  const int B = p.B, R = p.R;
+
+  // ---- flattened block space: sequence b owns blocks [P_b, P_b + n_b); P and the clamped
+  // lengths live in the (not yet used) stage memory while the stage table is built
+  int* tabP = (int*)smem;            // B + 1 entries
+  int* tabL = tabP + (B + 1);        // B entries
+  int carry = 0;
+  for (int base = 0; base < B; base += NT) {
+    const int b = base + tid;
+    int L = 0;
+    if (b < B) {
+      L = p.seq_lens[b];
+      L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    }
+    const int n = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    int x = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) sh_scan[w] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int j = 0; j < NT / 64; ++j) {
+      woff += j < w ? sh_scan[j] : 0;
+      tot += sh_scan[j];
+    }
+    if (b < B) {
+      tabP[b] = carry + woff + x - n;
+      tabL[b] = L;
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  const int total = carry;
+  if (tid == 0) tabP[B] = total;
+  const int per = max(1, (total + p.n_ranges - 1) / p.n_ranges);
+  __syncthreads();
+  if (u == 0) {
+    if (tid == 0) p.meta[0] = per;
+    for (int b = tid; b <= B; b += NT) p.meta[1 + b] = tabP[b];
+  }
+  // empty sequences (no blocks): o = 0 and lse = -inf, written by the workgroups of the range
+  // that holds their position in the block space
+  {
+    int* elist = tabL + B;
+    if (tid == 0) sh_scan[NT / 64] = 0;
+    __syncthreads();
+    for (int b = tid; b < B; b += NT) {
+      if (tabP[b + 1] == tabP[b]) {
+        const int owner = total > 0 ? min(tabP[b], total - 1) / per : 0;
+        if (owner == range) elist[atomicAdd(&sh_scan[NT / 64], 1)] = b;
+      }
+    }
+    __syncthreads();
+    const int n_empty = sh_scan[NT / 64];
+    for (int e = 0; e < n_empty; ++e) {
+      const int b = elist[e];
+      for (int q = tid; q < ROWS * 128; q += NT) {
+        const int row = rg * ROWS + q / 128;
+        if (row >= R) break;
+        const size_t o = ((size_t)b * R + row) * 512 + (q % 128) * 4;
+        if (p.out_bf16) *(uint2*)((bf16_t*)p.out + o) = uint2{0u, 0u};
+        else *(f32x4*)((float*)p.out + o) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (p.out_lse != nullptr && tid < ROWS && rg * ROWS + tid < R) p.out_lse[(size_t)b * R + rg * ROWS + tid] = NEG_INF;
+    }
+  }
+  const int start = range * per;
+  const int end = min(total, start + per);
+  if (start >= end) return;
+  const int nblk = end - start;      // <= MAX_RANGE_BLOCKS
+  const int nst = 2 * nblk;
+
+  // sequence holding block j: the last b with P_b <= j (P is non-decreasing; j < total)
+  auto seq_of = [&](int j) {
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tabP[mid] <= j) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+
+  // ---- per-wave state: rows rg * 128 + 16 w + lr
+  const int rowg = rg * ROWS + 16 * w + lr;
+  const bool row_ok = rowg < R;
+  bf16x8 qreg[18];
+  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
+  int lim = -1;
+  f32x4 acc[32];
+
+  // new piece: this sequence's queries, fresh softmax state
+  int cur_b = -1;
+  auto start_piece = [&](int b, int L) {
+    cur_b = b;
+    const size_t qb = (size_t)cur_b * R + (row_ok ? rowg : 0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qreg[ks] = row_ok ? load_q8(p.q_lat, qb * 512 + ks * 32 + lg * 8, QF32) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qreg[16 + ks] = row_ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
+    lim = row_ok ? L - p.s_q + rowg / p.H : -1;
+    m_s = NEG_INF;
+    l_s = 0.f;
+    l_x = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // The first piece's queries are loaded now, so that their latency overlaps the block-table
+  // loads below, and both are complete before the stage ring starts: the compiler, which does
+  // not see the ring's DMA, would otherwise wait for every stage in flight before using Q.
+  {
+    const int b0 = seq_of(start);
+    start_piece(b0, tabL[b0]);
+  }
+
+  // ---- stage table: block j = start + tid -> its sequence, block id and tokens
+  if (tid < nblk) {
+    const int j = start + tid;
+    const int b = seq_of(j);
+    const int P0 = tabP[b], P1 = tabP[b + 1], L = tabL[b];
+    const int jb = j - P0;
+    int id = p.block_table[(size_t)b * p.bt_stride + jb];
+    int v = min(BLOCK_TOKENS, L - jb * BLOCK_TOKENS);
+    if (id < 0 || (int64_t)id >= p.num_blocks) {
+      id = 0;
+      v = 0;
+    }
+    const bool whole = P0 >= start && P1 <= end;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 2 * tid + h;
+      const int valid = min(ST_TOK, max(0, v - ST_TOK * h));
+      int info = b | (valid << 20) | (whole ? INFO_WHOLE : 0);
+      if (h == 0 && (tid == 0 || jb == 0)) info |= INFO_START;
+      if (h == 1 && (tid == nblk - 1 || j == P1 - 1)) info |= INFO_END;
+      st_bid[k] = id;
+      st_tok[k] = jb * BLOCK_TOKENS + ST_TOK * h;
+      st_info[k] = info;
+      st_len[k] = L;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // ---- stages
+  const uint32_t smem_base = lds_addr(smem);
+  const QuantPlanes pl{(int)p.off_lc, (int)p.off_ls, (int)p.off_rc, (int)p.off_rs};
+  const int groups = 512 / p.g_lat, rgroups = 64 / p.g_rope;
+  // ring slot addresses: bf16 stage slot k at k * ST_BYTES; quantised: bf16 stages 0, 1, then
+  // code slot k at 2 * ST_BYTES + k * CBYTES
+  auto bf_stage = [&](int k) -> bf16_t* { return (bf16_t*)(smem + k * ST_BYTES); };
+  auto code_slot = [&](int k) -> int { return 2 * ST_BYTES + k * CBYTES; };
+  auto issue = [&](int s) {
+    const int id = __builtin_amdgcn_readfirstlane(st_bid[s]);
+    const int info = __builtin_amdgcn_readfirstlane(st_info[s]);
+    const uint8_t* blk = p.pool + (size_t)id * (size_t)p.block_bytes;
+    const int half = (__builtin_amdgcn_readfirstlane(st_tok[s]) / ST_TOK) & 1;
+    if constexpr (QUANT) {
+      QS::issue(blk, half, pl, groups, rgroups, smem_base + code_slot(s % DEPTH), tid);
+    } else {
+      BfProducer::issue(blk + half * ST_TOK * 1152, (info >> 20) & 63, smem_base + (s & 3) * ST_BYTES, tid);
+    }
+  };
+  // wait until a stage has landed, given how many later stages were issued after it
+  constexpr int LA = QUANT ? QS::LOADS_LO : BfProducer::LOADS_LO;
+  constexpr int LB = QUANT ? QS::LOADS_HI : BfProducer::LOADS_HI;
+  auto wait_stage = [&](int later) {
+    auto wait_k = [&](auto K) {
+      constexpr int k = decltype(K)::value;
+      if (w < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(k * LA));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(k * LB));
+    };
+    switch (later) {
+      case 0: wait_k(std::integral_constant<int, 0>{}); break;
+      case 1: wait_k(std::integral_constant<int, 1>{}); break;
+      case 2: wait_k(std::integral_constant<int, 2>{}); break;
+      case 3: wait_k(std::integral_constant<int, 3>{}); break;
+      case 4: wait_k(std::integral_constant<int, 4>{}); break;
+      case 5: wait_k(std::integral_constant<int, 5>{}); break;
+      default: wait_k(std::integral_constant<int, 6>{}); break;
+    }
+  };
+  static_assert((QUANT ? DEPTH - 2 : 2) <= 6 && 6 * LA <= 63, "stage waits out of range");
+
+  const typename QS::Work dq = QS::plan(groups, rgroups, tid);
+
+  // prologue.  bf16: stages 0..2 in flight, stage 0 landed.  Quantised: codes 0..DEPTH-1 in
+  // flight, code 0 dequantised into bf16 stage 0, code 1 landed.
+  if constexpr (!QUANT) {
+    for (int s = 0; s < 3 && s < nst; ++s) issue(s);
+    wait_stage(min(nst - 1, 2));
+    lds_barrier();
+  } else {
+    for (int s = 0; s < DEPTH && s < nst; ++s) issue(s);
+    wait_stage(min(nst - 1, DEPTH - 1));
+    lds_barrier();
+    QS::dequant(smem + code_slot(0), (__builtin_amdgcn_readfirstlane(st_info[0]) >> 20) & 63, dq, bf_stage(0), tid);
+    if (nst > 1) wait_stage(min(nst - 1, DEPTH - 1) - 1);
+    lds_barrier();
+  }
+
+  for (int s = 0; s < nst; ++s) {
+    const int info = __builtin_amdgcn_readfirstlane(st_info[s]);
+    const int valid = (info >> 20) & 63;
+    const int stok = __builtin_amdgcn_readfirstlane(st_tok[s]);
+    if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]));
+    // refill the ring: the slot of stage s-1 (bf16) / code s (dequantised in step s-1)
+    if constexpr (!QUANT) {
+      if (s + 3 < nst) issue(s + 3);
+    } else {
+      if (s + DEPTH < nst) issue(s + DEPTH);
+    }
+    const bf16_t* KS = QUANT ? bf_stage(s & 1) : bf_stage(s & 3);
+    if (!QUANT && valid < ST_TOK) {
+      // rows past the sequence end came from a stand-in address: zero them
+      bf16_t* Z = bf_stage(s & 3);
+      for (int q = tid; q < (ST_TOK - valid) * 72; q += NT)
+        *(u32x4*)&Z[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
+      lds_barrier();
+    }
+    if constexpr (QUANT) {
+      // dequantise the next stage while this one is consumed
+      if (s + 1 < nst)
+        QS::dequant(smem + code_slot((s + 1) % DEPTH), (__builtin_amdgcn_readfirstlane(st_info[s + 1]) >> 20) & 63,
+                    dq, bf_stage((s + 1) & 1), tid);
+    }
+
+    // ---- scores S^T[token][row] for token tiles tt (two accumulation chains each)
+    f32x4 sc[2];
+    {
+      const bf16_t* kb[2][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = tt * 16 + lr;
+        const int f = sw(t);
+        kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
+        kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
+        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // the two token tiles' chains interleave; two waves per SIMD hide the MFMA latency
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 a = *(const bf16x8*)(kb[tt][ks & 1] + ks * 32);
+          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], sc[tt], 0, 0, 0);
+        }
+        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
+      }
+    }
+
+    // ---- softmax of row lr (this lane holds tokens 16 tt + 4 lg + i)
+    float x[2][4];
+    float mt = NEG_INF;
+    {
+      // token k = 16 tt + 4 lg + i is kept if k < valid and stok + k <= lim
+      const int kb4 = 4 * lg;
+      const int lim_k = min(valid - 1, lim - stok);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = kb4 <= lim_k - (16 * tt + i);
+          x[tt][i] = ok ? sc[tt][i] * p.scale_log2 : NEG_INF;
+          mt = fmaxf(mt, x[tt][i]);
+        }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
+    const float mu = mn == NEG_INF ? 0.f : mn;
+    const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
+    l_s *= al;
+    l_x *= al;
+    m_s = mn;
+    uint32_t pw[4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint32_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pf = __builtin_amdgcn_exp2f(x[tt][i] - mu);
+        pb[i] = f32_to_bf16_bits(pf);
+        l_s += bf16_bits_to_f32(pb[i]);
+        l_x += pf;
+      }
+      pw[2 * tt] = pb[0] | (pb[1] << 16);
+      pw[2 * tt + 1] = pb[2] | (pb[3] << 16);
+    }
+    const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    if (__any(al != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) acc[nt] *= al;
+    }
+
+    // ---- O^T[col][row] += V^T[col][token] . P^T[token][row]; the 8 tokens of lane group lg
+    // are 4 lg .. 4 lg + 3 (first read) and 16 + 4 lg .. 16 + 4 lg + 3 (second read)
+    {
+      // column d = 16 nt + 4 (lr & 3) of token t is element st_off(t, d); with nt = 4 q + r its
+      // piece is (2 nt + h) ^ sw(t) = 8 q + ((2 r + h) ^ sw(t)), h = (lr & 3) / 2, since sw < 8:
+      // four per-lane bases (r) and an immediate offset of 64 q elements.  Token tb = ta + 16 has
+      // sw(tb) = sw(ta) ^ 1, so its pieces sit one piece up or down: a per-lane shift db.
+      const int ta = 4 * lg + (lr >> 2);
+      const int h = (lr & 3) >> 1, fa = sw(ta);
+      const int db = 16 * 576 + (((h ^ fa) & 1) ? -8 : 8);
+      int oa[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lr & 1) * 4;
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) {
+        const int q = nt >> 2, r = nt & 3;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + 64 * q]);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + db + 64 * q]);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pt, acc[nt], 0, 0, 0);
+        if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- end of a piece: normalise and write this wave's rows
+    if (info & INFO_END) {
+      const bool whole = info & INFO_WHOLE;
+      const size_t slot = whole ? (size_t)cur_b : (size_t)cur_b + range;
+      float ls = l_s, lx = l_x;
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      lx += __shfl_xor(lx, 16, 64);
+      lx += __shfl_xor(lx, 32, 64);
+      if (row_ok) {
+        const float inv = ls > 0.f ? 1.f / ls : 0.f;
+        const size_t ob = (slot * R + rowg) * 512 + 4 * lg;
+        if (whole && p.out_bf16) {
+          bf16_t* o = (bf16_t*)p.out;
+#pragma unroll
+          for (int nt = 0; nt < 32; ++nt) {
+            const f32x4 v = acc[nt] * inv;
+            *(uint2*)(o + ob + nt * 16) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        } else {
+          float* o = whole ? (float*)p.out : p.part_o;
+#pragma unroll
+          for (int nt = 0; nt < 32; ++nt) *(f32x4*)(o + ob + nt * 16) = acc[nt] * inv;
+        }
+        float* lse_out = whole ? p.out_lse : p.part_lse;
+        if (lg == 0 && lse_out != nullptr)
+          lse_out[slot * R + rowg] = lx > 0.f ? (m_s + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
+      }
+    }
+
+    // the next step's stage has landed and nobody reads stage s any more
+    if constexpr (!QUANT) {
+      if (s + 1 < nst) wait_stage(min(nst - 1, s + 3) - (s + 1));
+    } else {
+      if (s + 2 < nst) wait_stage(min(nst - 1, s + DEPTH) - (s + 2));
+    }
+    lds_barrier();
+  }
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const RowsParams& p, hipStream_t st) {
+  const int grid = 8 * p.units_per_xcd;
+  if (p.q_f32)
+    hipLaunchKernelGGL((decode_rows_kernel<FMT, true>), dim3(grid), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<FMT, false>), dim3(grid), dim3(NT), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace rows
+
+hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st) {
+  switch (fmt) {
+    case FMT_BF16: return rows::launch_fmt<FMT_BF16>(p, st);
+    case FMT_INT4: return rows::launch_fmt<FMT_INT4>(p, st);
+    case FMT_INT2: return rows::launch_fmt<FMT_INT2>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

@@ -29,12 +29,45 @@ struct DecodeParams {
   float* out_lse;           // [B*max_chunks][R] or lse (may be null when writing o_lat directly)
 };
 
+// Arguments of the row-owner decode kernel (128 query rows per workgroup).  The batch's
+// cache blocks, sequence after sequence, are cut into n_ranges equal ranges; workgroup
+// (range i, row group r) attends its rows over the blocks of range i.  A sequence that one
+// range covers entirely is written to out/out_lse directly; a sequence cut by ranges leaves
+// one partial (o normalised, lse) per piece in slot b + i of part_o/part_lse.
+struct RowsParams {
+  const void* q_lat;        // [B][R][512]
+  const void* q_rope;       // [B][R][64]
+  int q_f32;
+  const uint8_t* pool;
+  int64_t num_blocks;
+  int64_t block_bytes;
+  int64_t off_lc, off_ls, off_rc, off_rs;
+  int g_lat, g_rope;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  int B, s_q, H, R, RG;
+  int n_ranges, units_per_xcd, total_units;
+  float scale_log2;
+  void* out;                // o_lat [B][R][512]
+  int out_bf16;
+  float* out_lse;           // [B][R], may be null
+  float* part_o;            // [B + n_ranges - 1][R][512]
+  float* part_lse;          // [B + n_ranges - 1][R]
+  int32_t* meta;            // [0]: blocks per range; [1 + b]: first block of sequence b, b <= B
+};
+
+// Combine of split partials.  Partition mode (meta == null): max_chunks partitions of tpc
+// blocks per sequence, slot b * max_chunks + c.  Range mode: pieces of the ranges in meta,
+// slots b + i; sequences inside one range were written by the decode kernel.
 struct CombineParams {
   const float* part_o;
   const float* part_lse;
   const int32_t* seq_lens;
   int max_seq_len;
   int R, d_c, max_chunks, tpc;
+  const int32_t* meta;
   void* out;
   int out_bf16;
   float* out_lse;
@@ -66,6 +99,7 @@ struct DequantParams {
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
+hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
 

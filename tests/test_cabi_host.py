@@ -66,9 +66,9 @@ def _plan(a, cus=256):
 
 
 def test_split_plan_covers_the_longest_sequence():
-    for B, H, s_q, L, ns in [(32, 16, 1, 4096, 0), (64, 128, 1, 8192, 0), (64, 128, 2, 8192, 0),
-                             (16, 16, 1, 32768, 0), (4, 128, 1, 131072, 0), (1, 16, 1, 1, 0), (3, 16, 1, 700, 5),
-                             (2, 16, 2, 2, 0)]:
+    """Fewer than 96 query rows per sequence: partitions of the longest sequence."""
+    for B, H, s_q, L, ns in [(32, 16, 1, 4096, 0), (16, 16, 1, 32768, 0), (1, 16, 1, 1, 0), (3, 16, 1, 700, 5),
+                             (2, 16, 2, 2, 0), (8, 32, 2, 5000, 0)]:
         a = _args(batch=B, num_heads=H, s_q=s_q, max_seq_len=L, num_splits=ns, block_table_stride=-(-L // 64))
         st, splits, tpc = _plan(a)
         assert st == 0
@@ -77,6 +77,24 @@ def test_split_plan_covers_the_longest_sequence():
         assert 1 <= splits <= nblk
         if ns:
             assert splits <= ns
+
+
+def test_range_plan_covers_the_batch():
+    """96 or more query rows per sequence: the batch's blocks cut into equal ranges of at most
+    256 blocks, one round of workgroups over the CUs by default."""
+    cus = 256
+    for B, H, s_q, L, ns in [(64, 128, 1, 8192, 0), (64, 128, 2, 8192, 0), (4, 128, 1, 131072, 0),
+                             (1, 128, 1, 1, 0), (3, 128, 1, 700, 2), (4096, 128, 1, 65536, 0), (2, 64, 2, 300, 0)]:
+        a = _args(batch=B, num_heads=H, s_q=s_q, max_seq_len=L, num_splits=ns, block_table_stride=-(-L // 64))
+        st, ranges, per = _plan(a, cus)
+        assert st == 0
+        bound = B * -(-L // 64)                  # blocks of the batch, at most
+        rg = -(-(s_q * H) // 128)
+        assert 1 <= ranges <= bound and ranges * per >= bound and per <= 256
+        if ns:
+            assert ranges == max(min(ns * B, bound), -(-bound // 256))
+        elif bound >= cus // rg and -(-bound // 256) <= cus // rg:
+            assert ranges == cus // rg
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -1,0 +1,137 @@
+"""GPU parity of the many-rows decode path (96 or more query rows per sequence, e.g. 128 heads)
+and of batch edge cases shared by both decode paths, against the float64 oracle.
+
+The many-rows path cuts the batch's cache blocks into equal ranges that may cover several
+sequences or a part of one; these cases vary the range count (num_splits), mix sequence
+lengths, and cover empty sequences and block-table entries outside the pool.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from mla_synth import CONFIGS, make_inputs  # noqa: E402
+from tests.gpu_helpers import bf16_exact, desc_of, dev, logical_cache, norm_err, to_device  # noqa: E402
+from tests.test_gpu_parity import TOL_BF16, _decode_stage, assert_bf16_output  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_02_amd as m
+    m.lib()
+    return m
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check(o, lse, ref_o, ref_lse):
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    e = norm_err(o, ref_o)
+    el = float(np.max(np.abs(lse - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= TOL_BF16 and el <= TOL_BF16
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
+def test_range_count_invariance(mla, splits):
+    """Ranges of every size: whole sequences, pieces, several sequences per range."""
+    x = make_inputs(CONFIGS["3"], 47, lens=[1, 64, 200, 900, 65, 3], H=128)
+    _say("ranges", splits)
+    _check(*_decode_stage(mla, x, num_splits=splits))
+
+
+def test_range_many_sequences_two_queries(mla):
+    """s_q = 2 with 128 heads: 256 rows, two row groups over the same ranges."""
+    rng = np.random.default_rng(5)
+    lens = [int(v) for v in rng.integers(2, 700, size=20)]
+    x = make_inputs(CONFIGS["3b"], 48, lens=lens, H=128)
+    _say("many sequences s_q=2", lens)
+    _check(*_decode_stage(mla, x))
+
+
+@pytest.mark.parametrize("name,lens", [("4", [64, 333, 1030]), ("5", [1, 65, 700])])
+def test_range_quantised(mla, name, lens):
+    x = make_inputs(CONFIGS[name], 49, lens=lens, H=128)
+    _say("quantised ranges", name, lens)
+    _check(*_decode_stage(mla, x))
+
+
+def test_range_bf16_output(mla):
+    x = make_inputs(CONFIGS["3"], 50, lens=[100, 333, 7], H=128)
+    _say("bf16 o_lat ranges")
+    for splits in (0, 1, 3):
+        o, lse, ref_o, ref_lse = _decode_stage(mla, x, num_splits=splits, o_dtype=torch.bfloat16)
+        assert_bf16_output(o, ref_o, TOL_BF16)
+
+
+def test_range_deterministic(mla):
+    cfg = CONFIGS["3"]
+    x = make_inputs(cfg, 51, lens=[300, 1000, 17], H=128)
+    t = to_device(x)
+    q = torch.from_numpy(bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))).to(torch.bfloat16).to(dev())
+    _say("range determinism")
+    outs = []
+    for _ in range(2):
+        o, l = mla.decode_paged(q, t["q_rope"], t["pool"], desc_of(cfg), t["block_table"], t["seq_lens"],
+                                1000, cfg.sm_scale)
+        outs.append((o.cpu().numpy().copy(), l.cpu().numpy().copy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def _run(mla, x, seq_lens, block_table, splits=0):
+    cfg = x.cfg
+    t = to_device(x)
+    q_lat64 = bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))
+    q = torch.from_numpy(q_lat64).to(torch.bfloat16).to(dev())
+    o, l = mla.decode_paged(q, t["q_rope"], t["pool"], desc_of(cfg), torch.from_numpy(block_table).to(dev()),
+                            torch.from_numpy(seq_lens).to(dev()), int(x.seq_lens.max()), cfg.sm_scale,
+                            num_splits=splits)
+    torch.cuda.synchronize()
+    return q_lat64, o.float().cpu().numpy(), l.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,H", [("2", 16), ("3", 128)])
+def test_empty_sequences(mla, name, H):
+    """A sequence of length 0 attends to nothing: o = 0, lse = -inf; the others are unaffected."""
+    x = make_inputs(CONFIGS[name], 52, lens=[100, 1, 300, 1, 65], H=H)
+    lens = x.seq_lens.copy()
+    lens[[1, 3]] = 0
+    _say("empty sequences", name, H)
+    for splits in (0, 2):
+        q_lat64, o, lse = _run(mla, x, lens, x.block_table, splits)
+        assert np.all(o[[1, 3]] == 0.0) and np.all(lse[[1, 3]] == -np.inf)
+        keep = [0, 2, 4]
+        c, k = logical_cache(x)
+        ref_o, ref_lse = oracle.attend_latent(q_lat64[keep], x.q_rope[keep].astype(np.float64),
+                                              [c[b] for b in keep], [k[b] for b in keep], x.seq_lens[keep],
+                                              x.cfg.s_q, x.cfg.sm_scale)
+        _check(o[keep], lse[keep], ref_o, ref_lse)
+
+
+@pytest.mark.parametrize("name,H", [("2", 16), ("3", 128)])
+def test_out_of_range_block_ids_are_skipped(mla, name, H):
+    """Tokens of a block-table entry outside [0, num_blocks) take no part in the softmax:
+    the result equals attention over the sequence with that block's tokens removed."""
+    x = make_inputs(CONFIGS[name], 53, lens=[300, 200], H=H)
+    bt = x.block_table.copy()
+    nblocks = x.pool.shape[0]
+    bt[0, 1] = -1
+    bt[1, 2] = nblocks + 5
+    _say("out-of-range ids", name, H)
+    q_lat64, o, lse = _run(mla, x, x.seq_lens, bt)
+    c, k = logical_cache(x)
+    keep0 = np.r_[0:64, 128:300]
+    keep1 = np.r_[0:128, 192:200]
+    c2 = [c[0][keep0], c[1][keep1]]
+    k2 = [k[0][keep0], k[1][keep1]]
+    ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c2, k2,
+                                          np.array([len(keep0), len(keep1)]), x.cfg.s_q, x.cfg.sm_scale)
+    _check(o, lse, ref_o, ref_lse)
