@@ -313,8 +313,9 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     r.off_ls = lay.off[1];
     r.off_rc = lay.off[2];
     r.off_rs = lay.off[3];
-    r.g_lat = a->cache.latent_group > 0 ? a->cache.latent_group : 1;
-    r.g_rope = a->cache.rope_group > 0 ? a->cache.rope_group : 1;
+    auto log2i = [](int v) { int l = 0; while ((1 << (l + 1)) <= v) ++l; return l; };
+    r.g_lat_log2 = log2i(a->cache.latent_group > 0 ? a->cache.latent_group : 1);
+    r.g_rope_log2 = log2i(a->cache.rope_group > 0 ? a->cache.rope_group : 1);
     r.block_table = a->block_table;
     r.bt_stride = a->block_table_stride;
     r.seq_lens = a->seq_lens;

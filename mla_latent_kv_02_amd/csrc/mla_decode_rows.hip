@@ -145,53 +145,50 @@ struct QuantStage {
 
   // Thread q dequantises latent chunk kk = q / 32 (32 elements, inside one quantisation group
   // since groups are multiples of 32) of token t = q mod 32; threads q < 256 also dequantise
-  // RoPE elements 8 ri .. 8 ri + 7 (ri = q / 32) of token t.  Offsets are fixed per thread.
-  struct Work {
-    int t, code, sz, rcode, rsz;
-  };
-  __device__ __forceinline__ static Work plan(int groups, int rgroups, int tid) {
-    Work w;
-    w.t = tid & 31;
-    const int kk = tid >> 5;
-    const int cpiece = (kk * 32 * BITS) / 128, cbyte = ((kk * 32 * BITS) / 8) & 15;
-    w.code = (cpiece * ST_TOK + w.t) * 16 + cbyte;
-    w.sz = ST_TOK * LB + (w.t * groups + (kk * 32) / (512 / groups)) * 4;
-    const int ri = kk & 7;
-    const int rbase = ST_TOK * LB + ST_TOK * groups * 4;
-    w.rcode = rbase + ((ri >> 2) * ST_TOK + w.t) * 16 + (ri & 3) * 4;
-    w.rsz = rbase + ST_TOK * 32 + (w.t * rgroups + (ri * 8) / (64 / rgroups)) * 4;
-    return w;
-  }
-
-  // codes -> swizzled bf16 stage; tokens >= valid become zeros (scale and zero-point 0).
-  // Element 32 k + 8 j of token t sits at physical piece (4 k + j) ^ sw(t) = p0 ^ j.
-  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, const Work& w, bf16_t* stage,
+  // RoPE elements 8 ri .. 8 ri + 7 (ri = q / 32) of token t.  Group sizes are powers of two
+  // (gl = log2 latent group, gr = log2 rope group).  Offsets are recomputed every stage: a few
+  // ALU operations instead of registers held across the loop.
+  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, int gl, int gr, bf16_t* stage,
                                                  int tid) {
-    const bool ok = w.t < valid;
-    const int row = w.t * 576;
-    const int kk = tid >> 5;
-    uint32_t sz = *(const uint32_t*)(cst + w.sz);
+    asm volatile("" : "+v"(tid));
+    const int t = tid & 31, kk = tid >> 5;
+    const int groups_log2 = 9 - gl;
+    const bool ok = t < valid;
+    const int row = t * 576;
+    const int ls = ST_TOK * LB;                    // scale plane of the latent codes
+    uint32_t sz = *(const uint32_t*)(cst + ls + (((t << groups_log2) + ((kk * 32) >> gl)) << 2));
     sz = ok ? sz : 0u;
     float s, zs;
     scale_zero(sz, s, zs);
-    const int p0 = (4 * kk) ^ sw(w.t);
+    const int p0 = (4 * kk) ^ sw(t);
+    const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
+    const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
     if constexpr (BITS == 4) {
-      const u32x4 c = *(const u32x4*)(cst + w.code);
+      const u32x4 c = *(const u32x4*)code;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
+      for (int j = 0; j < 4; ++j) {
+        *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
+        __builtin_amdgcn_sched_barrier(0);     // one piece at a time: few registers
+      }
     } else {
-      const uint2 c = *(const uint2*)(cst + w.code);
-      *(u32x4*)&stage[row + ((p0 ^ 0) << 3)] = dequant_int2x8(c.x & 0xFFFFu, s, zs);
-      *(u32x4*)&stage[row + ((p0 ^ 1) << 3)] = dequant_int2x8(c.x >> 16, s, zs);
-      *(u32x4*)&stage[row + ((p0 ^ 2) << 3)] = dequant_int2x8(c.y & 0xFFFFu, s, zs);
-      *(u32x4*)&stage[row + ((p0 ^ 3) << 3)] = dequant_int2x8(c.y >> 16, s, zs);
+      const uint2 c = *(const uint2*)code;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wd = j < 2 ? c.x : c.y;
+        *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int2x8(j & 1 ? wd >> 16 : wd & 0xFFFFu, s, zs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (tid < 256) {
-      uint32_t rsz = *(const uint32_t*)(cst + w.rsz);
+      const int ri = kk & 7;
+      const int rbase = ls + (ST_TOK << (groups_log2 + 2));
+      const int rgroups_log2 = 6 - gr;
+      uint32_t rsz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << rgroups_log2) + ((ri * 8) >> gr)) << 2));
       rsz = ok ? rsz : 0u;
       float rsc, rzs;
       scale_zero(rsz, rsc, rzs);
-      *(u32x4*)&stage[st_off(w.t, 512 + (kk & 7) * 8)] = dequant_int4x8(*(const uint32_t*)(cst + w.rcode), rsc, rzs);
+      const uint32_t rc = *(const uint32_t*)(cst + rbase + (((ri >> 2) * ST_TOK + t) << 4) + (ri & 3) * 4);
+      *(u32x4*)&stage[st_off(t, 512 + ri * 8)] = dequant_int4x8(rc, rsc, rzs);
     }
   }
 };
@@ -340,6 +337,9 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     l_x = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // wait here, on this rare path: a load the compiler sees pending at the loop's back edge
+    // would make it wait for every stage in flight at the top of every step
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
   // The first piece's queries are loaded now, so that their latency overlaps the block-table
   // loads below, and both are complete before the stage ring starts: the compiler, which does
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   // ---- stages
   const uint32_t smem_base = lds_addr(smem);
   const QuantPlanes pl{(int)p.off_lc, (int)p.off_ls, (int)p.off_rc, (int)p.off_rs};
-  const int groups = 512 / p.g_lat, rgroups = 64 / p.g_rope;
+  const int groups = 512 >> p.g_lat_log2, rgroups = 64 >> p.g_rope_log2;
   // ring slot addresses: bf16 stage slot k at k * ST_BYTES; quantised: bf16 stages 0, 1, then
   // code slot k at 2 * ST_BYTES + k * CBYTES
   auto bf_stage = [&](int k) -> bf16_t* { return (bf16_t*)(smem + k * ST_BYTES); };
@@ -418,8 +418,6 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   };
   static_assert((QUANT ? DEPTH - 2 : 2) <= 6 && 6 * LA <= 63, "stage waits out of range");
 
-  const typename QS::Work dq = QS::plan(groups, rgroups, tid);
-
   // prologue.  bf16: stages 0..2 in flight, stage 0 landed.  Quantised: codes 0..DEPTH-1 in
   // flight, code 0 dequantised into bf16 stage 0, code 1 landed.
   if constexpr (!QUANT) {
@@ -430,7 +428,8 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     for (int s = 0; s < DEPTH && s < nst; ++s) issue(s);
     wait_stage(min(nst - 1, DEPTH - 1));
     lds_barrier();
-    QS::dequant(smem + code_slot(0), (__builtin_amdgcn_readfirstlane(st_info[0]) >> 20) & 63, dq, bf_stage(0), tid);
+    QS::dequant(smem + code_slot(0), (__builtin_amdgcn_readfirstlane(st_info[0]) >> 20) & 63, p.g_lat_log2,
+                p.g_rope_log2, bf_stage(0), tid);
     if (nst > 1) wait_stage(min(nst - 1, DEPTH - 1) - 1);
     lds_barrier();
   }
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       // dequantise the next stage while this one is consumed
       if (s + 1 < nst)
         QS::dequant(smem + code_slot((s + 1) % DEPTH), (__builtin_amdgcn_readfirstlane(st_info[s + 1]) >> 20) & 63,
-                    dq, bf_stage((s + 1) & 1), tid);
+                    p.g_lat_log2, p.g_rope_log2, bf_stage((s + 1) & 1), tid);
     }
 
     // ---- scores S^T[token][row] for token tiles tt (two accumulation chains each)
@@ -473,15 +472,25 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
         sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // the two token tiles' chains interleave; two waves per SIMD hide the MFMA latency
+      // software pipeline: the fragments of k-step ks + 1 are read while k-step ks multiplies;
+      // the two token tiles' chains interleave and two waves per SIMD hide the MFMA latency
+      constexpr int KD = 1;   // prefetch depth in k-steps
+      bf16x8 a[KD + 1][2];
+#pragma unroll
+      for (int i = 0; i < KD; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) a[i][tt] = *(const bf16x8*)(kb[tt][i & 1] + i * 32);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
+        if (ks + KD < 18) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 a = *(const bf16x8*)(kb[tt][ks & 1] + ks * 32);
-          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], sc[tt], 0, 0, 0);
+          for (int tt = 0; tt < 2; ++tt)
+            a[(ks + KD) % (KD + 1)][tt] = *(const bf16x8*)(kb[tt][(ks + KD) & 1] + (ks + KD) * 32);
         }
-        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the fragments in flight
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % (KD + 1)][tt], qreg[ks], sc[tt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -542,14 +551,22 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       int oa[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lr & 1) * 4;
-#pragma unroll
-      for (int nt = 0; nt < 32; ++nt) {
+      // software pipeline: the V^T fragment of tile nt + 2 is read while tile nt multiplies
+      auto vfrag = [&](int nt) {
         const int q = nt >> 2, r = nt & 3;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + 64 * q]);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + db + 64 * q]);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pt, acc[nt], 0, 0, 0);
-        if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int PD = 3;   // prefetch depth
+      bf16x8 va[PD + 1];
+#pragma unroll
+      for (int i = 0; i < PD; ++i) va[i] = vfrag(i);
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) {
+        if (nt + PD < 32) va[(nt + PD) % (PD + 1)] = vfrag(nt + PD);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nt % (PD + 1)], pt, acc[nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -581,6 +598,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         if (lg == 0 && lse_out != nullptr)
           lse_out[slot * R + rowg] = lx > 0.f ? (m_s + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
       }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
     }
 
     // the next step's stage has landed and nobody reads stage s any more

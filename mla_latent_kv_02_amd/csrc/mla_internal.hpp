@@ -42,7 +42,7 @@ struct RowsParams {
   int64_t num_blocks;
   int64_t block_bytes;
   int64_t off_lc, off_ls, off_rc, off_rs;
-  int g_lat, g_rope;
+  int g_lat_log2, g_rope_log2;  // quantisation group sizes (powers of two: they divide 512 and 64)
   const int32_t* block_table;
   int bt_stride;
   const int32_t* seq_lens;
