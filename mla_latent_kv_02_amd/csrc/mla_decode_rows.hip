@@ -464,9 +464,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     f32x4 sc[2];
     {
       const bf16_t* kb[2][2];
+      int lr_ = lr;
+      asm volatile("" : "+v"(lr_));   // recomputed per stage rather than held across the loop
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int t = tt * 16 + lr;
+        const int t = tt * 16 + lr_;
         const int f = sw(t);
         kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
         kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       }
       // software pipeline: the fragments of k-step ks + 1 are read while k-step ks multiplies;
       // the two token tiles' chains interleave and two waves per SIMD hide the MFMA latency
-      constexpr int KD = 1;   // prefetch depth in k-steps
+      constexpr int KD = 2;   // prefetch depth in k-steps
       bf16x8 a[KD + 1][2];
 #pragma unroll
       for (int i = 0; i < KD; ++i)
@@ -545,12 +547,15 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       // piece is (2 nt + h) ^ sw(t) = 8 q + ((2 r + h) ^ sw(t)), h = (lr & 3) / 2, since sw < 8:
       // four per-lane bases (r) and an immediate offset of 64 q elements.  Token tb = ta + 16 has
       // sw(tb) = sw(ta) ^ 1, so its pieces sit one piece up or down: a per-lane shift db.
-      const int ta = 4 * lg + (lr >> 2);
-      const int h = (lr & 3) >> 1, fa = sw(ta);
+      int lane_ = lane;
+      asm volatile("" : "+v"(lane_));   // recomputed per stage rather than held across the loop
+      const int lrp = lane_ & 15, lgp = lane_ >> 4;
+      const int ta = 4 * lgp + (lrp >> 2);
+      const int h = (lrp & 3) >> 1, fa = sw(ta);
       const int db = 16 * 576 + (((h ^ fa) & 1) ? -8 : 8);
       int oa[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lr & 1) * 4;
+      for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
       // software pipeline: the V^T fragment of tile nt + 2 is read while tile nt multiplies
       auto vfrag = [&](int nt) {
         const int q = nt >> 2, r = nt & 3;
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + db + 64 * q]);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int PD = 3;   // prefetch depth
+      constexpr int PD = 4;   // prefetch depth
       bf16x8 va[PD + 1];
 #pragma unroll
       for (int i = 0; i < PD; ++i) va[i] = vfrag(i);
