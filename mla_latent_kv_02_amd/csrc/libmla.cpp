@@ -161,8 +161,8 @@ int32_t device_cus(int* cus) {
   return MLA_OK;
 }
 
-// Workspace layout.  Row-owner kernel: meta [B + 2] int32, then partial o and lse of the
-// slots b + i (B + ranges - 1 of them).  Partition kernels: partial o, then lse.
+// Workspace layout.  Row-owner kernel: meta [B + 2] int32, then partial o, lse and 1/sum(P)
+// of the slots b + i (B + ranges - 1 of them).  Partition kernels: partial o, then lse.
 size_t rows_meta_bytes(const mla_decode_args* a) { return (size_t)align_up(((int64_t)a->batch + 2) * 4, 256); }
 
 size_t partial_bytes(const mla_decode_args* a, const Plan& p, size_t* lse_off) {
@@ -171,7 +171,7 @@ size_t partial_bytes(const mla_decode_args* a, const Plan& p, size_t* lse_off) {
     const int64_t rows = slots * a->s_q * a->num_heads;
     const int64_t o_bytes = align_up(rows * a->cache.d_c * 4, 256);
     *lse_off = rows_meta_bytes(a) + (size_t)o_bytes;
-    return *lse_off + (size_t)align_up(rows * 4, 256);
+    return *lse_off + 2 * (size_t)align_up(rows * 4, 256);
   }
   if (p.splits <= 1) {
     *lse_off = 0;
@@ -337,12 +337,14 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     r.meta = (int32_t*)a->workspace;
     r.part_o = (float*)((char*)a->workspace + rows_meta_bytes(a));
     r.part_lse = (float*)((char*)a->workspace + lse_off);
+    r.part_inv = (float*)((char*)a->workspace + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
     hipError_t e = mla::launch_decode_rows(r, a->cache.latent_fmt, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
-    if (plan.splits > 1) {
+    {
       mla::CombineParams c{};
       c.part_o = r.part_o;
       c.part_lse = r.part_lse;
+      c.part_inv = r.part_inv;
       c.seq_lens = a->seq_lens;
       c.max_seq_len = a->max_seq_len;
       c.R = r.R;

@@ -95,11 +95,12 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------------------
 // Combine: lse = log sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c over the partitions of
-// one (b, row).  One workgroup of 128 threads per (b, row); weights go through LDS in
+// one (b, row), o_c = part_o_c (partition mode) or part_o_c * part_inv_c (range mode).  One workgroup of 128 threads per (b, row); weights go through LDS in
 // batches of 128 partitions and each thread sums 4 columns with independent loads.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
-  __shared__ float wsh[128];
+  __shared__ float wsh[128];   // weight of a partial's lse
+  __shared__ float vsh[128];   // the same times its normalisation factor
   __shared__ float red[2];
   const int tid = threadIdx.x;
   const int R = p.R;
@@ -118,7 +119,6 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     const int per = p.meta[0], first = p.meta[1 + b], nblk = p.meta[2 + b] - first;
     if (nblk <= 0) return;  // empty sequence: written by the decode kernel
     const int i0 = first / per, i1 = (first + nblk - 1) / per;
-    if (i0 == i1) return;  // one range held the whole sequence and wrote its result
     nch = i1 - i0 + 1;
     u0 = (size_t)b + i0;
   }
@@ -138,7 +138,9 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     __syncthreads();
     if (tid < n) {
       const float lc = p.part_lse[(u0 + c0 + tid) * R + r];
-      wsh[tid] = m == NEG_INF ? 0.f : expf(lc - m);
+      const float wc = m == NEG_INF ? 0.f : expf(lc - m);
+      wsh[tid] = wc;
+      vsh[tid] = p.part_inv == nullptr ? wc : wc * p.part_inv[(u0 + c0 + tid) * R + r];
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) wsum += wsh[j];
@@ -153,9 +155,9 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
         const f32x4 v1 = *(const f32x4*)(base + (j + 1) * stride);
         const f32x4 v2 = *(const f32x4*)(base + (j + 2) * stride);
         const f32x4 v3 = *(const f32x4*)(base + (j + 3) * stride);
-        acc[k] += wsh[j] * v0 + wsh[j + 1] * v1 + wsh[j + 2] * v2 + wsh[j + 3] * v3;
+        acc[k] += vsh[j] * v0 + vsh[j + 1] * v1 + vsh[j + 2] * v2 + vsh[j + 3] * v3;
       }
-      for (; j < n; ++j) acc[k] += wsh[j] * *(const f32x4*)(base + j * stride);
+      for (; j < n; ++j) acc[k] += vsh[j] * *(const f32x4*)(base + j * stride);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

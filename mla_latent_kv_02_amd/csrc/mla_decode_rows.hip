@@ -39,20 +39,147 @@
 namespace mla {
 namespace rows {
 
-constexpr int NT = 512;                  // 8 wavefronts, two per SIMD
+constexpr int NT = 256;                  // 4 wavefronts, one per SIMD
 constexpr int ROWS = 128;                // query rows per workgroup
+constexpr int RT = 2;                    // 16-row tiles per wavefront
 constexpr int MAX_RANGE_BLOCKS = 256;    // cache blocks per range (host planner guarantees it)
 constexpr int MAX_ST = 2 * MAX_RANGE_BLOCKS;
 constexpr int ST_BYTES = ST_ELEMS * 2;   // one bf16 stage
+// Log2 headroom of P before a row's running maximum moves: rescaling the AGPR accumulators
+// is slow here, and P <= 2^16 keeps every sum well inside fp32 (at most 2^17 tokens per piece).
+constexpr float ROWS_SLACK = 16.f;
+static_assert(MAX_RANGE_BLOCKS <= NT, "one thread per block of a range builds the stage table");
 
-// 16 bytes per lane HBM -> LDS; lane i writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).
-// One wait state between the M0 write and the DMA that reads it.
-// The kernel makes no other use of M0.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
-                   __builtin_amdgcn_readfirstlane(lds_base)),
-               "v"(src)
+// 16 bytes per lane HBM -> LDS from base + off (base wave-uniform, off per lane); lane i writes
+// LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).  The addresses are precomputed per lane:
+// with one wavefront per SIMD, VALU address arithmetic for each DMA instruction stalls the
+// MFMA stream more than the copy itself.  One wait state between the M0 write and the DMA
+// that reads it; the kernel makes no other use of M0.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
                : "memory", "m0");
+}
+
+// Score MFMAs, v_mfma_f32_16x16x32_bf16 with VGPR accumulators.  The compiler gives every
+// MFMA of a function the same accumulator register file, and the O^T accumulators fill the
+// 256 AGPRs; written as inline asm, the score MFMAs keep theirs in VGPRs.  The compiler
+// inserts no hazard waits around inline asm, so each group of four starts with two wait
+// states (a VALU write of an operand may precede it; dependent MFMA accumulation is
+// interlocked by the hardware) and the last group waits out the MFMA latency before any
+// other instruction can read the results.  c[tt][rt] += a[tt] . q[rt].
+__device__ __forceinline__ void score4_first(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0,
+                                             const bf16x8& q1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
+      : "=&v"(c[0][0]), "=&v"(c[0][1]), "=&v"(c[1][0]), "=&v"(c[1][1])
+      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
+}
+__device__ __forceinline__ void score4(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0, const bf16x8& q1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
+      : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[1][0]), "+v"(c[1][1])
+      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
+}
+__device__ __forceinline__ void score4_last(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0,
+                                            const bf16x8& q1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+      : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[1][0]), "+v"(c[1][1])
+      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
+}
+
+// O^T MFMAs on AGPR accumulators, also inline asm, and so is every other access to those
+// accumulators: when C code reads them (a rescale, the final store), the compiler moves all
+// 256 through VGPRs and spills.  c0 += v . p0, c1 += v . p1 (FRESH: c = v . p, the first
+// step of a piece).  The first pair of a step waits two states for the VALU that wrote p0 /
+// p1; the last waits out the MFMA latency before anything else reads the accumulators.
+template <int POS, bool FRESH>   // POS 0: first of the step, 1: middle, 2: last
+__device__ __forceinline__ void pv2(f32x4& c0, f32x4& c1, const bf16x8& v, const bf16x8& p0, const bf16x8& p1) {
+#define MLA_PV_NOP0 "s_nop 1\n\t"
+#define MLA_PV_ACC "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
+#define MLA_PV_NEW "v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, 0"
+#define MLA_PV_DRAIN "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+  if constexpr (FRESH) {
+    if constexpr (POS == 0)
+      asm volatile(MLA_PV_NOP0 MLA_PV_NEW : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    else if constexpr (POS == 1)
+      asm volatile(MLA_PV_NEW : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    else
+      asm volatile(MLA_PV_NEW MLA_PV_DRAIN : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
+  } else {
+    if constexpr (POS == 0)
+      asm volatile(MLA_PV_NOP0 MLA_PV_ACC : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    else if constexpr (POS == 1)
+      asm volatile(MLA_PV_ACC : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    else
+      asm volatile(MLA_PV_ACC MLA_PV_DRAIN : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
+  }
+#undef MLA_PV_NOP0
+#undef MLA_PV_ACC
+#undef MLA_PV_NEW
+#undef MLA_PV_DRAIN
+}
+
+// c *= a (a per lane) for an AGPR tile, through 16 bytes per lane of this wave's LDS scratch:
+// inline asm cannot name the four registers of a tile one by one, and VALU instructions
+// cannot read AGPRs.  LDS operations of one wave complete in order.  Slow (two LDS round
+// trips) but rare: only when a row's running maximum moves.
+__device__ __forceinline__ void scale_tile(f32x4& c, float a, uint32_t lds) {
+  float x0, x1, x2, x3;
+  asm volatile(
+      "ds_write_b128 %5, %4\n\t"
+      "ds_read_b32 %0, %5\n\t"
+      "ds_read_b32 %1, %5 offset:4\n\t"
+      "ds_read_b32 %2, %5 offset:8\n\t"
+      "ds_read_b32 %3, %5 offset:12\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mul_f32 %0, %0, %6\n\t"
+      "v_mul_f32 %1, %1, %6\n\t"
+      "v_mul_f32 %2, %2, %6\n\t"
+      "v_mul_f32 %3, %3, %6\n\t"
+      "ds_write_b32 %5, %0\n\t"
+      "ds_write_b32 %5, %1 offset:4\n\t"
+      "ds_write_b32 %5, %2 offset:8\n\t"
+      "ds_write_b32 %5, %3 offset:12\n\t"
+      "ds_read_b128 %4, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "+a"(c)
+      : "v"(lds), "v"(a)
+      : "memory");
+}
+
+// 16 bytes of an AGPR tile to global memory (counted by vmcnt like the stage loads)
+__device__ __forceinline__ void store_tile(float* dst, const f32x4& c) {
+  asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "a"(c) : "memory");
+}
+
+// Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the gfx950 lane
+// swaps: with both operands equal, permlane32_swap / permlane16_swap return x at l and at l ^ 32
+// (l ^ 16), so one max / add per step gives the butterfly without an LDS round trip.
+__device__ __forceinline__ float max_lg(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_lg(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
@@ -71,29 +198,31 @@ __device__ __forceinline__ bf16x8 load_q8(const void* base, size_t elem_off, boo
 }
 
 // ----------------------------------------------------------------------------------------
-// Stage producers: every wave issues a fixed number of DMA instructions per stage, so its
-// count of outstanding stage loads is known exactly.
+// Stage producers: every thread issues LOADS DMA instructions per stage, one call of
+// issue_one(i) each, so a wave's count of outstanding stage loads is known exactly.
 // ----------------------------------------------------------------------------------------
 
-// bf16 rows: a half block is 32 tokens x 72 pieces = 2304 pieces; waves 0-3 issue 5 DMA
-// instructions, waves 4-7 issue 4.  Slot k of the stage receives (token k / 72, logical piece
-// (k mod 72) ^ sw(token)); tokens >= valid read the half block's first piece instead (and are
-// zeroed before use).
+// bf16 rows: a half block is 32 tokens x 72 pieces = 2304 pieces, 9 per thread.  Slot k of the
+// stage receives (token k / 72, logical piece (k mod 72) ^ sw(token)).  All 32 rows are copied
+// (a block is always allocated whole); rows past the sequence end are zeroed before use.
 struct BfProducer {
-  static constexpr int LOADS_LO = 5, LOADS_HI = 4;
-  __device__ __forceinline__ static void issue(const uint8_t* half, int valid, uint32_t stage, int tid) {
-    // recomputed per stage: keeping the per-slot offsets live across the loop costs registers
-    asm volatile("" : "+v"(tid));
-    const int wbase = tid & ~63;
+  static constexpr int LOADS = ST_TOK * 72 / NT;
+  static_assert(LOADS * NT == ST_TOK * 72, "threads must divide the stage");
+  struct Offsets {
+    uint32_t o[LOADS];
+  };
+  __device__ static Offsets offsets(int tid) {
+    Offsets r;
 #pragma unroll
-    for (int i = 0; i < LOADS_LO; ++i) {
-      if (i == LOADS_HI && tid >= 256) break;
+    for (int i = 0; i < LOADS; ++i) {
       const int slot = i * NT + tid;
       const int t = slot / 72;
-      const int c = (slot - t * 72) ^ sw(t);
-      const uint8_t* src = t < valid ? half + t * 1152 + c * 16 : half;
-      dma16(src, stage + (uint32_t)(i * NT + wbase) * 16);
+      r.o[i] = (uint32_t)(t * 1152 + (((slot - t * 72) ^ sw(t)) << 4));
     }
+    return r;
+  }
+  __device__ __forceinline__ static void issue_one(int i, const Offsets& off, const uint8_t* half, uint32_t lds) {
+    dma16(half, off.o[i], lds + (uint32_t)(i * NT * 16));
   }
 };
 
@@ -105,82 +234,91 @@ struct QuantStage {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
   static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
   static constexpr int PPT = LB / 16;              // latent code pieces per token
-  // waves 0-3 issue LOADS_LO DMA instructions per stage, waves 4-7 LOADS_HI
-  static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;
-  static constexpr int LOADS_HI = 1;
-  static constexpr int SLOTS = FMT == FMT_INT4 ? 768 : 512;   // INT4: 648 used, INT2: 456
+  static constexpr int LOADS = FMT == FMT_INT4 ? 3 : 2;
+  static constexpr int SLOTS = LOADS * NT;         // INT4: 648 used, INT2: 456
   static constexpr int DEPTH = FMT == FMT_INT4 ? 6 : 8;   // code ring slots
 
-  __device__ __forceinline__ static void issue(const uint8_t* blk, int half, const QuantPlanes& pl, int groups,
-                                               int rgroups, uint32_t cstage, int tid) {
-    asm volatile("" : "+v"(tid));   // recomputed per stage, as for bf16 stages
+  // per-lane source offsets inside a block of DMA instruction i, for the block's two halves
+  struct Offsets {
+    uint32_t o[2][LOADS];
+  };
+  __device__ static Offsets offsets(const QuantPlanes& pl, int groups, int rgroups, int tid) {
     const int n_lc = ST_TOK * LB / 16;
     const int n_ls = ST_TOK * groups * 4 / 16;
     const int n_rc = ST_TOK * 32 / 16;
     const int n_rs = (ST_TOK * rgroups * 4 + 15) / 16;
     const int n_all = n_lc + n_ls + n_rc + n_rs;
-    const uint8_t* lc = blk + pl.lc + half * ST_TOK * LB;
-    const uint8_t* ls = blk + pl.ls + half * ST_TOK * groups * 4;
-    const uint8_t* rc = blk + pl.rc + half * ST_TOK * 32;
-    const uint8_t* rs = blk + pl.rs + half * ST_TOK * rgroups * 4;
-    const int wbase = tid & ~63;
+    Offsets r;
 #pragma unroll
-    for (int i = 0; i < LOADS_LO; ++i) {
-      if (i == LOADS_HI && tid >= 256) break;
+    for (int i = 0; i < LOADS; ++i) {
       const int slot = i * NT + tid;
-      int p = slot < n_all ? slot : slot - n_all;   // padding slots re-load a real piece
-      const uint8_t* src;
-      if (p < n_lc) {
-        src = lc + ((p % ST_TOK) * PPT + p / ST_TOK) * 16;
-      } else if ((p -= n_lc) < n_ls) {
-        src = ls + p * 16;
-      } else if ((p -= n_ls) < n_rc) {
-        src = rc + ((p % ST_TOK) * 2 + p / ST_TOK) * 16;
+      int q = slot < n_all ? slot : slot - n_all;   // padding slots re-load a real piece
+      int base, hstride;
+      if (q < n_lc) {
+        base = pl.lc + ((q % ST_TOK) * PPT + q / ST_TOK) * 16;
+        hstride = ST_TOK * LB;
+      } else if ((q -= n_lc) < n_ls) {
+        base = pl.ls + q * 16;
+        hstride = ST_TOK * groups * 4;
+      } else if ((q -= n_ls) < n_rc) {
+        base = pl.rc + ((q % ST_TOK) * 2 + q / ST_TOK) * 16;
+        hstride = ST_TOK * 32;
       } else {
-        src = rs + (p - n_rc) * 16;
+        base = pl.rs + (q - n_rc) * 16;
+        hstride = ST_TOK * rgroups * 4;
       }
-      dma16(src, cstage + (uint32_t)(i * NT + wbase) * 16);
+      r.o[0][i] = (uint32_t)base;
+      r.o[1][i] = (uint32_t)(base + hstride);
     }
+    return r;
+  }
+  __device__ __forceinline__ static void issue_one(int i, const Offsets& off, const uint8_t* blk, int half,
+                                                   uint32_t lds) {
+    dma16(blk, half ? off.o[1][i] : off.o[0][i], lds + (uint32_t)(i * NT * 16));
   }
 
-  // Thread q dequantises latent chunk kk = q / 32 (32 elements, inside one quantisation group
-  // since groups are multiples of 32) of token t = q mod 32; threads q < 256 also dequantise
-  // RoPE elements 8 ri .. 8 ri + 7 (ri = q / 32) of token t.  Group sizes are powers of two
-  // (gl = log2 latent group, gr = log2 rope group).  Offsets are recomputed every stage: a few
-  // ALU operations instead of registers held across the loop.
+  // Thread q dequantises latent chunks kk and kk + 8 (kk = q / 32; 32 elements each, inside
+  // one quantisation group since groups are multiples of 32) and RoPE elements 8 kk .. 8 kk + 7
+  // of token t = q mod 32.  Group sizes are powers of two (gl = log2 latent group, gr = log2
+  // rope group).  Offsets are recomputed every stage: a few ALU operations instead of
+  // registers held across the loop.
   __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, int gl, int gr, bf16_t* stage,
                                                  int tid) {
     asm volatile("" : "+v"(tid));
-    const int t = tid & 31, kk = tid >> 5;
+    const int t = tid & 31, kk0 = tid >> 5;
     const int groups_log2 = 9 - gl;
     const bool ok = t < valid;
     const int row = t * 576;
     const int ls = ST_TOK * LB;                    // scale plane of the latent codes
-    uint32_t sz = *(const uint32_t*)(cst + ls + (((t << groups_log2) + ((kk * 32) >> gl)) << 2));
-    sz = ok ? sz : 0u;
-    float s, zs;
-    scale_zero(sz, s, zs);
-    const int p0 = (4 * kk) ^ sw(t);
-    const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
-    const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
-    if constexpr (BITS == 4) {
-      const u32x4 c = *(const u32x4*)code;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
-        __builtin_amdgcn_sched_barrier(0);     // one piece at a time: few registers
-      }
-    } else {
-      const uint2 c = *(const uint2*)code;
+    for (int h = 0; h < 2; ++h) {
+      const int kk = kk0 + 8 * h;
+      uint32_t sz = *(const uint32_t*)(cst + ls + (((t << groups_log2) + ((kk * 32) >> gl)) << 2));
+      sz = ok ? sz : 0u;
+      float s, zs;
+      scale_zero(sz, s, zs);
+      const int p0 = (4 * kk) ^ sw(t);
+      const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
+      const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
+      if constexpr (BITS == 4) {
+        const u32x4 c = *(const u32x4*)code;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t wd = j < 2 ? c.x : c.y;
-        *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int2x8(j & 1 ? wd >> 16 : wd & 0xFFFFu, s, zs);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) {
+          *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
+          __builtin_amdgcn_sched_barrier(0);     // one piece at a time: few registers
+        }
+      } else {
+        const uint2 c = *(const uint2*)code;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wd = j < 2 ? c.x : c.y;
+          *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int2x8(j & 1 ? wd >> 16 : wd & 0xFFFFu, s, zs);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    if (tid < 256) {
-      const int ri = kk & 7;
+    {
+      const int ri = kk0;
       const int rbase = ls + (ST_TOK << (groups_log2 + 2));
       const int rgroups_log2 = 6 - gr;
       uint32_t rsz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << rgroups_log2) + ((ri * 8) >> gr)) << 2));
@@ -196,7 +334,6 @@ struct QuantStage {
 // Stage table entry flags (st_info): sequence index in bits 0..19, valid tokens in 20..25.
 constexpr int INFO_START = 1 << 26;   // first stage of a piece (a sequence's blocks inside one range)
 constexpr int INFO_END = 1 << 27;     // last stage of a piece
-constexpr int INFO_WHOLE = 1 << 28;   // the piece is the whole sequence
 
 // ----------------------------------------------------------------------------------------
 // The kernel
@@ -215,6 +352,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   __shared__ int st_info[MAX_ST];
   __shared__ int st_len[MAX_ST];
   __shared__ int sh_scan[NT / 64 + 1];
+  __shared__ f32x4 resc[NT];         // per-lane scratch of scale_tile
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -312,31 +450,37 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     return lo;
   };
 
-  // ---- per-wave state: rows rg * 128 + 16 w + lr
-  const int rowg = rg * ROWS + 16 * w + lr;
-  const bool row_ok = rowg < R;
-  bf16x8 qreg[18];
-  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
-  int lim = -1;
-  f32x4 acc[32];
+  // ---- per-wave state: rows row0 + 16 rt, row0 = rg * 128 + 32 w + lr
+  const int row0 = rg * ROWS + 32 * w + lr;
+  bf16x8 qreg[RT][18];
+  float m_s[RT], l_s[RT], l_x[RT];
+  int lim[RT];
+  int lim_all = -1;   // every query row of the piece attends tokens 0 .. lim_all (L - s_q)
+  f32x4 acc[RT][32];
 
   // new piece: this sequence's queries, fresh softmax state
   int cur_b = -1;
+  bool fresh = true;
   auto start_piece = [&](int b, int L) {
     cur_b = b;
-    const size_t qb = (size_t)cur_b * R + (row_ok ? rowg : 0);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      qreg[ks] = row_ok ? load_q8(p.q_lat, qb * 512 + ks * 32 + lg * 8, QF32) : bf16x8{};
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = row0 + 16 * rt;
+      const bool ok = row < R;
+      const size_t qb = (size_t)cur_b * R + (ok ? row : 0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      qreg[16 + ks] = row_ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
-    lim = row_ok ? L - p.s_q + rowg / p.H : -1;
-    m_s = NEG_INF;
-    l_s = 0.f;
-    l_x = 0.f;
+      for (int ks = 0; ks < 16; ++ks)
+        qreg[rt][ks] = ok ? load_q8(p.q_lat, qb * 512 + ks * 32 + lg * 8, QF32) : bf16x8{};
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 2; ++ks)
+        qreg[rt][16 + ks] = ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
+      lim[rt] = ok ? L - p.s_q + row / p.H : -1;
+      m_s[rt] = NEG_INF;
+      l_s[rt] = 0.f;
+      l_x[rt] = 0.f;
+    }
+    lim_all = L - p.s_q;
+    fresh = true;   // the first step's P.V MFMAs start the accumulators from zero
     // wait here, on this rare path: a load the compiler sees pending at the loop's back edge
     // would make it wait for every stage in flight at the top of every step
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -361,12 +505,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       id = 0;
       v = 0;
     }
-    const bool whole = P0 >= start && P1 <= end;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = 2 * tid + h;
       const int valid = min(ST_TOK, max(0, v - ST_TOK * h));
-      int info = b | (valid << 20) | (whole ? INFO_WHOLE : 0);
+      int info = b | (valid << 20);
       if (h == 0 && (tid == 0 || jb == 0)) info |= INFO_START;
       if (h == 1 && (tid == nblk - 1 || j == P1 - 1)) info |= INFO_END;
       st_bid[k] = id;
@@ -386,25 +529,40 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   // code slot k at 2 * ST_BYTES + k * CBYTES
   auto bf_stage = [&](int k) -> bf16_t* { return (bf16_t*)(smem + k * ST_BYTES); };
   auto code_slot = [&](int k) -> int { return 2 * ST_BYTES + k * CBYTES; };
-  auto issue = [&](int s) {
+  constexpr int LOADS = QUANT ? QS::LOADS : BfProducer::LOADS;
+  // source of stage s: its block and which half (wave-uniform)
+  struct Src {
+    const uint8_t* blk;
+    int half;
+  };
+  auto src_of = [&](int s) {
     const int id = __builtin_amdgcn_readfirstlane(st_bid[s]);
-    const int info = __builtin_amdgcn_readfirstlane(st_info[s]);
-    const uint8_t* blk = p.pool + (size_t)id * (size_t)p.block_bytes;
-    const int half = (__builtin_amdgcn_readfirstlane(st_tok[s]) / ST_TOK) & 1;
+    return Src{p.pool + (size_t)id * (size_t)p.block_bytes, (__builtin_amdgcn_readfirstlane(st_tok[s]) / ST_TOK) & 1};
+  };
+  // per-lane DMA source offsets (held for the whole kernel) and this wave's LDS slice
+  const uint32_t wlds = (uint32_t)__builtin_amdgcn_readfirstlane((tid & ~63) * 16);
+  const auto offs = [&] {
+    if constexpr (QUANT) return QS::offsets(pl, groups, rgroups, tid);
+    else return BfProducer::offsets(tid);
+  }();
+  // DMA instruction i of stage s
+  auto issue_one = [&](int s, const Src& sr, int i) {
     if constexpr (QUANT) {
-      QS::issue(blk, half, pl, groups, rgroups, smem_base + code_slot(s % DEPTH), tid);
+      QS::issue_one(i, offs, sr.blk, sr.half, smem_base + code_slot(s % DEPTH) + wlds);
     } else {
-      BfProducer::issue(blk + half * ST_TOK * 1152, (info >> 20) & 63, smem_base + (s & 3) * ST_BYTES, tid);
+      BfProducer::issue_one(i, offs, sr.blk + sr.half * ST_TOK * 1152, smem_base + (s & 3) * ST_BYTES + wlds);
     }
   };
+  auto issue = [&](int s) {
+    const Src sr = src_of(s);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) issue_one(s, sr, i);
+  };
   // wait until a stage has landed, given how many later stages were issued after it
-  constexpr int LA = QUANT ? QS::LOADS_LO : BfProducer::LOADS_LO;
-  constexpr int LB = QUANT ? QS::LOADS_HI : BfProducer::LOADS_HI;
   auto wait_stage = [&](int later) {
     auto wait_k = [&](auto K) {
       constexpr int k = decltype(K)::value;
-      if (w < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(k * LA));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(k * LB));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(k * LOADS));
     };
     switch (later) {
       case 0: wait_k(std::integral_constant<int, 0>{}); break;
@@ -413,10 +571,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       case 3: wait_k(std::integral_constant<int, 3>{}); break;
       case 4: wait_k(std::integral_constant<int, 4>{}); break;
       case 5: wait_k(std::integral_constant<int, 5>{}); break;
-      default: wait_k(std::integral_constant<int, 6>{}); break;
+      case 6: wait_k(std::integral_constant<int, 6>{}); break;
+      default: wait_k(std::integral_constant<int, 7>{}); break;
     }
   };
-  static_assert((QUANT ? DEPTH - 2 : 2) <= 6 && 6 * LA <= 63, "stage waits out of range");
+  static_assert((QUANT ? DEPTH - 1 : 2) <= 7 && 7 * LOADS <= 63, "stage waits out of range");
 
   // prologue.  bf16: stages 0..2 in flight, stage 0 landed.  Quantised: codes 0..DEPTH-1 in
   // flight, code 0 dequantised into bf16 stage 0, code 1 landed.
@@ -439,12 +598,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     const int valid = (info >> 20) & 63;
     const int stok = __builtin_amdgcn_readfirstlane(st_tok[s]);
     if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]));
-    // refill the ring: the slot of stage s-1 (bf16) / code s (dequantised in step s-1)
-    if constexpr (!QUANT) {
-      if (s + 3 < nst) issue(s + 3);
-    } else {
-      if (s + DEPTH < nst) issue(s + DEPTH);
-    }
+    // the ring slot refilled in this step: stage s + 3 into the slot of stage s - 1 (bf16) /
+    // code s + DEPTH into the slot of code s (dequantised in step s - 1)
+    const int s_new = QUANT ? s + DEPTH : s + 3;
+    const bool refill = s_new < nst;
+    const Src sr_new = src_of(refill ? s_new : s);
     const bf16_t* KS = QUANT ? bf_stage(s & 1) : bf_stage(s & 3);
     if (!QUANT && valid < ST_TOK) {
       // rows past the sequence end came from a stand-in address: zero them
@@ -460,8 +618,9 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
                     p.g_lat_log2, p.g_rope_log2, bf_stage((s + 1) & 1), tid);
     }
 
-    // ---- scores S^T[token][row] for token tiles tt (two accumulation chains each)
-    f32x4 sc[2];
+    // ---- scores S^T[token][row] for token tiles tt and row tiles rt; the refill's DMA
+    // instructions are spread over the k-steps so that they queue behind MFMA work
+    f32x4 sc[2][RT];
     {
       const bf16_t* kb[2][2];
       int lr_ = lr;
@@ -472,11 +631,8 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         const int f = sw(t);
         kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
         kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
-        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // software pipeline: the fragments of k-step ks + 1 are read while k-step ks multiplies;
-      // the two token tiles' chains interleave and two waves per SIMD hide the MFMA latency
-      constexpr int KD = 2;   // prefetch depth in k-steps
+      constexpr int KD = 2;   // prefetch depth in k-steps (deeper gains nothing: the loop is MFMA-issue bound)
       bf16x8 a[KD + 1][2];
 #pragma unroll
       for (int i = 0; i < KD; ++i)
@@ -489,55 +645,76 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
           for (int tt = 0; tt < 2; ++tt)
             a[(ks + KD) % (KD + 1)][tt] = *(const bf16x8*)(kb[tt][(ks + KD) & 1] + (ks + KD) * 32);
         }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % (KD + 1)][tt], qreg[ks], sc[tt], 0, 0, 0);
+        if ((ks & 1) && (ks >> 1) < LOADS && refill) issue_one(s_new, sr_new, ks >> 1);
+        if (ks == 0) score4_first(sc, a[0], qreg[0][0], qreg[1][0]);
+        else if (ks == 17) score4_last(sc, a[ks % (KD + 1)], qreg[0][ks], qreg[1][ks]);
+        else score4(sc, a[ks % (KD + 1)], qreg[0][ks], qreg[1][ks]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    // ---- softmax of row lr (this lane holds tokens 16 tt + 4 lg + i)
-    float x[2][4];
-    float mt = NEG_INF;
-    {
-      // token k = 16 tt + 4 lg + i is kept if k < valid and stok + k <= lim
-      const int kb4 = 4 * lg;
-      const int lim_k = min(valid - 1, lim - stok);
+    // ---- softmax of rows row0 + 16 rt (this lane holds tokens 16 tt + 4 lg + i).  On most
+    // steps every token of the stage is visible to every row: no per-token mask.
+    bf16x8 pt[RT];
+    float al[RT];
+    auto softmax = [&](auto FULL) {
+      constexpr bool F = decltype(FULL)::value;
+      float mt[RT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int rt = 0; rt < RT; ++rt) {
+        // token k = 16 tt + 4 lg + i is kept if k < valid and stok + k <= lim
+        const int kb4 = 4 * lg;
+        const int lim_k = min(valid - 1, lim[rt] - stok);
+        mt[rt] = NEG_INF;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = kb4 <= lim_k - (16 * tt + i);
-          x[tt][i] = ok ? sc[tt][i] * p.scale_log2 : NEG_INF;
-          mt = fmaxf(mt, x[tt][i]);
-        }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
-    const float mu = mn == NEG_INF ? 0.f : mn;
-    const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
-    l_s *= al;
-    l_x *= al;
-    m_s = mn;
-    uint32_t pw[4];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      uint32_t pb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pf = __builtin_amdgcn_exp2f(x[tt][i] - mu);
-        pb[i] = f32_to_bf16_bits(pf);
-        l_s += bf16_bits_to_f32(pb[i]);
-        l_x += pf;
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (F) {
+              sc[tt][rt][i] *= p.scale_log2;
+            } else {
+              const bool ok = kb4 <= lim_k - (16 * tt + i);
+              sc[tt][rt][i] = ok ? sc[tt][rt][i] * p.scale_log2 : NEG_INF;
+            }
+            mt[rt] = fmaxf(mt[rt], sc[tt][rt][i]);
+          }
       }
-      pw[2 * tt] = pb[0] | (pb[1] << 16);
-      pw[2 * tt + 1] = pb[2] | (pb[3] << 16);
-    }
-    const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-    if (__any(al != 1.f)) {
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) acc[nt] *= al;
+      for (int rt = 0; rt < RT; ++rt) mt[rt] = max_lg(mt[rt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float mn = mt[rt] > m_s[rt] + ROWS_SLACK ? mt[rt] : m_s[rt];
+        const float mu = mn == NEG_INF ? 0.f : mn;
+        // while m_s = -inf every P so far was 0 and the accumulators hold zeros: nothing to scale
+        al[rt] = (mn == m_s[rt] || m_s[rt] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_s[rt] - mu);
+        l_s[rt] *= al[rt];
+        l_x[rt] *= al[rt];
+        m_s[rt] = mn;
+        uint32_t pw[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          uint32_t pb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pf = __builtin_amdgcn_exp2f(sc[tt][rt][i] - mu);
+            pb[i] = f32_to_bf16_bits(pf);
+            l_s[rt] += bf16_bits_to_f32(pb[i]);
+            l_x[rt] += pf;
+          }
+          pw[2 * tt] = pb[0] | (pb[1] << 16);
+          pw[2 * tt + 1] = pb[2] | (pb[3] << 16);
+        }
+        pt[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      }
+    };
+    if (valid == ST_TOK && stok + (ST_TOK - 1) <= lim_all) softmax(std::true_type{});
+    else softmax(std::false_type{});
+    if (!fresh && __any(al[0] != 1.f || al[1] != 1.f)) {
+      const uint32_t sa = lds_addr(&resc[tid]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) scale_tile(acc[rt][nt], al[rt], sa);
     }
 
     // ---- O^T[col][row] += V^T[col][token] . P^T[token][row]; the 8 tokens of lane group lg
@@ -556,52 +733,50 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       int oa[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
-      // software pipeline: the V^T fragment of tile nt + 2 is read while tile nt multiplies
+      // software pipeline: the V^T fragment of tile nt + PD is read while tile nt multiplies
       auto vfrag = [&](int nt) {
         const int q = nt >> 2, r = nt & 3;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + 64 * q]);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + db + 64 * q]);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int PD = 4;   // prefetch depth
-      bf16x8 va[PD + 1];
+      constexpr int PD = 2;   // prefetch depth
+      auto pv_loop = [&](auto FR) {
+        constexpr bool F = decltype(FR)::value;
+        bf16x8 va[PD + 1];
 #pragma unroll
-      for (int i = 0; i < PD; ++i) va[i] = vfrag(i);
+        for (int i = 0; i < PD; ++i) va[i] = vfrag(i);
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) {
-        if (nt + PD < 32) va[(nt + PD) % (PD + 1)] = vfrag(nt + PD);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nt % (PD + 1)], pt, acc[nt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int nt = 0; nt < 32; ++nt) {
+          if (nt + PD < 32) va[(nt + PD) % (PD + 1)] = vfrag(nt + PD);
+          if (nt == 0) pv2<0, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
+          else if (nt == 31) pv2<2, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
+          else pv2<1, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (fresh) pv_loop(std::true_type{});
+      else pv_loop(std::false_type{});
+      fresh = false;
     }
 
-    // ---- end of a piece: normalise and write this wave's rows
+    // ---- end of a piece: this wave's rows, unnormalised, with 1 / sum(P) and the lse, to
+    // slot cur_b + range; the combine normalises (a range's pieces have distinct slots)
     if (info & INFO_END) {
-      const bool whole = info & INFO_WHOLE;
-      const size_t slot = whole ? (size_t)cur_b : (size_t)cur_b + range;
-      float ls = l_s, lx = l_x;
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      lx += __shfl_xor(lx, 16, 64);
-      lx += __shfl_xor(lx, 32, 64);
-      if (row_ok) {
-        const float inv = ls > 0.f ? 1.f / ls : 0.f;
-        const size_t ob = (slot * R + rowg) * 512 + 4 * lg;
-        if (whole && p.out_bf16) {
-          bf16_t* o = (bf16_t*)p.out;
+      const size_t slot = (size_t)cur_b + range;
 #pragma unroll
-          for (int nt = 0; nt < 32; ++nt) {
-            const f32x4 v = acc[nt] * inv;
-            *(uint2*)(o + ob + nt * 16) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = row0 + 16 * rt;
+        const float ls = sum_lg(l_s[rt]), lx = sum_lg(l_x[rt]);
+        if (row < R) {
+          float* o = p.part_o + (slot * R + row) * 512 + 4 * lg;
+#pragma unroll
+          for (int nt = 0; nt < 32; ++nt) store_tile(o + nt * 16, acc[rt][nt]);
+          if (lg == 0) {
+            p.part_lse[slot * R + row] = lx > 0.f ? (m_s[rt] + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
+            p.part_inv[slot * R + row] = ls > 0.f ? 1.f / ls : 0.f;
           }
-        } else {
-          float* o = whole ? (float*)p.out : p.part_o;
-#pragma unroll
-          for (int nt = 0; nt < 32; ++nt) *(f32x4*)(o + ob + nt * 16) = acc[nt] * inv;
         }
-        float* lse_out = whole ? p.out_lse : p.part_lse;
-        if (lg == 0 && lse_out != nullptr)
-          lse_out[slot * R + rowg] = lx > 0.f ? (m_s + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
     }

@@ -31,9 +31,10 @@ struct DecodeParams {
 
 // Arguments of the row-owner decode kernel (128 query rows per workgroup).  The batch's
 // cache blocks, sequence after sequence, are cut into n_ranges equal ranges; workgroup
-// (range i, row group r) attends its rows over the blocks of range i.  A sequence that one
-// range covers entirely is written to out/out_lse directly; a sequence cut by ranges leaves
-// one partial (o normalised, lse) per piece in slot b + i of part_o/part_lse.
+// (range i, row group r) attends its rows over the blocks of range i.  Every piece (the
+// blocks of one sequence inside one range) leaves a partial in slot b + i: o unnormalised,
+// 1 / sum(P) and lse; the combine normalises and merges.  Empty sequences are written to
+// out/out_lse directly.
 struct RowsParams {
   const void* q_lat;        // [B][R][512]
   const void* q_rope;       // [B][R][64]
@@ -55,15 +56,18 @@ struct RowsParams {
   float* out_lse;           // [B][R], may be null
   float* part_o;            // [B + n_ranges - 1][R][512]
   float* part_lse;          // [B + n_ranges - 1][R]
+  float* part_inv;          // [B + n_ranges - 1][R]
   int32_t* meta;            // [0]: blocks per range; [1 + b]: first block of sequence b, b <= B
 };
 
 // Combine of split partials.  Partition mode (meta == null): max_chunks partitions of tpc
-// blocks per sequence, slot b * max_chunks + c.  Range mode: pieces of the ranges in meta,
-// slots b + i; sequences inside one range were written by the decode kernel.
+// blocks per sequence, slot b * max_chunks + c, o normalised.  Range mode: pieces of the
+// ranges in meta, slots b + i, o unnormalised with its factor in part_inv; every non-empty
+// sequence is combined (one piece included).
 struct CombineParams {
   const float* part_o;
   const float* part_lse;
+  const float* part_inv;    // range mode only
   const int32_t* seq_lens;
   int max_seq_len;
   int R, d_c, max_chunks, tpc;
