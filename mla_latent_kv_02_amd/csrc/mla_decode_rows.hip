@@ -63,69 +63,52 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_
 // Score MFMAs, v_mfma_f32_16x16x32_bf16 with VGPR accumulators.  The compiler gives every
 // MFMA of a function the same accumulator register file, and the O^T accumulators fill the
 // 256 AGPRs; written as inline asm, the score MFMAs keep theirs in VGPRs.  The compiler
-// inserts no hazard waits around inline asm, so each group of four starts with two wait
-// states (a VALU write of an operand may precede it; dependent MFMA accumulation is
-// interlocked by the hardware) and the last group waits out the MFMA latency before any
-// other instruction can read the results.  c[tt][rt] += a[tt] . q[rt].
-__device__ __forceinline__ void score4_first(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0,
-                                             const bf16x8& q1) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
-      : "=&v"(c[0][0]), "=&v"(c[0][1]), "=&v"(c[1][0]), "=&v"(c[1][1])
-      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
-}
-__device__ __forceinline__ void score4(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0, const bf16x8& q1) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
-      : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[1][0]), "+v"(c[1][1])
-      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
-}
-__device__ __forceinline__ void score4_last(f32x4 (&c)[2][RT], const bf16x8 (&a)[2], const bf16x8& q0,
-                                            const bf16x8& q1) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 3"
-      : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[1][0]), "+v"(c[1][1])
-      : "v"(a[0]), "v"(a[1]), "v"(q0), "v"(q1));
+// inserts no hazard waits around inline asm: the first pair of a step starts with two wait
+// states (the VALU may just have written an operand; the other pairs read only LDS loads and
+// the query registers), dependent MFMA accumulation is interlocked by the hardware, and the
+// last pair waits out the MFMA latency before anything else can read the results.
+// c0 += a . q0, c1 += a . q1 (FIRST: c = a . q).
+template <bool FIRST, bool NOP, bool DRAIN>
+__device__ __forceinline__ void score2(f32x4& c0, f32x4& c1, const bf16x8& a, const bf16x8& q0, const bf16x8& q1) {
+#define MLA_S_NOP0 "s_nop 1\n\t"
+#define MLA_S_ACC "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
+#define MLA_S_NEW "v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, 0"
+#define MLA_S_DRAIN "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+  if constexpr (FIRST) {
+    if constexpr (NOP)
+      asm volatile(MLA_S_NOP0 MLA_S_NEW : "=&v"(c0), "=&v"(c1) : "v"(a), "v"(q0), "v"(q1));
+    else
+      asm volatile(MLA_S_NEW : "=&v"(c0), "=&v"(c1) : "v"(a), "v"(q0), "v"(q1));
+  } else if constexpr (DRAIN) {
+    asm volatile(MLA_S_ACC MLA_S_DRAIN : "+v"(c0), "+v"(c1) : "v"(a), "v"(q0), "v"(q1));
+  } else {
+    asm volatile(MLA_S_ACC : "+v"(c0), "+v"(c1) : "v"(a), "v"(q0), "v"(q1));
+  }
+#undef MLA_S_NOP0
+#undef MLA_S_ACC
+#undef MLA_S_NEW
+#undef MLA_S_DRAIN
 }
 
 // O^T MFMAs on AGPR accumulators, also inline asm, and so is every other access to those
 // accumulators: when C code reads them (a rescale, the final store), the compiler moves all
-// 256 through VGPRs and spills.  c0 += v . p0, c1 += v . p1 (FRESH: c = v . p, the first
-// step of a piece).  The first pair of a step waits two states for the VALU that wrote p0 /
-// p1; the last waits out the MFMA latency before anything else reads the accumulators.
-template <int POS, bool FRESH>   // POS 0: first of the step, 1: middle, 2: last
-__device__ __forceinline__ void pv2(f32x4& c0, f32x4& c1, const bf16x8& v, const bf16x8& p0, const bf16x8& p1) {
+// 256 through VGPRs and spills.  c += v . p (FRESH: c = v . p, the first step of a piece).
+// The first MFMA of a step waits two states for the VALU that wrote p; the last waits out
+// the MFMA latency before anything else reads the accumulators.
+template <bool FRESH, bool NOP, bool DRAIN>
+__device__ __forceinline__ void pv1(f32x4& c, const bf16x8& v, const bf16x8& pp) {
 #define MLA_PV_NOP0 "s_nop 1\n\t"
-#define MLA_PV_ACC "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
-#define MLA_PV_NEW "v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %2, %4, 0"
+#define MLA_PV_ACC "v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+#define MLA_PV_NEW "v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
 #define MLA_PV_DRAIN "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
   if constexpr (FRESH) {
-    if constexpr (POS == 0)
-      asm volatile(MLA_PV_NOP0 MLA_PV_NEW : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
-    else if constexpr (POS == 1)
-      asm volatile(MLA_PV_NEW : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
-    else
-      asm volatile(MLA_PV_NEW MLA_PV_DRAIN : "=a"(c0), "=a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    if constexpr (NOP) asm volatile(MLA_PV_NOP0 MLA_PV_NEW : "=a"(c) : "v"(v), "v"(pp));
+    else if constexpr (DRAIN) asm volatile(MLA_PV_NEW MLA_PV_DRAIN : "=a"(c) : "v"(v), "v"(pp));
+    else asm volatile(MLA_PV_NEW : "=a"(c) : "v"(v), "v"(pp));
   } else {
-    if constexpr (POS == 0)
-      asm volatile(MLA_PV_NOP0 MLA_PV_ACC : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
-    else if constexpr (POS == 1)
-      asm volatile(MLA_PV_ACC : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
-    else
-      asm volatile(MLA_PV_ACC MLA_PV_DRAIN : "+a"(c0), "+a"(c1) : "v"(v), "v"(p0), "v"(p1));
+    if constexpr (NOP) asm volatile(MLA_PV_NOP0 MLA_PV_ACC : "+a"(c) : "v"(v), "v"(pp));
+    else if constexpr (DRAIN) asm volatile(MLA_PV_ACC MLA_PV_DRAIN : "+a"(c) : "v"(v), "v"(pp));
+    else asm volatile(MLA_PV_ACC : "+a"(c) : "v"(v), "v"(pp));
   }
 #undef MLA_PV_NOP0
 #undef MLA_PV_ACC
@@ -461,7 +444,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   // new piece: this sequence's queries, fresh softmax state
   int cur_b = -1;
   bool fresh = true;
-  auto start_piece = [&](int b, int L) {
+  auto start_piece = [&](int b, int L, bool wait) {
     cur_b = b;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -483,14 +466,14 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     fresh = true;   // the first step's P.V MFMAs start the accumulators from zero
     // wait here, on this rare path: a load the compiler sees pending at the loop's back edge
     // would make it wait for every stage in flight at the top of every step
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (wait) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
   // The first piece's queries are loaded now, so that their latency overlaps the block-table
   // loads below, and both are complete before the stage ring starts: the compiler, which does
   // not see the ring's DMA, would otherwise wait for every stage in flight before using Q.
   {
     const int b0 = seq_of(start);
-    start_piece(b0, tabL[b0]);
+    start_piece(b0, tabL[b0], false);   // completed with the block-table loads below
   }
 
   // ---- stage table: block j = start + tid -> its sequence, block id and tokens
@@ -593,16 +576,22 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     lds_barrier();
   }
 
+  // the ring slot refilled in step s: stage s + 3 into the slot of stage s - 1 (bf16) / code
+  // s + DEPTH into the slot of code s (dequantised in step s - 1)
+  constexpr int AHEAD = QUANT ? DEPTH : 3;
+  // stage-table entries of step s, read at the end of step s - 1 so that their LDS latency
+  // overlaps the end-of-step wait
+  int n_info = st_info[0], n_tok = st_tok[0];
+  int n_bid = st_bid[min(nst - 1, AHEAD)], n_btok = st_tok[min(nst - 1, AHEAD)];
   for (int s = 0; s < nst; ++s) {
-    const int info = __builtin_amdgcn_readfirstlane(st_info[s]);
+    const int info = __builtin_amdgcn_readfirstlane(n_info);
     const int valid = (info >> 20) & 63;
-    const int stok = __builtin_amdgcn_readfirstlane(st_tok[s]);
-    if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]));
-    // the ring slot refilled in this step: stage s + 3 into the slot of stage s - 1 (bf16) /
-    // code s + DEPTH into the slot of code s (dequantised in step s - 1)
-    const int s_new = QUANT ? s + DEPTH : s + 3;
+    const int stok = __builtin_amdgcn_readfirstlane(n_tok);
+    if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]), true);
+    const int s_new = s + AHEAD;
     const bool refill = s_new < nst;
-    const Src sr_new = src_of(refill ? s_new : s);
+    const Src sr_new{p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
+                     (__builtin_amdgcn_readfirstlane(n_btok) / ST_TOK) & 1};
     const bf16_t* KS = QUANT ? bf_stage(s & 1) : bf_stage(s & 3);
     if (!QUANT && valid < ST_TOK) {
       // rows past the sequence end came from a stand-in address: zero them
@@ -638,17 +627,20 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       for (int i = 0; i < KD; ++i)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) a[i][tt] = *(const bf16x8*)(kb[tt][i & 1] + i * 32);
+      // per k-step: read, MFMA pair (token tile 0), read, MFMA pair (token tile 1): reads issued
+      // between MFMAs keep the matrix pipe busier than reads grouped before four MFMAs
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        if (ks + KD < 18) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-            a[(ks + KD) % (KD + 1)][tt] = *(const bf16x8*)(kb[tt][(ks + KD) & 1] + (ks + KD) * 32);
-        }
+        const int nx = (ks + KD) % (KD + 1), cu = ks % (KD + 1);
+        if (ks + KD < 18) a[nx][0] = *(const bf16x8*)(kb[0][(ks + KD) & 1] + (ks + KD) * 32);
+        if (ks == 0) score2<true, true, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
+        else score2<false, false, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + KD < 18) a[nx][1] = *(const bf16x8*)(kb[1][(ks + KD) & 1] + (ks + KD) * 32);
         if ((ks & 1) && (ks >> 1) < LOADS && refill) issue_one(s_new, sr_new, ks >> 1);
-        if (ks == 0) score4_first(sc, a[0], qreg[0][0], qreg[1][0]);
-        else if (ks == 17) score4_last(sc, a[ks % (KD + 1)], qreg[0][ks], qreg[1][ks]);
-        else score4(sc, a[ks % (KD + 1)], qreg[0][ks], qreg[1][ks]);
+        if (ks == 0) score2<true, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
+        else if (ks == 17) score2<false, false, true>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
+        else score2<false, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -733,25 +725,34 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       int oa[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
-      // software pipeline: the V^T fragment of tile nt + PD is read while tile nt multiplies
-      auto vfrag = [&](int nt) {
-        const int q = nt >> 2, r = nt & 3;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + 64 * q]);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[r] + db + 64 * q]);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      // software pipeline: the two halves of the V^T fragment of tile nt + PD are read between
+      // the two MFMAs of tile nt
+      auto rlo = [&](int nt) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + 64 * (nt >> 2)]);
+      };
+      auto rhi = [&](int nt) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + db + 64 * (nt >> 2)]);
       };
       constexpr int PD = 2;   // prefetch depth
       auto pv_loop = [&](auto FR) {
         constexpr bool F = decltype(FR)::value;
-        bf16x8 va[PD + 1];
+        i16x4 lo[PD + 1], hi[PD + 1];
 #pragma unroll
-        for (int i = 0; i < PD; ++i) va[i] = vfrag(i);
+        for (int i = 0; i < PD; ++i) {
+          lo[i] = rlo(i);
+          hi[i] = rhi(i);
+        }
 #pragma unroll
         for (int nt = 0; nt < 32; ++nt) {
-          if (nt + PD < 32) va[(nt + PD) % (PD + 1)] = vfrag(nt + PD);
-          if (nt == 0) pv2<0, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
-          else if (nt == 31) pv2<2, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
-          else pv2<1, F>(acc[0][nt], acc[1][nt], va[nt % (PD + 1)], pt[0], pt[1]);
+          const int cu = nt % (PD + 1), nx = (nt + PD) % (PD + 1);
+          const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[cu], hi[cu], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (nt + PD < 32) lo[nx] = rlo(nt + PD);
+          if (nt == 0) pv1<F, true, false>(acc[0][nt], v, pt[0]);
+          else pv1<F, false, false>(acc[0][nt], v, pt[0]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (nt + PD < 32) hi[nx] = rhi(nt + PD);
+          if (nt == 31) pv1<F, false, true>(acc[1][nt], v, pt[1]);
+          else pv1<F, false, false>(acc[1][nt], v, pt[1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -781,6 +782,12 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
     }
 
+    if (s + 1 < nst) {
+      n_info = st_info[s + 1];
+      n_tok = st_tok[s + 1];
+      n_bid = st_bid[min(nst - 1, s + 1 + AHEAD)];
+      n_btok = st_tok[min(nst - 1, s + 1 + AHEAD)];
+    }
     // the next step's stage has landed and nobody reads stage s any more
     if constexpr (!QUANT) {
       if (s + 1 < nst) wait_stage(min(nst - 1, s + 3) - (s + 1));
