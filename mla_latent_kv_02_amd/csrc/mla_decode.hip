@@ -187,10 +187,15 @@ struct QuantProducer {
       for (int j = 0; j < 4; ++j) lds_store16(&stage[row + ((p0 ^ j) << 3)], dequant_int4x8(c[j], s, zs));
     } else {
       const uint2 c = *(const uint2*)(cst + w.code);
-      lds_store16(&stage[row + ((p0 ^ 0) << 3)], dequant_int2x8(c.x & 0xFFFFu, s, zs));
-      lds_store16(&stage[row + ((p0 ^ 1) << 3)], dequant_int2x8(c.x >> 16, s, zs));
-      lds_store16(&stage[row + ((p0 ^ 2) << 3)], dequant_int2x8(c.y & 0xFFFFu, s, zs));
-      lds_store16(&stage[row + ((p0 ^ 3) << 3)], dequant_int2x8(c.y >> 16, s, zs));
+      uint32_t t_lo, t_hi;
+      int2_table(s, zs, t_lo, t_hi);
+      u32x4 lo, hi;
+      dequant_int2x16(c.x, t_lo, t_hi, lo, hi);
+      lds_store16(&stage[row + ((p0 ^ 0) << 3)], lo);
+      lds_store16(&stage[row + ((p0 ^ 1) << 3)], hi);
+      dequant_int2x16(c.y, t_lo, t_hi, lo, hi);
+      lds_store16(&stage[row + ((p0 ^ 2) << 3)], lo);
+      lds_store16(&stage[row + ((p0 ^ 3) << 3)], hi);
     }
     if (tid < 256) {
       uint32_t rsz = *(const uint32_t*)(cst + w.rsz);

@@ -263,54 +263,84 @@ struct QuantStage {
   // Thread q dequantises latent chunks kk and kk + 8 (kk = q / 32; 32 elements each, inside
   // one quantisation group since groups are multiples of 32) and RoPE elements 8 kk .. 8 kk + 7
   // of token t = q mod 32.  Group sizes are powers of two (gl = log2 latent group, gr = log2
-  // rope group).  Offsets are recomputed every stage: a few ALU operations instead of
-  // registers held across the loop.
+  // rope group).  load_chunk(h) reads latent chunk kk + 8 h (code words and the raw scale
+  // word), chunk_piece() converts and stores one of its four 8-element pieces (INT2: two);
+  // load_rope() and rope_piece() do the same for the RoPE piece.
+  struct Chunk {
+    uint32_t c[BITS];   // INT4: 16 code bytes, INT2: 8
+    uint32_t sz;        // fp16 (scale, zero), 0 for tokens past the end
+  };
+  __device__ __forceinline__ static Chunk load_chunk(const uint8_t* cst, int valid, int gl, int h, int tid) {
+    asm volatile("" : "+v"(tid));
+    const int t = tid & 31, kk = (tid >> 5) + 8 * h;
+    const int ls = ST_TOK * LB;                    // scale plane of the latent codes
+    Chunk d;
+    const uint32_t sz = *(const uint32_t*)(cst + ls + (((t << (9 - gl)) + ((kk * 32) >> gl)) << 2));
+    d.sz = t < valid ? sz : 0u;
+    const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
+    const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
+    if constexpr (BITS == 4) {
+      const u32x4 c = *(const u32x4*)code;
+      d.c[0] = c[0];
+      d.c[1] = c[1];
+      d.c[2] = c[2];
+      d.c[3] = c[3];
+    } else {
+      const uint2 c = *(const uint2*)code;
+      d.c[0] = c.x;
+      d.c[1] = c.y;
+    }
+    return d;
+  }
+  __device__ __forceinline__ static void chunk_piece(const Chunk& d, int h, int jj, bf16_t* stage, int tid) {
+    asm volatile("" : "+v"(tid));
+    const int t = tid & 31, kk = (tid >> 5) + 8 * h;
+    float sc, zs;
+    scale_zero(d.sz, sc, zs);
+    const int p0 = (4 * kk) ^ sw(t);
+    if constexpr (BITS == 4) {
+      *(u32x4*)&stage[t * 576 + ((p0 ^ jj) << 3)] = dequant_int4x8(d.c[jj], sc, zs);
+    } else {
+      // INT2: pieces jj and jj + 1 (jj even) from one code word
+      uint32_t t_lo, t_hi;
+      int2_table(sc, zs, t_lo, t_hi);
+      u32x4 lo, hi;
+      dequant_int2x16(d.c[jj >> 1], t_lo, t_hi, lo, hi);
+      *(u32x4*)&stage[t * 576 + ((p0 ^ jj) << 3)] = lo;
+      *(u32x4*)&stage[t * 576 + ((p0 ^ (jj + 1)) << 3)] = hi;
+    }
+  }
+  struct Rope {
+    uint32_t c, sz;
+  };
+  __device__ __forceinline__ static Rope load_rope(const uint8_t* cst, int valid, int gl, int gr, int tid) {
+    asm volatile("" : "+v"(tid));
+    const int t = tid & 31, ri = tid >> 5;
+    const int rbase = ST_TOK * LB + (ST_TOK << (9 - gl + 2));
+    Rope r;
+    const uint32_t sz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << (6 - gr)) + ((ri * 8) >> gr)) << 2));
+    r.sz = t < valid ? sz : 0u;
+    r.c = *(const uint32_t*)(cst + rbase + (((ri >> 2) * ST_TOK + t) << 4) + (ri & 3) * 4);
+    return r;
+  }
+  __device__ __forceinline__ static void rope_piece(const Rope& r, bf16_t* stage, int tid) {
+    asm volatile("" : "+v"(tid));
+    const int t = tid & 31, ri = tid >> 5;
+    float sc, zs;
+    scale_zero(r.sz, sc, zs);
+    *(u32x4*)&stage[st_off(t, 512 + ri * 8)] = dequant_int4x8(r.c, sc, zs);
+  }
   __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, int gl, int gr, bf16_t* stage,
                                                  int tid) {
-    asm volatile("" : "+v"(tid));
-    const int t = tid & 31, kk0 = tid >> 5;
-    const int groups_log2 = 9 - gl;
-    const bool ok = t < valid;
-    const int row = t * 576;
-    const int ls = ST_TOK * LB;                    // scale plane of the latent codes
+    const Chunk d0 = load_chunk(cst, valid, gl, 0, tid);
+    const Chunk d1 = load_chunk(cst, valid, gl, 1, tid);
+    const Rope r = load_rope(cst, valid, gl, gr, tid);
+    constexpr int STEP = BITS == 4 ? 1 : 2;   // pieces per chunk_piece call
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = kk0 + 8 * h;
-      uint32_t sz = *(const uint32_t*)(cst + ls + (((t << groups_log2) + ((kk * 32) >> gl)) << 2));
-      sz = ok ? sz : 0u;
-      float s, zs;
-      scale_zero(sz, s, zs);
-      const int p0 = (4 * kk) ^ sw(t);
-      const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
-      const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
-      if constexpr (BITS == 4) {
-        const u32x4 c = *(const u32x4*)code;
+    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d0, 0, jj, stage, tid);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int4x8(c[j], s, zs);
-          __builtin_amdgcn_sched_barrier(0);     // one piece at a time: few registers
-        }
-      } else {
-        const uint2 c = *(const uint2*)code;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t wd = j < 2 ? c.x : c.y;
-          *(u32x4*)&stage[row + ((p0 ^ j) << 3)] = dequant_int2x8(j & 1 ? wd >> 16 : wd & 0xFFFFu, s, zs);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    {
-      const int ri = kk0;
-      const int rbase = ls + (ST_TOK << (groups_log2 + 2));
-      const int rgroups_log2 = 6 - gr;
-      uint32_t rsz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << rgroups_log2) + ((ri * 8) >> gr)) << 2));
-      rsz = ok ? rsz : 0u;
-      float rsc, rzs;
-      scale_zero(rsz, rsc, rzs);
-      const uint32_t rc = *(const uint32_t*)(cst + rbase + (((ri >> 2) * ST_TOK + t) << 4) + (ri & 3) * 4);
-      *(u32x4*)&stage[st_off(t, 512 + ri * 8)] = dequant_int4x8(rc, rsc, rzs);
-    }
+    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d1, 1, jj, stage, tid);
+    rope_piece(r, stage, tid);
   }
 };
 
@@ -601,7 +631,8 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       lds_barrier();
     }
     if constexpr (QUANT) {
-      // dequantise the next stage while this one is consumed
+      // dequantise the next stage while this one is consumed: its code stage has landed and
+      // its bf16 slot was last read in step s - 1
       if (s + 1 < nst)
         QS::dequant(smem + code_slot((s + 1) % DEPTH), (__builtin_amdgcn_readfirstlane(st_info[s + 1]) >> 20) & 63,
                     p.g_lat_log2, p.g_rope_log2, bf_stage((s + 1) & 1), tid);

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mla {
 
 typedef __bf16 bf16_t;
@@ -50,28 +52,59 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return (float)v;
 }
 
+// Byte b of x as a float (v_cvt_f32_ubyte0..3).  The compiler turns (x >> 8b) & 0xFF into a
+// bit-field extract plus a byte-0 conversion; the byte-select forms save the extract.
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  float r;
+  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // Eight INT4 codes of one 32-bit word (element e at bits 4e..4e+3) -> 8 bf16 (as 4 words).
 __device__ __forceinline__ u32x4 dequant_int4x8(uint32_t w, float s, float zs) {
   uint32_t lo = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6 in bytes 0..3
   uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
   u32x4 r;
-  r[0] = pack_bf16x2(__builtin_fmaf((float)(lo & 0xFF), s, -zs), __builtin_fmaf((float)(hi & 0xFF), s, -zs));
-  r[1] = pack_bf16x2(__builtin_fmaf((float)((lo >> 8) & 0xFF), s, -zs), __builtin_fmaf((float)((hi >> 8) & 0xFF), s, -zs));
-  r[2] = pack_bf16x2(__builtin_fmaf((float)((lo >> 16) & 0xFF), s, -zs), __builtin_fmaf((float)((hi >> 16) & 0xFF), s, -zs));
-  r[3] = pack_bf16x2(__builtin_fmaf((float)(lo >> 24), s, -zs), __builtin_fmaf((float)(hi >> 24), s, -zs));
+  r[0] = pack_bf16x2(__builtin_fmaf(ubyte_f32<0>(lo), s, -zs), __builtin_fmaf(ubyte_f32<0>(hi), s, -zs));
+  r[1] = pack_bf16x2(__builtin_fmaf(ubyte_f32<1>(lo), s, -zs), __builtin_fmaf(ubyte_f32<1>(hi), s, -zs));
+  r[2] = pack_bf16x2(__builtin_fmaf(ubyte_f32<2>(lo), s, -zs), __builtin_fmaf(ubyte_f32<2>(hi), s, -zs));
+  r[3] = pack_bf16x2(__builtin_fmaf(ubyte_f32<3>(lo), s, -zs), __builtin_fmaf(ubyte_f32<3>(hi), s, -zs));
   return r;
 }
 
-// Eight INT2 codes of the low 16 bits of w (element e at bits 2e..2e+1) -> 8 bf16.
-__device__ __forceinline__ u32x4 dequant_int2x8(uint32_t w, float s, float zs) {
-  u32x4 r;
+// INT2: a group has only four code values, so its four dequantised bf16 values are computed
+// once (the same fma + RNE conversion per value) into an 8-byte table {t_hi : t_lo}, code c at
+// bytes 2c, 2c + 1, and every output pair is a byte permute of that table.
+__device__ __forceinline__ void int2_table(float s, float zs, uint32_t& t_lo, uint32_t& t_hi) {
+  t_lo = pack_bf16x2(__builtin_fmaf(0.f, s, -zs), __builtin_fmaf(1.f, s, -zs));
+  t_hi = pack_bf16x2(__builtin_fmaf(2.f, s, -zs), __builtin_fmaf(3.f, s, -zs));
+}
+
+// Sixteen INT2 codes of a 32-bit word (element e at bits 2e..2e+1) -> 16 bf16 (elements 0..7 in
+// lo, 8..15 in hi) through the group's table.  Masking w >> 2j with 0x03030303 puts element
+// 4b + j in byte b of m_j; for the pair (4b + j, 4b + j + 1), j even, one permute gathers
+// (c, c, c', c') from m_j and m_j+1, 2x + 0x01000100 turns it into the byte selector
+// (2c, 2c + 1, 2c', 2c' + 1), and a second permute reads the two bf16 values from the table.
+__device__ __forceinline__ void dequant_int2x16(uint32_t w, uint32_t t_lo, uint32_t t_hi, u32x4& lo, u32x4& hi) {
+  const uint32_t m0 = w & 0x03030303u, m1 = (w >> 2) & 0x03030303u;
+  const uint32_t m2 = (w >> 4) & 0x03030303u, m3 = (w >> 6) & 0x03030303u;
+  auto pair = [&](uint32_t ma, uint32_t mb, int b) {
+    // byte select: bytes 0..3 of the permute source are its second operand, 4..7 its first
+    const uint32_t gsel = (uint32_t)b * 0x0101u + (uint32_t)(4 + b) * 0x01010000u;
+    const uint32_t x = __builtin_amdgcn_perm(mb, ma, gsel);
+    return __builtin_amdgcn_perm(t_hi, t_lo, (x << 1) + 0x01000100u);
+  };
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float a = (float)((w >> (4 * k)) & 3u);
-    float b = (float)((w >> (4 * k + 2)) & 3u);
-    r[k] = pack_bf16x2(__builtin_fmaf(a, s, -zs), __builtin_fmaf(b, s, -zs));
+  for (int b = 0; b < 4; ++b) {
+    u32x4& r = b < 2 ? lo : hi;
+    const int k = (b & 1) * 2;   // elements 4b .. 4b + 3 -> words k, k + 1
+    r[k] = pair(m0, m1, b);
+    r[k + 1] = pair(m2, m3, b);
   }
-  return r;
 }
 
 // (scale, zero) fp16 pair packed in a 32-bit word -> (s, z*s) as fp32.
@@ -198,8 +231,12 @@ struct QuantTileReader {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float s = j < 2 ? s0 : s1, zs = j < 2 ? zs0 : zs1;
-          f(tok, col8 + 2 * j, dequant_int2x8(c[k][j] & 0xFFFFu, s, zs));
-          f(tok, col8 + 2 * j + 1, dequant_int2x8(c[k][j] >> 16, s, zs));
+          uint32_t t_lo, t_hi;
+          int2_table(s, zs, t_lo, t_hi);
+          u32x4 lo, hi;
+          dequant_int2x16(c[k][j], t_lo, t_hi, lo, hi);
+          f(tok, col8 + 2 * j, lo);
+          f(tok, col8 + 2 * j + 1, hi);
         }
       }
     }
