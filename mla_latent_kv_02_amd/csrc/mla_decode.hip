@@ -51,6 +51,14 @@ __device__ __forceinline__ void dma16(const void* src, lds_void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
+// 16 bytes per lane from base + off (base wave-uniform, off per lane) to LDS bytes
+// [lds_base + 16 lane, + 16).  With the per-lane offsets precomputed, an issue costs no VALU
+// work.  One wait state between the M0 write and the DMA; the kernel makes no other use of M0.
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ float wave_max_16_32(float v) {
   v = fmaxf(v, __shfl_xor(v, 16, 64));
   v = fmaxf(v, __shfl_xor(v, 32, 64));
@@ -83,20 +91,31 @@ template <int FMT>
 struct Producer;
 
 // bf16 rows: the 2304 pieces of a half block; waves 0-3 issue 5 instructions, waves 4-7 issue 4.
+// Slot k receives (token k / 72, logical piece (k mod 72) ^ sw(token)); all 32 rows are copied
+// (a block is allocated whole) and rows past the sequence end are zeroed before use.
 template <>
 struct Producer<FMT_BF16> {
   static constexpr int LOADS_LO = 5;  // waves 0..3
   static constexpr int LOADS_HI = 4;  // waves 4..7
-  __device__ __forceinline__ static void issue(const uint8_t* half, int valid, bf16_t* stage, int tid) {
+  struct Offsets {
+    uint32_t o[LOADS_LO];
+  };
+  __device__ static Offsets offsets(int tid) {
+    Offsets r;
+#pragma unroll
+    for (int i = 0; i < LOADS_LO; ++i) {
+      const int slot = min(i * NT + tid, ST_TOK * 72 - 1);
+      const int t = slot / 72;
+      r.o[i] = (uint32_t)(t * 1152 + (((slot - t * 72) ^ sw(t)) << 4));
+    }
+    return r;
+  }
+  __device__ __forceinline__ static void issue(const uint8_t* half, const Offsets& off, bf16_t* stage, int tid) {
     const int wbase = tid & ~63;
 #pragma unroll
     for (int i = 0; i < LOADS_LO; ++i) {
       if (i == LOADS_HI && tid >= 256) break;
-      const int slot = i * NT + tid;
-      const int t = slot / 72;
-      const int c = (slot - t * 72) ^ sw(t);  // logical piece held by this physical slot
-      const uint8_t* src = t < valid ? half + t * 1152 + c * 16 : half;
-      dma16(src, (lds_void*)(stage + (size_t)(i * NT + wbase) * 8));
+      dma16(half + off.o[i], (lds_void*)(stage + (size_t)(i * NT + wbase) * 8));
     }
   }
 };
@@ -318,13 +337,14 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
     }
     return p.pool + (size_t)id * (size_t)p.block_bytes;
   };
+  const auto bf_off = Producer<FMT_BF16>::offsets(tid);
   auto issue = [&](int s, bf16_t* st, uint8_t* cst) {
     int half, valid;
     const uint8_t* blk = stage_src(s, half, valid);
     if constexpr (QUANT)
       Prod::issue(blk, half, pl, groups, rgroups, cst, tid);
     else
-      Prod::issue(blk + half * ST_TOK * 1152, valid, st, tid);
+      Prod::issue(blk + half * ST_TOK * 1152, bf_off, st, tid);
   };
   // wait until a stage has landed, given how many later stages were issued after it
   // (each loader wave issues a fixed number of DMA instructions per stage)
