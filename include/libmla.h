@@ -138,7 +138,9 @@ typedef struct mla_decode_args {
   size_t workspace_bytes;
 } mla_decode_args;
 
-/* Workspace needed by mla_decode_paged for these arguments (0 when no split is used).
+/* Workspace needed by mla_decode_paged for these arguments: 0 for fewer than 96 query rows
+ * per sequence when the plan uses no split; 96 rows or more always need one (every piece of
+ * a sequence is written there unnormalised and merged by a second kernel).
  * Device memory, 256-byte aligned, owned by the caller; its contents need no initialisation
  * and are scratch between calls (calls that overlap on one workspace race). */
 int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes);

@@ -11,23 +11,26 @@
 //   * scores S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: K fragments from the LDS stage, Q^T
 //     for both 16-row tiles held in registers; each K fragment feeds two MFMAs;
 //   * softmax in registers: the 32 scores of a row sit in 4 lane groups, so a row maximum is
-//     two cross-lane steps; the running maximum moves only when a stage exceeds it by more
-//     than RESCALE_SLACK (log2 units), so rescaling the accumulators is rare;
+//     two lane swaps; the running maximum moves only when a stage exceeds it by more than
+//     ROWS_SLACK (log2 units), so rescaling the accumulators is rare;
 //   * O^T += V^T . P^T: the score accumulators are already the P^T operand once the token
 //     order inside the 32-token step is taken as (4 tokens of tile 0, 4 of tile 1) per lane
 //     group, and V^T fragments come from the token-major stage with ds_read_b64_tr_b16 in the
-//     same order; each V^T fragment feeds two MFMAs; O^T (32 rows x 512) stays in AGPRs.
+//     same order; each V^T fragment feeds two MFMAs; O^T (32 rows x 512) stays in AGPRs,
+//     touched only by inline asm (MFMAs, a rare LDS round-trip rescale, stores).
 // There is no cross-wave dependency inside a step: one barrier per 32-token stage guards the
 // ring of LDS stages.
 //
 // Stages stream HBM -> LDS with global_load_lds_dwordx4 (bf16: a 4-deep ring, three stages
 // in flight; INT4/INT2: a ring of code stages, dequantised one step ahead into a second bf16
-// stage).  The DMA is written as inline asm: the compiler then never inserts waits for it,
-// and each step waits with an explicit vmcnt for exactly the stage it needs.
+// stage).  The DMA is written as inline asm with precomputed per-lane source offsets: the
+// compiler never inserts waits for it, and each step waits with an explicit vmcnt for exactly
+// the stage it needs.
 //
 // Work balance: the batch's cache blocks, sequence after sequence, are cut into n_ranges equal
-// ranges (one workgroup per range and row group); a range may cover several sequences, and a
-// sequence cut by range boundaries leaves partials that combine_kernel merges.
+// ranges (one workgroup per range and row group); a range may cover several sequences or part
+// of one.  Every piece (a sequence's blocks inside one range) is stored unnormalised with
+// 1 / sum(P) and its lse; combine_kernel normalises and merges.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
