@@ -51,23 +51,29 @@ __device__ __forceinline__ void dma16(const void* src, lds_void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// 16 bytes per lane from base + off (base wave-uniform, off per lane) to LDS bytes
-// [lds_base + 16 lane, + 16).  With the per-lane offsets precomputed, an issue costs no VALU
-// work.  One wait state between the M0 write and the DMA; the kernel makes no other use of M0.
-__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
+// 16 bytes per lane from a per-lane address to LDS bytes [lds_base + 16 lane, + 16), invisible
+// to the compiler's wait insertion (every wait for it is explicit).
+__device__ __forceinline__ void dma16a(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(src)
                : "memory", "m0");
 }
 
-__device__ __forceinline__ float wave_max_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+// Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the gfx950 lane
+// swaps: with both operands equal, permlane32_swap / permlane16_swap return x at l and at l ^ 32
+// (l ^ 16), so one max / add per step gives the butterfly without an LDS round trip.
+__device__ __forceinline__ float wave_max_16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float wave_sum_16_32(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+__device__ __forceinline__ float wave_sum_16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ bf16x8 load_q8(const void* base, size_t elem_off, bool f32) {
@@ -121,27 +127,31 @@ struct Producer<FMT_BF16> {
 };
 
 // Quantised latent (INT4 or INT2) + INT4 rope: the four code planes of a half block are
-// copied into a flat code stage [lc | ls | rc | rs], padded to SLOTS pieces.
+// copied into a flat, token-major code stage [lc | ls | rc | rs], padded to SLOTS pieces.
 template <int FMT>
 struct QuantProducer {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
   static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
-  static constexpr int PPT = LB / 16;              // latent code pieces (16 B) per token
   // code stage capacity in 16-byte slots: INT4 waves 0-3 issue 2 instructions, waves 4-7 one
   static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;
   static constexpr int LOADS_HI = 1;
   static constexpr int SLOTS = FMT == FMT_INT4 ? 768 : 512;
   __device__ __forceinline__ static void issue(const uint8_t* blk, int half, const QuantPlanes& pl, int groups,
                                                int rgroups, uint8_t* cstage, int tid) {
+    issue_with(half, pl, groups, rgroups, tid, [&](int off, int i, int wbase) {
+      dma16(blk + off, (lds_void*)(cstage + (size_t)(i * NT + wbase) * 16));
+    });
+  }
+  // byte offset inside the block of the piece that slot i * NT + tid of a code stage receives:
+  // dma(offset, i, first thread of the wave) for each of this thread's DMA instructions
+  template <class F>
+  __device__ __forceinline__ static void issue_with(int half, const QuantPlanes& pl, int groups, int rgroups, int tid,
+                                                    F&& dma) {
     const int n_lc = ST_TOK * LB / 16;
     const int n_ls = ST_TOK * groups * 4 / 16;
     const int n_rc = ST_TOK * 32 / 16;
     const int n_rs = (ST_TOK * rgroups * 4 + 15) / 16;
     const int n_all = n_lc + n_ls + n_rc + n_rs;
-    const uint8_t* lc = blk + pl.lc + half * ST_TOK * LB;
-    const uint8_t* ls = blk + pl.ls + half * ST_TOK * groups * 4;
-    const uint8_t* rc = blk + pl.rc + half * ST_TOK * 32;
-    const uint8_t* rs = blk + pl.rs + half * ST_TOK * rgroups * 4;
     const int wbase = tid & ~63;
 #pragma unroll
     for (int i = 0; i < LOADS_LO; ++i) {
@@ -149,80 +159,70 @@ struct QuantProducer {
       const int slot = i * NT + tid;
       // padding slots re-load a real piece (spread over the stage, never one shared address)
       int p = slot < n_all ? slot : slot - n_all;
-      const uint8_t* src;
+      int off;
       if (p < n_lc) {
-        // latent code pieces are stored piece-major: slot k * 32 + t holds piece k of token t
-        src = lc + ((p % ST_TOK) * PPT + p / ST_TOK) * 16;
+        off = pl.lc + half * ST_TOK * LB + p * 16;
       } else if ((p -= n_lc) < n_ls) {
-        src = ls + p * 16;
+        off = pl.ls + half * ST_TOK * groups * 4 + p * 16;
       } else if ((p -= n_ls) < n_rc) {
-        src = rc + ((p % ST_TOK) * 2 + p / ST_TOK) * 16;   // rope code halves, also piece-major
+        off = pl.rc + half * ST_TOK * 32 + p * 16;
       } else {
-        src = rs + (p - n_rc) * 16;
+        off = pl.rs + half * ST_TOK * rgroups * 4 + (p - n_rc) * 16;
       }
-      dma16(src, (lds_void*)(cstage + (size_t)(i * NT + wbase) * 16));
+      dma(off, i, wbase);
     }
   }
 
-  // Per-thread dequantisation work, fixed for the whole partition.  Thread q owns latent
-  // chunk kk = q / 32 (32 elements, inside one quantisation group since groups are multiples
-  // of 32) of token t = q mod 32: a wavefront's code reads are contiguous and its swizzled
-  // bf16 stores spread over all banks.  Threads 0..255 also own 8 RoPE elements
-  // (token rt, elements 8 ri .. 8 ri + 7).
-  struct Work {
-    int t, code, sz, dst;       // latent: token, code byte offset, scale byte offset, stage element
-    int rt, rcode, rsz, rdst;   // rope (tid < 256)
-  };
-  __device__ __forceinline__ static Work plan(int groups, int rgroups, int tid) {
-    Work w;
-    w.t = tid & 31;
-    const int kk = tid >> 5;                      // 0..15
-    const int cpiece = (kk * 32 * BITS) / 128;    // 16-byte code piece holding the chunk
-    const int cbyte = ((kk * 32 * BITS) / 8) & 15;
-    w.code = (cpiece * ST_TOK + w.t) * 16 + cbyte;
-    w.sz = ST_TOK * LB + (w.t * groups + (kk * 32) / (512 / groups)) * 4;
-    w.dst = st_off(w.t, kk * 32);
-    w.rt = tid & 31;
-    const int ri = (tid >> 5) & 7;
-    w.rcode = ST_TOK * LB + ST_TOK * groups * 4 + ((ri >> 2) * ST_TOK + w.rt) * 16 + (ri & 3) * 4;
-    w.rsz = ST_TOK * LB + ST_TOK * groups * 4 + ST_TOK * 32 + (w.rt * rgroups + (ri * 8) / (64 / rgroups)) * 4;
-    w.rdst = st_off(w.rt, 512 + ri * 8);
-    return w;
-  }
-
-  // codes -> swizzled bf16 stage; tokens >= valid become zeros (scale and zero-point 0)
-  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, const Work& w, bf16_t* stage,
-                                                 int tid) {
-    uint32_t sz = *(const uint32_t*)(cst + w.sz);
-    sz = w.t < valid ? sz : 0u;
-    float s, zs;
-    scale_zero(sz, s, zs);
-    // element 32 kk + 8 j sits at physical piece (4 kk + j) ^ sw(t) = (base piece) ^ j
-    const int row = w.t * 576;
-    const int p0 = (w.dst - row) >> 3;
-    if constexpr (BITS == 4) {
-      const u32x4 c = *(const u32x4*)(cst + w.code);
+  // Latent task k (k < 512) or RoPE task k - 512 of a code stage into the swizzled bf16 stage;
+  // tokens >= valid become zeros (scale and zero-point 0).  gl, gr: log2 of the latent and
+  // rope group sizes (powers of two: they divide 512 and 64).
+  __device__ __forceinline__ static void dequant_task(const uint8_t* cst, int valid, int k, int gl, int gr,
+                                                      bf16_t* stage) {
+    const int groups_log2 = 9 - gl;
+    const int ls = ST_TOK * LB;
+    if (k < 512) {
+      int t, kk;
+      lat_task(k, t, kk);
+      uint32_t sz = *(const uint32_t*)(cst + ls + (((t << groups_log2) + ((kk * 32) >> gl)) << 2));
+      sz = t < valid ? sz : 0u;
+      float sc, zs;
+      scale_zero(sz, sc, zs);
+      // element 32 kk + 8 j sits at physical piece (4 kk + j) ^ sw(t) = (base piece) ^ j
+      const int row = t * 576, p0 = (4 * kk) ^ sw(t);
+      const uint8_t* code = cst + t * LB + kk * 4 * BITS;
+      if constexpr (BITS == 4) {
+        const u32x4 c = *(const u32x4*)code;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lds_store16(&stage[row + ((p0 ^ j) << 3)], dequant_int4x8(c[j], s, zs));
+        for (int j = 0; j < 4; ++j) lds_store16(&stage[row + ((p0 ^ j) << 3)], dequant_int4x8(c[j], sc, zs));
+      } else {
+        const uint2 c = *(const uint2*)code;
+        uint32_t t_lo, t_hi;
+        int2_table(sc, zs, t_lo, t_hi);
+        u32x4 lo, hi;
+        dequant_int2x16(c.x, t_lo, t_hi, lo, hi);
+        lds_store16(&stage[row + ((p0 ^ 0) << 3)], lo);
+        lds_store16(&stage[row + ((p0 ^ 1) << 3)], hi);
+        dequant_int2x16(c.y, t_lo, t_hi, lo, hi);
+        lds_store16(&stage[row + ((p0 ^ 2) << 3)], lo);
+        lds_store16(&stage[row + ((p0 ^ 3) << 3)], hi);
+      }
     } else {
-      const uint2 c = *(const uint2*)(cst + w.code);
-      uint32_t t_lo, t_hi;
-      int2_table(s, zs, t_lo, t_hi);
-      u32x4 lo, hi;
-      dequant_int2x16(c.x, t_lo, t_hi, lo, hi);
-      lds_store16(&stage[row + ((p0 ^ 0) << 3)], lo);
-      lds_store16(&stage[row + ((p0 ^ 1) << 3)], hi);
-      dequant_int2x16(c.y, t_lo, t_hi, lo, hi);
-      lds_store16(&stage[row + ((p0 ^ 2) << 3)], lo);
-      lds_store16(&stage[row + ((p0 ^ 3) << 3)], hi);
+      int t, ri;
+      rope_task(k - 512, t, ri);
+      const int rbase = ls + (ST_TOK << (groups_log2 + 2));
+      uint32_t rsz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << (6 - gr)) + ((ri * 8) >> gr)) << 2));
+      rsz = t < valid ? rsz : 0u;
+      float sc, zs;
+      scale_zero(rsz, sc, zs);
+      const uint32_t rc = *(const uint32_t*)(cst + rbase + t * 32 + ri * 4);
+      lds_store16(&stage[st_off(t, 512 + ri * 8)], dequant_int4x8(rc, sc, zs));
     }
-    if (tid < 256) {
-      uint32_t rsz = *(const uint32_t*)(cst + w.rsz);
-      rsz = w.rt < valid ? rsz : 0u;
-      float rsc, rzs;
-      scale_zero(rsz, rsc, rzs);
-      lds_store16(&stage[w.rdst], dequant_int4x8(*(const uint32_t*)(cst + w.rcode), rsc, rzs));
-    }
+  }
+  // every thread's share of a whole stage: latent task tid, RoPE task tid (tid < 256)
+  __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, int gl, int gr, bf16_t* stage,
+                                                 int tid) {
+    dequant_task(cst, valid, tid, gl, gr, stage);
+    if (tid < 256) dequant_task(cst, valid, 512 + tid, gl, gr, stage);
   }
 };
 
@@ -242,12 +242,16 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   using QP = QuantProducer<FMT == FMT_BF16 ? FMT_INT4 : FMT>;
   constexpr int CBYTES = QUANT ? QP::SLOTS * 16 : 16;
 
-  // bf16 path: a 4-deep ring of bf16 stages.  Quantised path: an 8-deep ring of code stages
-  // and one bf16 stage that every step dequantises into.  Distinct arrays let the compiler
-  // see that reading one ring slot does not depend on the DMA into another.
-  constexpr int DEPTH = QUANT ? 8 : 4;
+  // bf16 path: a 4-deep ring of bf16 stages.  Quantised path with fewer than 64 rows: the
+  // wavefronts that do not score dequantise stage s + 1 into the second of two bf16 stages
+  // while stage s is scored, over a 6-deep ring of code stages.  Quantised, 64 rows (every
+  // wavefront scores): an 8-deep code ring and one bf16 stage dequantised at each step.
+  // Distinct arrays let the compiler see that reading one ring slot does not depend on the
+  // DMA into another.
+  constexpr bool SPLIT = QUANT && RT < 4;
+  constexpr int DEPTH = QUANT ? (SPLIT ? 6 : 8) : 4;
   __shared__ __attribute__((aligned(16))) bf16_t S0[ST_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16_t S1[QUANT ? 8 : ST_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t S1[(QUANT && !SPLIT) ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t S2[QUANT ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t S3[QUANT ? 8 : ST_ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t C0[CBYTES];
@@ -256,8 +260,8 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t C3[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C4[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C5[CBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t C6[CBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t C7[CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C6[SPLIT ? 16 : CBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t C7[SPLIT ? 16 : CBYTES];
   __shared__ __attribute__((aligned(16))) bf16_t Ps[ROWS * PROW];
   __shared__ float red[2][ROWS];
   __shared__ float redl[2][ROWS];   // row sums of the bf16-rounded P (normalise o)
@@ -367,46 +371,42 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
     }
   };
   static_assert(DEPTH - 2 <= 6, "wait_stage covers at most 6 later stages");
+  const int gl_log2 = 31 - __builtin_clz(p.g_lat > 0 ? p.g_lat : 1);
+  const int gr_log2 = 31 - __builtin_clz(p.g_rope > 0 ? p.g_rope : 1);
 
-  const typename QP::Work dq = QP::plan(groups, rgroups, tid);
-
-  // prologue: stages 0 .. DEPTH-2 in flight; stage 0 landed
+  // prologue: stages 0 .. DEPTH-2 in flight; stage 0 landed (split: stages 0 and 1 landed and
+  // stage 0 dequantised by every wavefront)
   if constexpr (QUANT) {
     if (0 < nst) issue(0, S0, C0);
     if (1 < nst) issue(1, S0, C1);
     if (2 < nst) issue(2, S0, C2);
     if (3 < nst) issue(3, S0, C3);
     if (4 < nst) issue(4, S0, C4);
-    if (5 < nst) issue(5, S0, C5);
-    if (6 < nst) issue(6, S0, C6);
+    if (!SPLIT && 5 < nst) issue(5, S0, C5);
+    if (!SPLIT && 6 < nst) issue(6, S0, C6);
   } else {
     if (0 < nst) issue(0, S0, C0);
     if (1 < nst) issue(1, S1, C0);
     if (2 < nst) issue(2, S2, C0);
   }
-  wait_stage(min(nst - 1, DEPTH - 2));
-  lds_barrier();
-
-  // one stage: KS = bf16 stage read by the MFMAs, CCUR = its code stage (quantised formats),
-  // NXT/CNXT = ring slot refilled with stage s + DEPTH - 1
-  auto step = [&](int s, bf16_t* KS, uint8_t* CCUR, bf16_t* NXT, uint8_t* CNXT) {
-    // stage s has landed and every wave is done with stage s-1 (barrier at the end of the
-    // previous step), so the ring slot of stage s-1 can take stage s + DEPTH - 1
-    if (s + DEPTH - 1 < nst) issue(s + DEPTH - 1, NXT, CNXT);
-    int half_unused, valid;
-    stage_src(s, half_unused, valid);
-    if constexpr (QUANT) {
-      QP::dequant(CCUR, valid, dq, KS, tid);
-      lds_barrier();
-    } else if (valid < ST_TOK) {
-      // rows past the sequence end were filled from a dummy address: zero them
-      for (int q = tid; q < (ST_TOK - valid) * 72; q += NT)
-        *(u32x4*)&KS[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
-      lds_barrier();
+  if constexpr (SPLIT) {
+    wait_stage(min(nst - 1, DEPTH - 2) - min(nst - 1, 1));
+    lds_barrier();
+    if (0 < nst) {
+      int half_unused, valid0;
+      stage_src(0, half_unused, valid0);
+      QP::dequant(C0, valid0, gl_log2, gr_log2, S0, tid);
     }
-
+    lds_barrier();
+  } else {
+    wait_stage(min(nst - 1, DEPTH - 2));
+    lds_barrier();
+  }
+  // ---- the phases of one step
+  f32x4 sv = {0.f, 0.f, 0.f, 0.f};   // this scorer's scores of the current stage
+  auto score_phase = [&](int s, const bf16_t* KS, int valid) {
+    sv = f32x4{0.f, 0.f, 0.f, 0.f};
     // ---- scores for (row tile sc_rt, token tile sc_tt)
-    f32x4 sv = {0.f, 0.f, 0.f, 0.f};
     if (scorer) {
       // k-step ks reads logical piece 4 ks + lg, physical 8 (ks / 2) + ((4 (ks & 1) + lg) ^ f):
       // one base register for even and one for odd ks, the rest is an immediate offset of 32
@@ -441,8 +441,8 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       mx = wave_max_16_32(mx);
       if (lg == 0) red[sc_tt][row_s] = mx;
     }
-    lds_barrier();
-
+  };
+  auto softmax_phase = [&]() {
     // ---- running max, P for the scored tile; the scorers of token tile 0 publish the
     // rescale factor of their rows, every wave then rescales the output rows it owns
     if (scorer) {
@@ -468,7 +468,8 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       }
       *(uint2*)&Ps[row_s * PROW + sc_tt * 16 + lg * 4] = uint2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
     }
-    lds_barrier();
+  };
+  auto pv_phase = [&](const bf16_t* KS) {
     {
       bool any = false;
       f32x4 al[RT];
@@ -502,8 +503,69 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], bv, acc[rt][nt], 0, 0, 0);
       }
     }
+  };
+
+  // one stage: KS = bf16 stage read by the MFMAs, CCUR = its code stage (quantised formats,
+  // not split), NXT/CNXT = ring slot refilled with stage s + DEPTH - 1
+  auto step = [&](int s, bf16_t* KS, uint8_t* CCUR, bf16_t* NXT, uint8_t* CNXT) {
+    // stage s has landed and every wave is done with stage s-1 (barrier at the end of the
+    // previous step), so the ring slot of stage s-1 can take stage s + DEPTH - 1
+    if (s + DEPTH - 1 < nst) issue(s + DEPTH - 1, NXT, CNXT);
+    int half_unused, valid;
+    stage_src(s, half_unused, valid);
+    if constexpr (QUANT) {
+      QP::dequant(CCUR, valid, gl_log2, gr_log2, KS, tid);
+      lds_barrier();
+    } else if (valid < ST_TOK) {
+      // rows past the sequence end were filled from a dummy address: zero them
+      for (int q = tid; q < (ST_TOK - valid) * 72; q += NT)
+        *(u32x4*)&KS[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
+      lds_barrier();
+    }
+    score_phase(s, KS, valid);
+    lds_barrier();
+    softmax_phase();
+    lds_barrier();
+    pv_phase(KS);
     // stage s+1 landed, and nobody reads stage s any more
     wait_stage(min(nst - 2 - s, DEPTH - 2));
+    lds_barrier();
+  };
+
+  // split quantised step: KS = bf16 stage of s, KN = bf16 stage of s + 1, CDQ = code stage of
+  // s + 1, CNXT = ring slot refilled with stage s + DEPTH - 1 (the slot of s - 1, dequantised in
+  // step s - 2).  The wavefronts that do not score dequantise stage s + 1 meanwhile: tasks
+  // q, q + G, ... (G = their thread count), the first half during the scores, the rest during
+  // the softmax.
+  constexpr int G = SPLIT ? NT - 128 * RT : 1;
+  constexpr int N_IT = (768 + G - 1) / G;
+  constexpr int IT_A = (N_IT + 1) / 2;
+  auto step_split = [&](int s, bf16_t* KS, bf16_t* KN, uint8_t* CDQ, uint8_t* CNXT) {
+    if (s + DEPTH - 1 < nst) issue(s + DEPTH - 1, KN, CNXT);
+    int half_unused, valid, valid_n = 0;
+    stage_src(s, half_unused, valid);
+    const bool deq = !scorer && s + 1 < nst;
+    if (s + 1 < nst) stage_src(s + 1, half_unused, valid_n);
+    const int q = tid - 128 * RT;
+    if (scorer) {
+      score_phase(s, KS, valid);
+    } else if (deq) {
+#pragma unroll
+      for (int it = 0; it < IT_A; ++it)
+        if (it * G + q < 768) QP::dequant_task(CDQ, valid_n, it * G + q, gl_log2, gr_log2, KN);
+    }
+    lds_barrier();
+    if (scorer) {
+      softmax_phase();
+    } else if (deq) {
+#pragma unroll
+      for (int it = IT_A; it < N_IT; ++it)
+        if (it * G + q < 768) QP::dequant_task(CDQ, valid_n, it * G + q, gl_log2, gr_log2, KN);
+    }
+    lds_barrier();
+    pv_phase(KS);
+    // stage s + 2 landed (dequantised in the next step), and nobody reads stage s any more
+    if (s + 2 < nst) wait_stage(min(nst - 1, s + DEPTH - 1) - (s + 2));
     lds_barrier();
   };
 
@@ -513,6 +575,15 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       if (s + 1 < nst) step(s + 1, S1, C1, S0, C0);
       if (s + 2 < nst) step(s + 2, S2, C2, S1, C1);
       if (s + 3 < nst) step(s + 3, S3, C3, S2, C2);
+    }
+  } else if constexpr (SPLIT) {
+    for (int s = 0; s < nst; s += 6) {
+      step_split(s, S0, S1, C1, C5);
+      if (s + 1 < nst) step_split(s + 1, S1, S0, C2, C0);
+      if (s + 2 < nst) step_split(s + 2, S0, S1, C3, C1);
+      if (s + 3 < nst) step_split(s + 3, S1, S0, C4, C2);
+      if (s + 4 < nst) step_split(s + 4, S0, S1, C5, C3);
+      if (s + 5 < nst) step_split(s + 5, S1, S0, C0, C4);
     }
   } else {
     for (int s = 0; s < nst; s += 8) {
@@ -568,10 +639,317 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Pipelined decode for quantised caches and at most 16 query rows (the V2-Lite shapes), one
+// barrier per 32-token step.  In step s wavefront 0 scores stage s + 1 and runs its softmax in
+// registers (a row's 32 scores sit in its 4 lane groups), every wavefront adds P(s) . C(s) to
+// the 64 output columns it owns, and wavefronts 1-7 dequantise stage s + 2 into the third
+// bf16 buffer, so the dequantisation (VALU), the scores (MFMA) and the HBM reads of later
+// code stages overlap.  Code stage k sits in ring slot k mod 4, bf16 stage k in buffer k mod 3,
+// P and the rescale factors of stage k in buffer k mod 2.  The DMA is inline asm (each wait
+// for it is explicit), so one LDS array holds every buffer.
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool QF32>
+__global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
+  using QP = QuantProducer<FMT>;
+  constexpr int DEPTH = 4;                         // code ring slots
+  constexpr int CBYTES = QP::SLOTS * 16;
+  constexpr int BF = ST_ELEMS * 2;                 // bytes of a bf16 stage
+  constexpr int OFF_C = 3 * BF;
+  constexpr int OFF_P = OFF_C + DEPTH * CBYTES;
+  constexpr int PBYTES = 16 * PROW * 2;
+  constexpr int SMEM = OFF_P + 2 * PBYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(16))) float alpha[2][16];
+  __shared__ float fin[3][16];                     // row sums of bf16 P, of unrounded P, maximum
+  __shared__ int bids[MAX_TPC];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const float NEG_INF = -__builtin_inff();
+
+  const int u = (int)(blockIdx.x & 7) * p.units_per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= p.total_units) return;
+  const int bc = u / p.RG;                         // RG = 1: at most 16 rows
+  const int b = bc / p.max_chunks, c = bc % p.max_chunks;
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  int nch = (nblk + p.tpc - 1) / p.tpc;
+  nch = nch < 1 ? 1 : nch;
+  if (c >= nch) return;
+  const int T0 = c * p.tpc * BLOCK_TOKENS;
+  const int T1 = min((c + 1) * p.tpc * BLOCK_TOKENS, L);
+  const int nst = T1 > T0 ? (T1 - T0 + ST_TOK - 1) / ST_TOK : 0;
+  const int R = p.R;
+
+  // wavefront 0: the queries of the 16 rows (row lr) and their softmax state
+  const bool qrow = lr < R;
+  const int lim = qrow ? L - p.s_q + lr / p.H : -1;
+  bf16x8 qreg[18];
+  if (w == 0) {
+    const size_t qbase = (size_t)b * R + (qrow ? lr : 0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qreg[ks] = qrow ? load_q8(p.q_lat, qbase * 512 + ks * 32 + lg * 8, QF32) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qreg[16 + ks] = qrow ? load_q8(p.q_rope, qbase * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
+  }
+  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
+  // output columns: wave w owns column group w
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const QuantPlanes pl{(int)p.off_lc, (int)p.off_ls, (int)p.off_rc, (int)p.off_rs};
+  const int groups = 512 / p.g_lat, rgroups = 64 / p.g_rope;
+  const int gl_log2 = 31 - __builtin_clz(p.g_lat > 0 ? p.g_lat : 1);
+  const int gr_log2 = 31 - __builtin_clz(p.g_rope > 0 ? p.g_rope : 1);
+  const int32_t* btab = p.block_table + (size_t)b * p.bt_stride;
+  const int blk0 = T0 / BLOCK_TOKENS;
+  const int nb_unit = min(p.tpc, nblk - blk0);
+  for (int j = tid; j < nb_unit; j += NT) bids[j] = btab[blk0 + j];
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries and block ids, before any DMA
+  __syncthreads();
+
+  auto stage_src = [&](int s, int& half, int& valid) -> const uint8_t* {
+    const int tok = T0 + s * ST_TOK;
+    half = (tok / ST_TOK) & 1;
+    valid = min(ST_TOK, T1 - tok);
+    int id = __builtin_amdgcn_readfirstlane(bids[tok / BLOCK_TOKENS - blk0]);
+    if (id < 0 || (int64_t)id >= p.num_blocks) {
+      id = 0;
+      valid = 0;
+    }
+    return p.pool + (size_t)id * (size_t)p.block_bytes;
+  };
+  const uint32_t sbase = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto bbuf = [&](int k) { return (bf16_t*)(smem + (k % 3) * BF); };
+  auto cslot = [&](int k) { return smem + OFF_C + (k % DEPTH) * CBYTES; };
+  auto pbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * PBYTES); };
+  // every thread issues its LOADS_LO / LOADS_HI pieces of a code stage
+  auto issue = [&](int k) {
+    int half, valid;
+    const uint8_t* blk = stage_src(k, half, valid);
+    const uint32_t cst = sbase + OFF_C + (k % DEPTH) * CBYTES;
+    QP::issue_with(half, pl, groups, rgroups, tid, [&](int off, int i, int wbase) {
+      dma16a(blk + off, cst + (uint32_t)(i * NT + wbase) * 16);
+    });
+  };
+  // wait until code stage k has landed, `later` code stages having been issued after it
+  auto wait_later = [&](int later) {
+    auto wait_n = [&](auto K) {
+      if (w < 4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * QP::LOADS_LO));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * QP::LOADS_HI));
+    };
+    switch (later) {
+      case 0: wait_n(std::integral_constant<int, 0>{}); break;
+      case 1: wait_n(std::integral_constant<int, 1>{}); break;
+      case 2: wait_n(std::integral_constant<int, 2>{}); break;
+      default: wait_n(std::integral_constant<int, 3>{}); break;
+    }
+  };
+
+  // wavefront 0: scores of stage s, softmax, P into pbuf(s), rescale factors into alpha[s & 1]
+  auto score_softmax = [&](int s) {
+    const bf16_t* KS = bbuf(s);
+    int half_unused, valid;
+    stage_src(s, half_unused, valid);
+    // k-step ks reads logical piece 4 ks + lg of token t, physical 8 (ks / 2) + ((4 (ks & 1) + lg)
+    // ^ sw(t)): one base per token tile and k-step parity, the rest an immediate offset.  The
+    // fragments of k-step ks + KD are read while k-step ks multiplies; two accumulation chains
+    // per token tile keep dependent MFMAs four apart.
+    f32x4 sv[2];
+    {
+      const bf16_t* kb[2][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = tt * 16 + lr;
+        const int f = sw(t);
+        kb[tt][0] = &KS[t * 576 + (lg ^ f) * 8];
+        kb[tt][1] = &KS[t * 576 + ((4 + lg) ^ f) * 8 - 32];
+      }
+      constexpr int KD = 4;
+      bf16x8 a[KD + 1][2];
+#pragma unroll
+      for (int i = 0; i < KD; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) a[i][tt] = *(const bf16x8*)(kb[tt][i & 1] + i * 32);
+      f32x4 ac[2][2] = {};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + KD < 18) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            a[(ks + KD) % (KD + 1)][tt] = *(const bf16x8*)(kb[tt][(ks + KD) & 1] + (ks + KD) * 32);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          ac[tt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % (KD + 1)][tt], qreg[ks], ac[tt][ks & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sv[0] = ac[0][0] + ac[0][1];
+      sv[1] = ac[1][0] + ac[1][1];
+    }
+    // token 16 tt + 4 lg + i of the stage is kept if it is valid and within the row's limit
+    const int tok0 = T0 + s * ST_TOK + 4 * lg;
+    float mt = NEG_INF;
+    if (valid == ST_TOK && T0 + s * ST_TOK + ST_TOK - 1 <= L - p.s_q) {
+      // every token of the stage is visible to every row (rows past R have zero queries)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[tt][i] *= p.scale_log2;
+          mt = fmaxf(mt, sv[tt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = 16 * tt + 4 * lg + i;
+          const bool ok = k < valid && tok0 + 16 * tt + i <= lim;
+          sv[tt][i] = ok ? sv[tt][i] * p.scale_log2 : NEG_INF;
+          mt = fmaxf(mt, sv[tt][i]);
+        }
+    }
+    mt = wave_max_16_32(mt);
+    const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
+    const float mu = mn == NEG_INF ? 0.f : mn;
+    const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
+    l_s *= al;
+    l_x *= al;
+    m_s = mn;
+    bf16_t* P = pbuf(s);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint32_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pf = __builtin_amdgcn_exp2f(sv[tt][i] - mu);
+        pb[i] = f32_to_bf16_bits(pf);
+        l_s += bf16_bits_to_f32(pb[i]);
+        l_x += pf;
+      }
+      *(uint2*)&P[lr * PROW + tt * 16 + lg * 4] = uint2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+    }
+    if (lg == 0) alpha[s & 1][lr] = al;
+  };
+
+  // O[16 rows][64 cg .. 64 cg + 63] = alpha(s) O + P(s) . C(s) into accumulators o
+  auto pv = [&](int s, int cg, f32x4 (&o)[4]) {
+    const bf16_t* KS = bbuf(s);
+    const f32x4 al = *(const f32x4*)&alpha[s & 1][lg * 4];
+    if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) o[nt] *= al;
+    }
+    f32x4* acc = o;
+    const bf16x8 a = *(const bf16x8*)&pbuf(s)[lr * PROW + lg * 8];
+    const int t0 = lg * 8 + (lr >> 2);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int d = cg * 64 + nt * 16 + (lr & 3) * 4;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[st_off(t0, d)]);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[st_off(t0 + 4, d)]);
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[nt], 0, 0, 0);
+    }
+  };
+
+  if (nst > 0) {
+    // prologue: code stages 0..3 issued, 0 and 1 dequantised by every thread, code 4 issued,
+    // stage 0 scored, code 2 landed
+    for (int k = 0; k < DEPTH && k < nst; ++k) issue(k);
+    wait_later(min(nst - 1, DEPTH - 1) - min(nst - 1, 1));
+    lds_barrier();
+      for (int k = 0; k < 2 && k < nst; ++k) {
+      int half_unused, valid;
+      stage_src(k, half_unused, valid);
+      QP::dequant(cslot(k), valid, gl_log2, gr_log2, bbuf(k), tid);
+    }
+    lds_barrier();
+    if (DEPTH < nst) issue(DEPTH);
+    if (w == 0) score_softmax(0);
+    if (2 < nst) wait_later(min(nst - 1, DEPTH) - 2);
+    lds_barrier();
+
+    for (int s = 0; s < nst; ++s) {
+      // refill the slot of code s + 1 (dequantised in step s - 1) with code s + 5
+      if (s + DEPTH + 1 < nst) issue(s + DEPTH + 1);
+      if (w == 0 && s + 1 < nst) score_softmax(s + 1);
+      pv(s, w, acc);
+      // dequantisation by the six wavefronts that share no SIMD with wavefront 0 (waves are
+      // dealt to SIMDs w mod 4): the scorer keeps its SIMD's issue slots to itself
+      if ((w & 3) != 0 && s + 2 < nst) {
+        int half_unused, valid;
+        stage_src(s + 2, half_unused, valid);
+        const int q = (w < 4 ? w - 1 : w - 2) * 64 + lane;
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+          QP::dequant_task(cslot(s + 2), valid, it * 384 + q, gl_log2, gr_log2, bbuf(s + 2));
+      }
+      // code s + 3 landed (dequantised in the next step); nobody reads the buffers of stage s
+      if (s + 3 < nst) wait_later(min(nst - 1, s + DEPTH + 1) - (s + 3));
+      lds_barrier();
+    }
+  }
+
+  // ---- finish: wavefront 0 publishes the row sums and maxima; every wavefront normalises and
+  // writes its 64 columns
+  if (w == 0) {
+    const float ls = wave_sum_16_32(l_s), lx = wave_sum_16_32(l_x);
+    if (lg == 0) {
+      fin[0][lr] = ls;
+      fin[1][lr] = lx;
+      fin[2][lr] = m_s;
+    }
+  }
+  lds_barrier();
+  const size_t unit_row0 = ((size_t)b * p.max_chunks + c) * R;
+  auto write_cols = [&](int cg, const f32x4 (&o4)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lg * 4 + i;
+      if (row >= R) continue;
+      const float lt = fin[0][row];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const size_t obase = (unit_row0 + row) * 512 + cg * 64 + lr;
+      if (p.out_bf16) {
+        bf16_t* o = (bf16_t*)p.out;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          o[obase + nt * 16] = __builtin_bit_cast(bf16_t, (uint16_t)f32_to_bf16_bits(o4[nt][i] * inv));
+      } else {
+        float* o = (float*)p.out;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) o[obase + nt * 16] = o4[nt][i] * inv;
+      }
+    }
+  };
+  write_cols(w, acc);
+  if (p.out_lse != nullptr && tid < 16 && tid < R) {
+    const float lt = fin[1][tid];
+    p.out_lse[unit_row0 + tid] = lt > 0.f ? (fin[2][tid] + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
 template <int RT, int FMT>
 static hipError_t launch_mfma(const DecodeParams& p, int grid, hipStream_t st) {
+  if constexpr (RT == 1 && FMT != FMT_BF16) {
+    // quantised cache, at most 16 rows: the pipelined kernel
+    if (p.q_f32)
+      hipLaunchKernelGGL((decode_pipe_kernel<FMT, true>), dim3(grid), dim3(NT), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_pipe_kernel<FMT, false>), dim3(grid), dim3(NT), 0, st, p);
+    return hipGetLastError();
+  }
   if (p.q_f32)
     hipLaunchKernelGGL((decode_mfma_kernel<RT, FMT, true>), dim3(grid), dim3(NT), 0, st, p);
   else

@@ -219,12 +219,12 @@ template <int FMT>
 struct QuantStage {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
   static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
-  static constexpr int PPT = LB / 16;              // latent code pieces per token
   static constexpr int LOADS = FMT == FMT_INT4 ? 3 : 2;
   static constexpr int SLOTS = LOADS * NT;         // INT4: 648 used, INT2: 456
   static constexpr int DEPTH = FMT == FMT_INT4 ? 6 : 8;   // code ring slots
 
-  // per-lane source offsets inside a block of DMA instruction i, for the block's two halves
+  // per-lane source offsets inside a block of DMA instruction i, for the block's two halves;
+  // the code stage is the four planes of the half block, token-major, one after the other
   struct Offsets {
     uint32_t o[2][LOADS];
   };
@@ -241,13 +241,13 @@ struct QuantStage {
       int q = slot < n_all ? slot : slot - n_all;   // padding slots re-load a real piece
       int base, hstride;
       if (q < n_lc) {
-        base = pl.lc + ((q % ST_TOK) * PPT + q / ST_TOK) * 16;
+        base = pl.lc + q * 16;
         hstride = ST_TOK * LB;
       } else if ((q -= n_lc) < n_ls) {
         base = pl.ls + q * 16;
         hstride = ST_TOK * groups * 4;
       } else if ((q -= n_ls) < n_rc) {
-        base = pl.rc + ((q % ST_TOK) * 2 + q / ST_TOK) * 16;
+        base = pl.rc + q * 16;
         hstride = ST_TOK * 32;
       } else {
         base = pl.rs + (q - n_rc) * 16;
@@ -263,25 +263,29 @@ struct QuantStage {
     dma16(blk, half ? off.o[1][i] : off.o[0][i], lds + (uint32_t)(i * NT * 16));
   }
 
-  // Thread q dequantises latent chunks kk and kk + 8 (kk = q / 32; 32 elements each, inside
-  // one quantisation group since groups are multiples of 32) and RoPE elements 8 kk .. 8 kk + 7
-  // of token t = q mod 32.  Group sizes are powers of two (gl = log2 latent group, gr = log2
-  // rope group).  load_chunk(h) reads latent chunk kk + 8 h (code words and the raw scale
-  // word), chunk_piece() converts and stores one of its four 8-element pieces (INT2: two);
-  // load_rope() and rope_piece() do the same for the RoPE piece.
+  // Thread q dequantises latent tasks q and q + 256 (32-element chunks, each inside one
+  // quantisation group since groups are multiples of 32) and RoPE task q; the task to (token,
+  // chunk) maps keep a wavefront's code reads and bf16 stores free of bank conflicts.  Group
+  // sizes are powers of two (gl = log2 latent group, gr = log2 rope group).  load_chunk(h)
+  // reads the code words and the raw scale word of latent task q + 256 h, chunk_piece()
+  // converts and stores one of its four 8-element pieces (INT2: two); load_rope() and
+  // rope_piece() do the same for the RoPE piece.
   struct Chunk {
     uint32_t c[BITS];   // INT4: 16 code bytes, INT2: 8
     uint32_t sz;        // fp16 (scale, zero), 0 for tokens past the end
+    int row, p0;        // stage row of the token, physical piece of the chunk's first 8 elements
   };
   __device__ __forceinline__ static Chunk load_chunk(const uint8_t* cst, int valid, int gl, int h, int tid) {
     asm volatile("" : "+v"(tid));
-    const int t = tid & 31, kk = (tid >> 5) + 8 * h;
+    int t, kk;
+    lat_task(tid + 256 * h, t, kk);
     const int ls = ST_TOK * LB;                    // scale plane of the latent codes
     Chunk d;
     const uint32_t sz = *(const uint32_t*)(cst + ls + (((t << (9 - gl)) + ((kk * 32) >> gl)) << 2));
     d.sz = t < valid ? sz : 0u;
-    const int cpiece = (kk * 32 * BITS) >> 7, cbyte = ((kk * 32 * BITS) >> 3) & 15;
-    const uint8_t* code = cst + ((cpiece * ST_TOK + t) << 4) + cbyte;
+    d.row = t * 576;
+    d.p0 = (4 * kk) ^ sw(t);
+    const uint8_t* code = cst + t * LB + kk * 4 * BITS;
     if constexpr (BITS == 4) {
       const u32x4 c = *(const u32x4*)code;
       d.c[0] = c[0];
@@ -295,43 +299,41 @@ struct QuantStage {
     }
     return d;
   }
-  __device__ __forceinline__ static void chunk_piece(const Chunk& d, int h, int jj, bf16_t* stage, int tid) {
-    asm volatile("" : "+v"(tid));
-    const int t = tid & 31, kk = (tid >> 5) + 8 * h;
+  __device__ __forceinline__ static void chunk_piece(const Chunk& d, int jj, bf16_t* stage) {
     float sc, zs;
     scale_zero(d.sz, sc, zs);
-    const int p0 = (4 * kk) ^ sw(t);
     if constexpr (BITS == 4) {
-      *(u32x4*)&stage[t * 576 + ((p0 ^ jj) << 3)] = dequant_int4x8(d.c[jj], sc, zs);
+      *(u32x4*)&stage[d.row + ((d.p0 ^ jj) << 3)] = dequant_int4x8(d.c[jj], sc, zs);
     } else {
       // INT2: pieces jj and jj + 1 (jj even) from one code word
       uint32_t t_lo, t_hi;
       int2_table(sc, zs, t_lo, t_hi);
       u32x4 lo, hi;
       dequant_int2x16(d.c[jj >> 1], t_lo, t_hi, lo, hi);
-      *(u32x4*)&stage[t * 576 + ((p0 ^ jj) << 3)] = lo;
-      *(u32x4*)&stage[t * 576 + ((p0 ^ (jj + 1)) << 3)] = hi;
+      *(u32x4*)&stage[d.row + ((d.p0 ^ jj) << 3)] = lo;
+      *(u32x4*)&stage[d.row + ((d.p0 ^ (jj + 1)) << 3)] = hi;
     }
   }
   struct Rope {
     uint32_t c, sz;
+    int dst;            // stage element of the piece
   };
   __device__ __forceinline__ static Rope load_rope(const uint8_t* cst, int valid, int gl, int gr, int tid) {
     asm volatile("" : "+v"(tid));
-    const int t = tid & 31, ri = tid >> 5;
+    int t, ri;
+    rope_task(tid, t, ri);
     const int rbase = ST_TOK * LB + (ST_TOK << (9 - gl + 2));
     Rope r;
     const uint32_t sz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << (6 - gr)) + ((ri * 8) >> gr)) << 2));
     r.sz = t < valid ? sz : 0u;
-    r.c = *(const uint32_t*)(cst + rbase + (((ri >> 2) * ST_TOK + t) << 4) + (ri & 3) * 4);
+    r.c = *(const uint32_t*)(cst + rbase + t * 32 + ri * 4);
+    r.dst = st_off(t, 512 + ri * 8);
     return r;
   }
-  __device__ __forceinline__ static void rope_piece(const Rope& r, bf16_t* stage, int tid) {
-    asm volatile("" : "+v"(tid));
-    const int t = tid & 31, ri = tid >> 5;
+  __device__ __forceinline__ static void rope_piece(const Rope& r, bf16_t* stage) {
     float sc, zs;
     scale_zero(r.sz, sc, zs);
-    *(u32x4*)&stage[st_off(t, 512 + ri * 8)] = dequant_int4x8(r.c, sc, zs);
+    *(u32x4*)&stage[r.dst] = dequant_int4x8(r.c, sc, zs);
   }
   __device__ __forceinline__ static void dequant(const uint8_t* cst, int valid, int gl, int gr, bf16_t* stage,
                                                  int tid) {
@@ -340,10 +342,10 @@ struct QuantStage {
     const Rope r = load_rope(cst, valid, gl, gr, tid);
     constexpr int STEP = BITS == 4 ? 1 : 2;   // pieces per chunk_piece call
 #pragma unroll
-    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d0, 0, jj, stage, tid);
+    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d0, jj, stage);
 #pragma unroll
-    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d1, 1, jj, stage, tid);
-    rope_piece(r, stage, tid);
+    for (int jj = 0; jj < 4; jj += STEP) chunk_piece(d1, jj, stage);
+    rope_piece(r, stage);
   }
 };
 

@@ -28,6 +28,27 @@ __device__ __forceinline__ int sw(int t) { return (t & 2) | ((t >> 1) & 4) | ((t
 // bf16 element offset of (token t, latent/rope column d) in a stage
 __device__ __forceinline__ int st_off(int t, int d) { return t * 576 + (((d >> 3) ^ sw(t)) << 3) + (d & 7); }
 
+// Code stage of a quantised cache: the four code planes of a half block copied as they lie in
+// the block, token-major: latent codes [32][LB], latent scales [32][groups] (4 bytes each), RoPE
+// codes [32][32], RoPE scales [32][rgroups].
+//
+// Dequantisation tasks of a code stage.  Latent task k (0..511) is 32-element chunk kk of token
+// t, RoPE task r (0..255) is the 8-element piece ri of token t.  Each aligned block of 64 tasks
+// (one wavefront instruction) reads its codes and writes its bf16 pieces on 64 distinct banks
+// per cycle under the lane sets above: a latent block covers the tokens {T, T^2, T^17, T^19}
+// with all 16 chunks each (lanes 4m .. 4m + 3 read 64 consecutive code bytes), a RoPE block 8
+// consecutive tokens with all 8 pieces each.
+__device__ __forceinline__ void lat_task(int k, int& t, int& kk) {
+  const int l = k & 63, blk = k >> 6, tau = (l >> 2) & 3;
+  t = ((blk & 1) | ((blk & 6) << 1)) ^ ((tau & 1) << 1) ^ ((tau >> 1) * 17);
+  kk = (l & 3) | ((((l >> 4) & 3) ^ (((l >> 2) & 1) * 3)) << 2);
+}
+__device__ __forceinline__ void rope_task(int r, int& t, int& ri) {
+  const int l = r & 63;
+  t = (r >> 6) * 8 + (l & 3) + ((l >> 5) << 2);
+  ri = (l >> 2) & 7;
+}
+
 // s_waitcnt immediate: wait until at most n vector-memory operations are outstanding
 __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8); }
 
