@@ -213,7 +213,7 @@ int32_t run_proj(const void* x, int64_t sn, int64_t sh, int32_t xdt, const void*
   p.H = H;
   p.K = K;
   p.M = M;
-  p.aligned16 = aligned(x, 16) && aligned(w, 16);
+  p.aligned16 = aligned(x, 16) && aligned(w, 16) && aligned(y, 16);
   return hip_status(mla::launch_proj(p, (hipStream_t)stream));
 }
 

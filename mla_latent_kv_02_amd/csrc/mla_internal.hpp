@@ -86,7 +86,7 @@ struct ProjParams {
   void* Y;                  // [N][H][M]
   int y_f32;
   int N, H, K, M;
-  int aligned16;            // X and W base addresses are 16-byte aligned
+  int aligned16;            // X, W and Y base addresses are 16-byte aligned
 };
 
 struct DequantParams {

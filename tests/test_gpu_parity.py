@@ -230,6 +230,35 @@ def test_out_proj_matches_oracle(mla, H, N):
     assert norm_err(got, ref) <= TOL_F32 * 10
 
 
+# Column block (MB) and row block the launcher picks for each case, from its rule (widest of
+# 128/64/32/16 dividing M with >= 512 workgroups, rows in blocks of 64 when N >= 64, else 16):
+@pytest.mark.parametrize("H,N,K,M,xf32,yf32", [
+    (128, 4, 128, 512, False, False),   # MB 128, one 16-row block, eight tiles per workgroup
+    (64, 4, 128, 512, True, False),     # MB 64, four tiles: one per wave
+    (128, 4, 512, 128, True, True),     # MB 32, two tiles: K split over two wave pairs
+    (16, 16, 512, 128, True, True),     # MB 16, one tile: K split over the four waves
+    (7, 67, 96, 48, False, True),       # 64-row blocks, the second one ragged; three k-steps
+    (2, 130, 512, 64, True, False),     # three 64-row blocks, the last with two rows
+    (9, 20, 256, 160, False, False),    # two 16-row blocks, M not a multiple of 32
+])
+def test_projection_shapes(mla, H, N, K, M, xf32, yf32):
+    rng = np.random.default_rng(H * 1000 + N * 10 + K + M)
+    x = rng.standard_normal((N, H, K))
+    x = x.astype(np.float32).astype(np.float64) if xf32 else bf16_exact(x)
+    w = bf16_exact(rng.standard_normal((H, K, M)) / np.sqrt(K))
+    _say("projection", H, N, K, M, xf32, yf32)
+    xt = torch.from_numpy(x).to(torch.float32 if xf32 else torch.bfloat16).to(dev())
+    got = mla.absorb_q(xt, torch.from_numpy(w).to(torch.bfloat16).to(dev()),
+                       out_dtype=torch.float32 if yf32 else torch.bfloat16)
+    got = got.float().cpu().numpy()
+    ref = oracle.absorb_q(x, w)
+    tol = TOL_F32 * (10 if xf32 else 1)   # fp32 X enters as bf16 hi + lo terms (~16 bits)
+    if yf32:
+        assert norm_err(got, ref) <= tol
+    else:
+        assert_bf16_output(got, ref, tol)
+
+
 # ------------------------------------------------------------------------------------ fp32 path
 
 def test_tiny_fp32_pipeline_matches_unabsorbed(mla):
