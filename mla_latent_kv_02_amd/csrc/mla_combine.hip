@@ -94,14 +94,15 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Combine: lse = log sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c over the partitions of
-// one (b, row), o_c = part_o_c (partition mode) or part_o_c * part_inv_c (range mode).  One workgroup of 128 threads per (b, row); weights go through LDS in
-// batches of 128 partitions and each thread sums 4 columns with independent loads.
+// Combine: lse = log sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c over the partials of one
+// (b, row), o_c = part_o_c (partition mode) or part_o_c * part_inv_c (range mode).  One
+// workgroup of 128 threads per (b, row), each thread owning 4 columns (of every 512).  The
+// partials are taken in batches of CB: all loads of a batch (lse, 1/sum and the thread's
+// columns) are issued together, so a (b, row) with at most CB partials costs one memory round
+// trip; batches merge with a running maximum.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
-  __shared__ float wsh[128];   // weight of a partial's lse
-  __shared__ float vsh[128];   // the same times its normalisation factor
-  __shared__ float red[2];
+  constexpr int CB = 8;
   const int tid = threadIdx.x;
   const int R = p.R;
   const int b = blockIdx.x / R, r = blockIdx.x % R;
@@ -122,56 +123,71 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     nch = i1 - i0 + 1;
     u0 = (size_t)b + i0;
   }
-  // max of the partition LSEs
-  float m = NEG_INF;
-  for (int c = tid; c < nch; c += 128) m = fmaxf(m, p.part_lse[(u0 + c) * R + r]);
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(red[0], red[1]);
   const int d_c = p.d_c;
-  f32x4 acc[4];
-  for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 128) {
-    const int n = min(128, nch - c0);
-    __syncthreads();
-    if (tid < n) {
-      const float lc = p.part_lse[(u0 + c0 + tid) * R + r];
-      const float wc = m == NEG_INF ? 0.f : expf(lc - m);
-      wsh[tid] = wc;
-      vsh[tid] = p.part_inv == nullptr ? wc : wc * p.part_inv[(u0 + c0 + tid) * R + r];
-    }
-    __syncthreads();
-    for (int j = 0; j < n; ++j) wsum += wsh[j];
-    for (int k = 0; k < 4; ++k) {
-      const int d = (tid + k * 128) * 4;
-      if (d >= d_c) break;
-      const float* base = p.part_o + ((u0 + c0) * R + r) * (size_t)d_c + d;
-      const size_t stride = (size_t)R * d_c;
-      int j = 0;
-      for (; j + 4 <= n; j += 4) {
-        const f32x4 v0 = *(const f32x4*)(base + (j + 0) * stride);
-        const f32x4 v1 = *(const f32x4*)(base + (j + 1) * stride);
-        const f32x4 v2 = *(const f32x4*)(base + (j + 2) * stride);
-        const f32x4 v3 = *(const f32x4*)(base + (j + 3) * stride);
-        acc[k] += vsh[j] * v0 + vsh[j + 1] * v1 + vsh[j + 2] * v2 + vsh[j + 3] * v3;
+  const size_t stride = (size_t)R * d_c;          // between consecutive partials
+  const bool vec4 = (d_c & 3) == 0;               // 16-byte column groups (else element by element)
+  float lse_out = NEG_INF;
+  for (int d = tid * 4; d < d_c; d += 512) {
+    float m = NEG_INF, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += CB) {
+      const int n = min(CB, nch - c0);
+      const size_t ub = (u0 + c0) * R + r;
+      float lc[CB], iv[CB];
+      f32x4 v[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const bool ok = j < n;
+        lc[j] = ok ? p.part_lse[ub + (size_t)j * R] : NEG_INF;
+        iv[j] = ok && p.part_inv != nullptr ? p.part_inv[ub + (size_t)j * R] : 1.f;
+        v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+          const float* src = p.part_o + ub * d_c + d + j * stride;
+          if (vec4) {
+            v[j] = *(const f32x4*)src;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[j][i] = d + i < d_c ? src[i] : 0.f;
+          }
+        }
       }
-      for (; j < n; ++j) acc[k] += vsh[j] * *(const f32x4*)(base + j * stride);
+      float mb = NEG_INF;
+#pragma unroll
+      for (int j = 0; j < CB; ++j) mb = fmaxf(mb, lc[j]);
+      if (mb > m) {
+        // every earlier weight is relative to m; m = -inf means nothing was added yet
+        const float sc = m == NEG_INF ? 0.f : expf(m - mb);
+        acc *= sc;
+        wsum *= sc;
+        m = mb;
+      }
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const float wc = lc[j] == NEG_INF ? 0.f : expf(lc[j] - m);
+        wsum += wc;
+        acc += (wc * iv[j]) * v[j];
+      }
     }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int k = 0; k < 4; ++k) {
-    const int d = (tid + k * 128) * 4;
-    if (d >= d_c) break;
-    const f32x4 v = acc[k] * inv;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const f32x4 o = acc * inv;
     const size_t ob = ((size_t)b * R + r) * d_c + d;
-    if (p.out_bf16)
-      *(uint2*)((bf16_t*)p.out + ob) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    else
-      *(f32x4*)((float*)p.out + ob) = v;
+    if (!vec4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (d + i >= d_c) break;
+        if (p.out_bf16)
+          ((uint16_t*)p.out)[ob + i] = (uint16_t)f32_to_bf16_bits(o[i]);
+        else
+          ((float*)p.out)[ob + i] = o[i];
+      }
+    } else if (p.out_bf16) {
+      *(uint2*)((bf16_t*)p.out + ob) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      *(f32x4*)((float*)p.out + ob) = o;
+    }
+    lse_out = wsum > 0.f ? m + logf(wsum) : NEG_INF;
   }
-  if (p.out_lse != nullptr && tid == 0) p.out_lse[(size_t)b * R + r] = wsum > 0.f ? m + logf(wsum) : NEG_INF;
+  if (p.out_lse != nullptr && tid == 0) p.out_lse[(size_t)b * R + r] = lse_out;
 }
 
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st) {

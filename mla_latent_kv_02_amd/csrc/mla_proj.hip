@@ -235,14 +235,15 @@ static hipError_t launch_mb(const ProjParams& p, int mb, int n_nb, hipStream_t s
 }
 
 // Row blocks of 64 rows for N >= 64, else of 16; column block: the widest of 128/64/32/16
-// dividing M whose grid still gives >= 512 workgroups (two per CU) and whose W tile fits
-// 64 KB of LDS, else the narrowest.
+// dividing M whose grid still gives enough workgroups (two per CU; one per CU for fp32 X,
+// which every column block re-reads) and whose W tile fits 64 KB of LDS, else the narrowest.
 template <bool XF32>
 static hipError_t launch_proj_mfma(const ProjParams& p, hipStream_t st) {
   const int nbt = p.N >= 64 ? 4 : 1;
   const int n_nb = (p.N + 16 * nbt - 1) / (16 * nbt);
+  const int64_t want = XF32 ? 256 : 512;
   int mb = 128;
-  while (mb > 16 && (p.M % mb != 0 || (int64_t)p.K * mb * 2 > 64 * 1024 || (int64_t)p.H * (p.M / mb) * n_nb < 512))
+  while (mb > 16 && (p.M % mb != 0 || (int64_t)p.K * mb * 2 > 64 * 1024 || (int64_t)p.H * (p.M / mb) * n_nb < want))
     mb >>= 1;
   const bool short_k = p.K <= 128;
   if (nbt == 4)

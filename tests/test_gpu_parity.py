@@ -277,11 +277,13 @@ def test_tiny_fp32_pipeline_matches_unabsorbed(mla):
     assert float(np.max(np.abs(step.lse.cpu().numpy() - ref_lse))) <= TOL_F32
 
 
-@pytest.mark.parametrize("lens,s_q", [([1, 63, 64, 65, 300], 1), ([2, 64, 129], 2)])
-def test_fp32_decode_ragged(mla, lens, s_q):
-    cfg = CONFIGS["1"].with_(s_q=s_q)
+@pytest.mark.parametrize("lens,s_q,d_c,d_r", [([1, 63, 64, 65, 300], 1, 64, 16), ([2, 64, 129], 2, 64, 16),
+                                              ([5, 130, 300], 1, 66, 10)])
+def test_fp32_decode_ragged(mla, lens, s_q, d_c, d_r):
+    """fp32 cache, ragged lengths; d_c = 66 leaves a two-column group at the end of every row."""
+    cfg = CONFIGS["1"].with_(s_q=s_q, d_c=d_c, d_r=d_r)
     x = make_inputs(cfg, 50, lens=lens)
-    _say("fp32 ragged", lens, s_q)
+    _say("fp32 ragged", lens, s_q, d_c, d_r)
     for splits in (1, 3):
         o, lse, ref_o, ref_lse = _decode_stage(mla, x, num_splits=splits)
         assert norm_err(o, ref_o) <= TOL_F32
