@@ -237,6 +237,8 @@ def main():
         roof["kernel"] = "mla_decode_paged (decode_f32_kernel + combine_kernel)"
     elif s_q * H >= 96:
         roof["kernel"] = "mla_decode_paged (decode_rows_kernel + combine_kernel)"
+    elif cfg.latent_fmt in ("int4", "int2") and s_q * H <= 16:
+        roof["kernel"] = "mla_decode_paged (decode_pipe_kernel + combine_kernel)"
     else:
         roof["kernel"] = "mla_decode_paged (decode_mfma_kernel + combine_kernel)"
     roof["algorithmic_bytes_per_launch"] = alg_bytes
