@@ -42,6 +42,15 @@
 namespace mla {
 namespace rows {
 
+// Piece swizzle of this kernel's bf16 stages: piece c of token t sits at c ^ rsw(t).  The
+// P.V operand reads here take tokens 0..7 (and 16..23, 8..15, 24..31) per 32 lanes, in the
+// order the score accumulators give P; the shared stage swizzle sw() maps t and t + 4 to the
+// same banks for that order.  t & 7 keeps these reads, the score operand reads and the
+// dequantised piece stores on 64 distinct banks per cycle (exhaustive check under the
+// measured lane-set model), and rsw(t + 16) = rsw(t).
+__device__ __forceinline__ int rsw(int t) { return t & 7; }
+__device__ __forceinline__ int rst_off(int t, int d) { return t * 576 + (((d >> 3) ^ rsw(t)) << 3) + (d & 7); }
+
 constexpr int NT = 256;                  // 4 wavefronts, one per SIMD
 constexpr int ROWS = 128;                // query rows per workgroup
 constexpr int RT = 2;                    // 16-row tiles per wavefront
@@ -189,7 +198,7 @@ __device__ __forceinline__ bf16x8 load_q8(const void* base, size_t elem_off, boo
 // ----------------------------------------------------------------------------------------
 
 // bf16 rows: a half block is 32 tokens x 72 pieces = 2304 pieces, 9 per thread.  Slot k of the
-// stage receives (token k / 72, logical piece (k mod 72) ^ sw(token)).  All 32 rows are copied
+// stage receives (token k / 72, logical piece (k mod 72) ^ rsw(token)).  All 32 rows are copied
 // (a block is always allocated whole); rows past the sequence end are zeroed before use.
 struct BfProducer {
   static constexpr int LOADS = ST_TOK * 72 / NT;
@@ -203,7 +212,7 @@ struct BfProducer {
     for (int i = 0; i < LOADS; ++i) {
       const int slot = i * NT + tid;
       const int t = slot / 72;
-      r.o[i] = (uint32_t)(t * 1152 + (((slot - t * 72) ^ sw(t)) << 4));
+      r.o[i] = (uint32_t)(t * 1152 + (((slot - t * 72) ^ rsw(t)) << 4));
     }
     return r;
   }
@@ -284,7 +293,7 @@ struct QuantStage {
     const uint32_t sz = *(const uint32_t*)(cst + ls + (((t << (9 - gl)) + ((kk * 32) >> gl)) << 2));
     d.sz = t < valid ? sz : 0u;
     d.row = t * 576;
-    d.p0 = (4 * kk) ^ sw(t);
+    d.p0 = (4 * kk) ^ rsw(t);
     const uint8_t* code = cst + t * LB + kk * 4 * BITS;
     if constexpr (BITS == 4) {
       const u32x4 c = *(const u32x4*)code;
@@ -327,7 +336,7 @@ struct QuantStage {
     const uint32_t sz = *(const uint32_t*)(cst + rbase + ST_TOK * 32 + (((t << (6 - gr)) + ((ri * 8) >> gr)) << 2));
     r.sz = t < valid ? sz : 0u;
     r.c = *(const uint32_t*)(cst + rbase + t * 32 + ri * 4);
-    r.dst = st_off(t, 512 + ri * 8);
+    r.dst = rst_off(t, 512 + ri * 8);
     return r;
   }
   __device__ __forceinline__ static void rope_piece(const Rope& r, bf16_t* stage) {
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int t = tt * 16 + lr_;
-        const int f = sw(t);
+        const int f = rsw(t);
         kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
         kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
       }
@@ -748,16 +757,16 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     // ---- O^T[col][row] += V^T[col][token] . P^T[token][row]; the 8 tokens of lane group lg
     // are 4 lg .. 4 lg + 3 (first read) and 16 + 4 lg .. 16 + 4 lg + 3 (second read)
     {
-      // column d = 16 nt + 4 (lr & 3) of token t is element st_off(t, d); with nt = 4 q + r its
-      // piece is (2 nt + h) ^ sw(t) = 8 q + ((2 r + h) ^ sw(t)), h = (lr & 3) / 2, since sw < 8:
-      // four per-lane bases (r) and an immediate offset of 64 q elements.  Token tb = ta + 16 has
-      // sw(tb) = sw(ta) ^ 1, so its pieces sit one piece up or down: a per-lane shift db.
+      // column d = 16 nt + 4 (lr & 3) of token t is element rst_off(t, d); with nt = 4 q + r its
+      // piece is (2 nt + h) ^ rsw(t) = 8 q + ((2 r + h) ^ rsw(t)), h = (lr & 3) / 2, since
+      // rsw < 8: four per-lane bases (r) and an immediate offset of 64 q elements.  Token
+      // tb = ta + 16 has rsw(tb) = rsw(ta): its pieces sit exactly 16 rows further on (db).
       int lane_ = lane;
       asm volatile("" : "+v"(lane_));   // recomputed per stage rather than held across the loop
       const int lrp = lane_ & 15, lgp = lane_ >> 4;
       const int ta = 4 * lgp + (lrp >> 2);
-      const int h = (lrp & 3) >> 1, fa = sw(ta);
-      const int db = 16 * 576 + (((h ^ fa) & 1) ? -8 : 8);
+      const int h = (lrp & 3) >> 1, fa = rsw(ta);
+      constexpr int db = 16 * 576;
       int oa[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
