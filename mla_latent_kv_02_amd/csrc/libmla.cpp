@@ -353,6 +353,8 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
       c.out = a->o_lat;
       c.out_bf16 = a->o_dtype == MLA_BF16;
       c.out_lse = a->lse;
+      // a sequence meets about n_ranges / batch + 1 ranges
+      c.many_parts = plan.splits > 16 * a->batch;
       e = mla::launch_combine(c, a->batch, st);
       if (e != hipSuccess) return MLA_ERR_HIP;
     }
@@ -412,6 +414,7 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     c.out = a->o_lat;
     c.out_bf16 = a->o_dtype == MLA_BF16;
     c.out_lse = a->lse;
+    c.many_parts = plan.splits > 16;
     e = mla::launch_combine(c, a->batch, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
   }

@@ -97,13 +97,14 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
 // Combine: lse = log sum_c exp(lse_c), o = sum_c exp(lse_c - lse) o_c over the partials of one
 // (b, row), o_c = part_o_c (partition mode) or part_o_c * part_inv_c (range mode).  One
 // workgroup of 128 threads per (b, row), each thread owning 4 columns (of every 512).  The
-// partials are taken in batches of CB: all loads of a batch (lse, 1/sum and the thread's
-// columns) are issued together, so a (b, row) with at most CB partials costs one memory round
-// trip; batches merge with a running maximum.  Weights use the hardware exp2 (relative error
+// partials are taken in batches of CB (8, or 32 when rows usually hold more than 16
+// partials): all loads of a batch (lse, 1/sum and the thread's columns) are issued together,
+// so a (b, row) with at most CB partials costs one memory round trip; batches merge with a
+// running maximum.  Weights use the hardware exp2 (relative error
 // ~1e-7 for the lse differences that occur, far inside the fp32 tolerance).
 // ---------------------------------------------------------------------------------------
+template <int CB>
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
-  constexpr int CB = 8;
   constexpr float LOG2E = 1.4426950408889634f;
   const int tid = threadIdx.x;
   const int R = p.R;
@@ -198,7 +199,10 @@ hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st) {
 }
 
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(batch * p.R), dim3(128), 0, st, p);
+  if (p.many_parts)
+    hipLaunchKernelGGL(combine_kernel<32>, dim3(batch * p.R), dim3(128), 0, st, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(batch * p.R), dim3(128), 0, st, p);
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ struct CombineParams {
   void* out;
   int out_bf16;
   float* out_lse;
+  int many_parts;           // rows usually hold more than 16 partials: wider load batches
 };
 
 struct ProjParams {

@@ -47,6 +47,17 @@ def test_range_count_invariance(mla, splits):
     _check(*_decode_stage(mla, x, num_splits=splits))
 
 
+@pytest.mark.parametrize("splits", [40, 100])
+def test_range_many_pieces_per_sequence(mla, splits):
+    """More than 16 ranges per sequence (the combine's wide load batches).  95 blocks over two
+    sequences: num_splits = 40 asks for 80 ranges (two blocks each, ~24 partials per row: one
+    ragged batch of 32), 100 is capped at one block per range (~48 partials per row: a full
+    batch of 32 and a ragged one)."""
+    x = make_inputs(CONFIGS["3"], 49, lens=[2900, 3100], H=128)
+    _say("many pieces", splits)
+    _check(*_decode_stage(mla, x, num_splits=splits))
+
+
 def test_range_many_sequences_two_queries(mla):
     """s_q = 2 with 128 heads: 256 rows, two row groups over the same ranges."""
     rng = np.random.default_rng(5)
