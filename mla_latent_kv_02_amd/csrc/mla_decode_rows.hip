@@ -682,7 +682,6 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         else score2<false, false, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
         __builtin_amdgcn_sched_barrier(0);
         if (ks + KD < 18) a[nx][1] = *(const bf16x8*)(kb[1][(ks + KD) & 1] + (ks + KD) * 32);
-        if ((ks & 1) && (ks >> 1) < LOADS && refill) issue_one(s_new, sr_new, ks >> 1);
         if (ks == 0) score2<true, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
         else if (ks == 17) score2<false, false, true>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
         else score2<false, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
@@ -832,6 +831,12 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       n_tok = st_tok[s + 1];
       n_bid = st_bid[min(nst - 1, s + 1 + AHEAD)];
       n_btok = st_tok[min(nst - 1, s + 1 + AHEAD)];
+    }
+    // the refill of this step, issued where the wave waits anyway: an issue blocks while many
+    // reads are outstanding, and between MFMAs that stalls the matrix pipe
+    if (refill) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) issue_one(s_new, sr_new, i);
     }
     // the next step's stage has landed and nobody reads stage s any more
     if constexpr (!QUANT) {
