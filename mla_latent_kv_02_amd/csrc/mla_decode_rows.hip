@@ -222,8 +222,8 @@ struct BfProducer {
 };
 
 // Quantised latent (INT4 or INT2) + INT4 rope: the four code planes of a half block are copied
-// into a code stage [lc | ls | rc | rs] of SLOTS 16-byte slots; latent and rope code pieces are
-// stored piece-major (slot k * 32 + t holds piece k of token t), scale planes as they are.
+// as they lie in the block (token-major) into a code stage [lc | ls | rc | rs] of SLOTS 16-byte
+// slots.
 template <int FMT>
 struct QuantStage {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
