@@ -147,9 +147,11 @@ int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes);
 
 /* The work split mla_decode_paged will use.  Fewer than 96 query rows per sequence
  * (s_q * num_heads): *num_splits partitions of the longest sequence of *tiles_per_split
- * 64-token blocks each.  96 rows or more: the batch's blocks, sequence after sequence, cut
- * into *num_splits equal ranges (one workgroup per range and 128-row group) of at most
- * *tiles_per_split blocks.  num_cus = compute units to plan for (0 = query the current
+ * 64-token blocks each.  96 rows or more: the batch's blocks, sequence after sequence, each
+ * non-empty sequence counted with 3 extra positions for the cost of starting it (none when
+ * every sequence already starts on a range boundary), cut into
+ * *num_splits equal ranges (one workgroup per range and 128-row group) of at most
+ * *tiles_per_split positions.  num_cus = compute units to plan for (0 = query the current
  * device).  Pure host logic. */
 int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* num_splits,
                         int32_t* tiles_per_split);

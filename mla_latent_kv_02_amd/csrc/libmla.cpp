@@ -99,6 +99,12 @@ constexpr int kRowsMinRows = 96;        // query rows per sequence from which th
 constexpr int kRowsPerGroup = 128;      // its rows per workgroup
 constexpr int kRowsMaxBatch = 8192;     // sequences it tabulates in LDS
 constexpr int kRowsMaxRangeBlocks = 256;
+// Block-space positions charged for the start of each sequence when the row-owner kernel cuts
+// the batch into ranges: a workgroup whose range starts a sequence in its middle stores a
+// 256 KB piece and loads the next sequence's 144 KB of queries there, about the time of two
+// to three blocks; 3 gave the shortest decode among 1..6 on the 128-head bf16 workloads.
+// The kernel drops the charge when every sequence already starts on a range boundary.
+constexpr int kRowsPhantom = 3;
 
 Plan make_plan(const mla_decode_args* a, int cus) {
   Plan p{};
@@ -109,11 +115,12 @@ Plan make_plan(const mla_decode_args* a, int cus) {
     p.rows = true;
     p.rg = (int)ceil_div(R, kRowsPerGroup);
     const int64_t bound = (int64_t)a->batch * ceil_div(a->max_seq_len, kBlock);  // blocks, at most
+    const int64_t vbound = bound + (int64_t)a->batch * kRowsPhantom;              // positions, at most
     int64_t n = a->num_splits > 0 ? (int64_t)a->num_splits * a->batch : std::max<int64_t>(1, cus / p.rg);
-    n = std::max<int64_t>(n, ceil_div(bound, kRowsMaxRangeBlocks));
+    n = std::max<int64_t>(n, ceil_div(vbound, kRowsMaxRangeBlocks));
     n = std::min<int64_t>(n, bound);
     p.splits = (int)n;
-    p.tpc = (int)ceil_div(bound, n);
+    p.tpc = (int)ceil_div(vbound, n);
     return p;
   }
   int64_t target;  // workgroups to aim for
@@ -326,6 +333,7 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     r.R = a->s_q * a->num_heads;
     r.RG = plan.rg;
     r.n_ranges = plan.splits;
+    r.phantom = kRowsPhantom;
     const int64_t units = (int64_t)plan.splits * plan.rg;
     if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
     r.total_units = (int)units;

@@ -120,9 +120,13 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
     u0 = (size_t)b * p.max_chunks;
   } else {
-    const int per = p.meta[0], first = p.meta[1 + b], nblk = p.meta[2 + b] - first;
+    // sequence b's blocks are the last n_b positions of its part of the block space
+    int L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
     if (nblk <= 0) return;  // empty sequence: written by the decode kernel
-    const int i0 = first / per, i1 = (first + nblk - 1) / per;
+    const int per = p.meta[0], last = p.meta[2 + b] - 1;
+    const int i0 = (last - nblk + 1) / per, i1 = last / per;
     nch = i1 - i0 + 1;
     u0 = (size_t)b + i0;
   }

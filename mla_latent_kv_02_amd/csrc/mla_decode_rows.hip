@@ -29,7 +29,8 @@
 //
 // Work balance: the batch's cache blocks, sequence after sequence, are cut into n_ranges equal
 // ranges (one workgroup per range and row group); a range may cover several sequences or part
-// of one.  Every piece (a sequence's blocks inside one range) is stored unnormalised with
+// of one.  Each sequence's start is charged a few extra positions, the cost of a piece's store
+// and query load, so that ranges which start a sequence in their middle get fewer blocks.  Every piece (a sequence's blocks inside one range) is stored unnormalised with
 // 1 / sum(P) and its lse; combine_kernel normalises and merges.
 #include <hip/hip_runtime.h>
 
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   __shared__ int st_info[MAX_ST];
   __shared__ int st_len[MAX_ST];
   __shared__ int sh_scan[NT / 64 + 1];
+  __shared__ int sh_scanc[NT / 64];
   __shared__ f32x4 resc[NT];         // per-lane scratch of scale_tile
 
   const int tid = threadIdx.x;
@@ -392,11 +394,18 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   const int range = u / p.RG;
   const int B = p.B, R = p.R;
 
-  // ---- flattened block space: sequence b owns blocks [P_b, P_b + n_b); P and the clamped
-  // lengths live in the (not yet used) stage memory while the stage table is built
+  // ---- flattened block space: sequence b owns positions [P_b, P_{b+1}): G positions that
+  // stand for the cost of starting a piece (a query load, a piece store), then its n_b cache
+  // blocks (an empty sequence owns none).  Ranges cut this space into equal parts, so a range
+  // that starts a sequence in its middle gets correspondingly fewer blocks.  G = p.phantom
+  // unless every sequence already starts on a range boundary of the plain block space (equal
+  // lengths that divide evenly), where no range pays for a start and G = 0.  P, the clamped
+  // lengths and the count of non-empty sequences before b live in the (not yet used) stage
+  // memory while the stage table is built.
   int* tabP = (int*)smem;            // B + 1 entries
   int* tabL = tabP + (B + 1);        // B entries
-  int carry = 0;
+  int* tabC = tabL + B;              // B + 1 entries, dead once P includes the charges
+  int carry = 0, carry_c = 0;
   for (int base = 0; base < B; base += NT) {
     const int b = base + tid;
     int L = 0;
@@ -405,29 +414,53 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
     }
     const int n = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
-    int x = n;
+    const int c = n > 0 ? 1 : 0;
+    int x = n, xc = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      const int yc = __shfl_up(xc, o, 64);
+      if (lane >= o) {
+        x += y;
+        xc += yc;
+      }
     }
-    if (lane == 63) sh_scan[w] = x;
+    if (lane == 63) {
+      sh_scan[w] = x;
+      sh_scanc[w] = xc;
+    }
     __syncthreads();
-    int woff = 0, tot = 0;
+    int woff = 0, tot = 0, woffc = 0, totc = 0;
 #pragma unroll
     for (int j = 0; j < NT / 64; ++j) {
       woff += j < w ? sh_scan[j] : 0;
       tot += sh_scan[j];
+      woffc += j < w ? sh_scanc[j] : 0;
+      totc += sh_scanc[j];
     }
     if (b < B) {
       tabP[b] = carry + woff + x - n;
       tabL[b] = L;
+      tabC[b] = carry_c + woffc + xc - c;
     }
     carry += tot;
+    carry_c += totc;
     __syncthreads();
   }
-  const int total = carry;
-  if (tid == 0) tabP[B] = total;
+  if (tid == 0) {
+    tabP[B] = carry;
+    tabC[B] = carry_c;
+  }
+  __syncthreads();
+  {
+    const int per0 = max(1, (carry + p.n_ranges - 1) / p.n_ranges);
+    int off = 0;
+    for (int b = tid; b < B; b += NT) off |= (tabP[b + 1] > tabP[b] && tabP[b] % per0 != 0) ? 1 : 0;
+    const int G = __syncthreads_or(off) ? p.phantom : 0;
+    for (int b = tid; b <= B; b += NT) tabP[b] += G * tabC[b];
+  }
+  __syncthreads();
+  const int total = tabP[B];
   const int per = max(1, (total + p.n_ranges - 1) / p.n_ranges);
   __syncthreads();
   if (u == 0) {
@@ -463,8 +496,6 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   const int start = range * per;
   const int end = min(total, start + per);
   if (start >= end) return;
-  const int nblk = end - start;      // <= MAX_RANGE_BLOCKS
-  const int nst = 2 * nblk;
 
   // sequence holding block j: the last b with P_b <= j (P is non-decreasing; j < total)
   auto seq_of = [&](int j) {
@@ -520,33 +551,59 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     start_piece(b0, tabL[b0], false);   // completed with the block-table loads below
   }
 
-  // ---- stage table: block j = start + tid -> its sequence, block id and tokens
-  if (tid < nblk) {
+  // ---- stage table: position j = start + tid -> its sequence and, for a cache block, its
+  // rank k among the range's blocks (a workgroup scan), block id and tokens
+  {
     const int j = start + tid;
-    const int b = seq_of(j);
-    const int P0 = tabP[b], P1 = tabP[b + 1], L = tabL[b];
-    const int jb = j - P0;
-    int id = p.block_table[(size_t)b * p.bt_stride + jb];
-    int v = min(BLOCK_TOKENS, L - jb * BLOCK_TOKENS);
-    if (id < 0 || (int64_t)id >= p.num_blocks) {
-      id = 0;
-      v = 0;
+    int b = 0, jb = -1;
+    if (j < end) {
+      b = seq_of(j);
+      jb = j - (tabP[b + 1] - (tabL[b] + BLOCK_TOKENS - 1) / BLOCK_TOKENS);   // < 0: a phantom
     }
+    const int is_blk = jb >= 0 ? 1 : 0;
+    int x = is_blk;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = 2 * tid + h;
-      const int valid = min(ST_TOK, max(0, v - ST_TOK * h));
-      int info = b | (valid << 20);
-      if (h == 0 && (tid == 0 || jb == 0)) info |= INFO_START;
-      if (h == 1 && (tid == nblk - 1 || j == P1 - 1)) info |= INFO_END;
-      st_bid[k] = id;
-      st_tok[k] = jb * BLOCK_TOKENS + ST_TOK * h;
-      st_info[k] = info;
-      st_len[k] = L;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
+    if (lane == 63) sh_scan[w] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      woff += i < w ? sh_scan[i] : 0;
+      tot += sh_scan[i];
+    }
+    const int k = woff + x - is_blk;
+    if (is_blk) {
+      const int L = tabL[b];
+      int id = p.block_table[(size_t)b * p.bt_stride + jb];
+      int v = min(BLOCK_TOKENS, L - jb * BLOCK_TOKENS);
+      if (id < 0 || (int64_t)id >= p.num_blocks) {
+        id = 0;
+        v = 0;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = 2 * k + h;
+        const int valid = min(ST_TOK, max(0, v - ST_TOK * h));
+        int info = b | (valid << 20);
+        if (h == 0 && (k == 0 || jb == 0)) info |= INFO_START;
+        if (h == 1 && (k == tot - 1 || j == tabP[b + 1] - 1)) info |= INFO_END;
+        st_bid[kk] = id;
+        st_tok[kk] = jb * BLOCK_TOKENS + ST_TOK * h;
+        st_info[kk] = info;
+        st_len[kk] = L;
+      }
+    }
+    if (tid == 0) sh_scan[NT / 64] = tot;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
+  const int nblk = sh_scan[NT / 64];   // cache blocks of the range, <= MAX_RANGE_BLOCKS
+  if (nblk == 0) return;               // phantom positions only
+  const int nst = 2 * nblk;
 
   // ---- stages
   const uint32_t smem_base = lds_addr(smem);

@@ -30,8 +30,9 @@ struct DecodeParams {
 };
 
 // Arguments of the row-owner decode kernel (128 query rows per workgroup).  The batch's
-// cache blocks, sequence after sequence, are cut into n_ranges equal ranges; workgroup
-// (range i, row group r) attends its rows over the blocks of range i.  Every piece (the
+// cache blocks, sequence after sequence, each non-empty sequence preceded by `phantom`
+// positions that stand for the cost of starting a piece, are cut into n_ranges equal ranges;
+// workgroup (range i, row group r) attends its rows over the blocks of range i.  Every piece (the
 // blocks of one sequence inside one range) leaves a partial in slot b + i: o unnormalised,
 // 1 / sum(P) and lse; the combine normalises and merges.  Empty sequences are written to
 // out/out_lse directly.
@@ -50,6 +51,7 @@ struct RowsParams {
   int max_seq_len;
   int B, s_q, H, R, RG;
   int n_ranges, units_per_xcd, total_units;
+  int phantom;              // block-space positions charged for each non-empty sequence's start
   float scale_log2;
   void* out;                // o_lat [B][R][512]
   int out_bf16;
@@ -57,7 +59,8 @@ struct RowsParams {
   float* part_o;            // [B + n_ranges - 1][R][512]
   float* part_lse;          // [B + n_ranges - 1][R]
   float* part_inv;          // [B + n_ranges - 1][R]
-  int32_t* meta;            // [0]: blocks per range; [1 + b]: first block of sequence b, b <= B
+  int32_t* meta;            // [0]: positions per range; [1 + b]: first position of sequence b, b <= B
+                            // (its blocks are the last n_b positions before that of b + 1)
 };
 
 // Combine of split partials.  Partition mode (meta == null): max_chunks partitions of tpc

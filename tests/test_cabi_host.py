@@ -80,8 +80,9 @@ def test_split_plan_covers_the_longest_sequence():
 
 
 def test_range_plan_covers_the_batch():
-    """96 or more query rows per sequence: the batch's blocks cut into equal ranges of at most
-    256 blocks, one round of workgroups over the CUs by default."""
+    """96 or more query rows per sequence: the batch's blocks, with 3 positions charged for
+    each sequence's start, cut into equal ranges of at most 256 positions, one round of
+    workgroups over the CUs by default."""
     cus = 256
     for B, H, s_q, L, ns in [(64, 128, 1, 8192, 0), (64, 128, 2, 8192, 0), (4, 128, 1, 131072, 0),
                              (1, 128, 1, 1, 0), (3, 128, 1, 700, 2), (4096, 128, 1, 65536, 0), (2, 64, 2, 300, 0)]:
@@ -89,11 +90,12 @@ def test_range_plan_covers_the_batch():
         st, ranges, per = _plan(a, cus)
         assert st == 0
         bound = B * -(-L // 64)                  # blocks of the batch, at most
+        vbound = bound + 3 * B                   # with the positions charged per sequence
         rg = -(-(s_q * H) // 128)
-        assert 1 <= ranges <= bound and ranges * per >= bound and per <= 256
+        assert 1 <= ranges <= bound and ranges * per >= vbound and per <= 256
         if ns:
-            assert ranges == max(min(ns * B, bound), -(-bound // 256))
-        elif bound >= cus // rg and -(-bound // 256) <= cus // rg:
+            assert ranges == max(min(ns * B, bound), -(-vbound // 256))
+        elif bound >= cus // rg and -(-vbound // 256) <= cus // rg:
             assert ranges == cus // rg
 
 

@@ -146,3 +146,28 @@ def test_out_of_range_block_ids_are_skipped(mla, name, H):
     ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c2, k2,
                                           np.array([len(keep0), len(keep1)]), x.cfg.s_q, x.cfg.sm_scale)
     _check(o, lse, ref_o, ref_lse)
+
+
+def test_range_start_charge(mla):
+    """Ranges cut a block space in which each non-empty sequence's start counts 3 extra
+    positions (the sequence starts here are off the plain range boundaries).  Lengths within
+    the V3 workload's [1024, 8192].  [2000, 2000] with 24 ranges of 3 positions: the first range
+    holds only start positions and does no work, one range ends with the second sequence's
+    start positions and the next begins with them.  [1100, 0, 2000, 1300] with 28 ranges adds
+    an empty sequence (written by the range holding its position), a range in the middle that
+    holds only start positions, and a last range with no position at all."""
+    x = make_inputs(CONFIGS["3"], 53, lens=[2000, 2000], H=128)
+    _say("start charge", [2000, 2000], 12)
+    _check(*_decode_stage(mla, x, num_splits=12))
+    x = make_inputs(CONFIGS["3"], 54, lens=[1100, 1, 2000, 1300], H=128)
+    lens = x.seq_lens.copy()
+    lens[1] = 0
+    _say("start charge", [int(v) for v in lens], 7)
+    q_lat64, o, lse = _run(mla, x, lens, x.block_table, 7)
+    assert np.all(o[1] == 0.0) and np.all(lse[1] == -np.inf)
+    keep = [0, 2, 3]
+    c, k = logical_cache(x)
+    ref_o, ref_lse = oracle.attend_latent(q_lat64[keep], x.q_rope[keep].astype(np.float64),
+                                          [c[b] for b in keep], [k[b] for b in keep], x.seq_lens[keep],
+                                          x.cfg.s_q, x.cfg.sm_scale)
+    _check(o[keep], lse[keep], ref_o, ref_lse)
