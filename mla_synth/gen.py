@@ -52,7 +52,7 @@ def quantise_rtn(x: np.ndarray, group: int, bits: int):
     s16 = ((mx - mn) / qmax).astype(np.float16)
     s16 = np.where(s16 == 0, np.float16(1.0), s16)
     s = s16.astype(np.float64)
-    z = np.clip(np.rint(-mn / s), 0, qmax)
+    z = np.clip(np.rint(-mn / s), 0, qmax) + 0.0   # an integer: a zero is stored as +0
     codes = np.clip(np.rint(xg / s[..., None]) + z[..., None], 0, qmax).astype(np.uint8)
     sz = np.stack([s16, z.astype(np.float16)], axis=-1)
     return codes.reshape(x.shape), sz
@@ -67,6 +67,43 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     for k in range(per):
         out |= (c[..., k] << np.uint8(bits * k)).astype(np.uint8)
     return out
+
+
+def append_rows(cfg: MlaConfig, n: int, seed: int):
+    """Seeded new-token rows for the cache writer: c [n, d_c] and k_rope [n, d_r] float32,
+    drawn like the workload's cache (N(0,1), the workload's outlier channels scaled), with edge
+    rows mixed in: a constant row, an all-negative row, rows of tiny (fp16-subnormal scale) and
+    of large magnitude, and rows whose values lie exactly half a quantisation step between two
+    INT4 codes (groups [0, 3.75], step 0.25) or two INT2 codes (groups [0, 0.75], step 0.25)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = rng.standard_normal((n, cfg.d_c), dtype=np.float32)
+    k = rng.standard_normal((n, cfg.d_r), dtype=np.float32)
+    if cfg.outliers:
+        ch = np.sort(rng.choice(cfg.d_c, cfg.outliers, replace=False))
+        c[:, ch] *= np.float32(cfg.outlier_scale)
+    edges = []
+    for d in (cfg.d_c, cfg.d_r):
+        j = np.arange(d)
+        tie4 = ((j % 15) + 0.5) * 0.25
+        tie4[j % 64 == 0], tie4[j % 64 == 1] = 0.0, 3.75
+        tie2 = ((j % 3) + 0.5) * 0.25
+        tie2[j % 32 == 0], tie2[j % 32 == 1] = 0.0, 0.75
+        edges.append([np.full(d, 0.7), -np.abs(rng.standard_normal(d)) - 0.5, rng.standard_normal(d) * 1e-6,
+                      rng.standard_normal(d) * 3e3, tie4, tie2])
+    for r, (ec, ek) in enumerate(zip(*edges)):
+        if r < n:
+            c[r], k[r] = ec, ek
+    return c, k
+
+
+def append_slots(num_blocks: int, n: int, seed: int) -> np.ndarray:
+    """n distinct cache slots (block * 64 + position) of a pool of num_blocks blocks, seeded,
+    with about one in twenty replaced by -1 or by a slot past the pool (both to be skipped)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slots = rng.choice(num_blocks * BLOCK_TOKENS, n, replace=False).astype(np.int64)
+    bad = rng.random(n) < 0.05
+    slots[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, num_blocks * BLOCK_TOKENS + 7)
+    return slots.astype(np.int32)
 
 
 def rope_rotate(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
@@ -257,5 +294,6 @@ def attended_pairs(seq_lens: np.ndarray, s_q: int) -> int:
     return int(sum(int((L - s_q + i + 1).sum()) for i in range(s_q)))
 
 
-__all__ = ["MlaInputs", "make_inputs", "workload", "quantise_rtn", "pack_codes", "to_bf16_exact",
+__all__ = ["MlaInputs", "make_inputs", "workload", "quantise_rtn", "pack_codes", "to_bf16_exact", "append_rows",
+           "append_slots",
            "bf16_bits", "rope_rotate", "attended_pairs"]

@@ -24,6 +24,12 @@ What it computes, and where the pages fix it:
   scale s per (token, group); the product is exact, the bf16 rounding is the
   only rounding (a reading: the pages give no formula).
 
+* The cache writer (``write_tokens``) fills a paged pool with new tokens: float
+  caches take the values (float32) or their bf16 rounding; quantised caches take
+  the round-to-nearest asymmetric quantiser per token and group (``quantise_rtn``;
+  the pages pair an INT4 or INT2 latent with an INT4 RoPE key and name
+  round-to-nearest as the plain quantiser: QuantMLA abstract and podcast page).
+
 Conventions (readings where the pages are silent): W_UK[h] is [d_n, d_c] with
 k_nope = W_UK[h] c; W_UV[h] is [d_c, d_v] with v = c W_UV[h]; query i of s_q
 attends cached tokens 0 .. L - s_q + i; lse is the natural log of the softmax
@@ -86,8 +92,8 @@ def dequant(codes: np.ndarray, sz: np.ndarray, group: int) -> np.ndarray:
 def quantise_rtn(x: np.ndarray, group: int, bits: int):
     """Round-to-nearest asymmetric quantiser (independent of the input generator's).
 
-    Per group: s = fp16((max-min)/(2^b-1)) (1 if 0); z = clamp(rint(-min/s), 0, 2^b-1);
-    code = clamp(rint(x/s) + z, 0, 2^b-1).  Used to pin the stored codes.
+    Per group: s = fp16((max-min)/(2^b-1)) (1 if 0); z = clamp(rint(-min/s), 0, 2^b-1), an
+    integer (stored as +0 when it is zero); code = clamp(rint(x/s) + z, 0, 2^b-1).
     """
     qmax = 2 ** bits - 1
     x = np.asarray(x, dtype=np.float64)
@@ -102,7 +108,7 @@ def quantise_rtn(x: np.ndarray, group: int, bits: int):
         s = ((hi - lo) / qmax).astype(np.float16)
         s[s == 0] = np.float16(1)
         sd = s.astype(np.float64)
-        z = np.minimum(np.maximum(np.rint(-lo / sd), 0), qmax)
+        z = np.minimum(np.maximum(np.rint(-lo / sd), 0), qmax) + 0.0   # an integer: a zero is +0
         q = np.rint(seg / sd[..., None]) + z[..., None]
         codes[..., g * group:(g + 1) * group] = np.minimum(np.maximum(q, 0), qmax).astype(np.uint8)
         sz[..., g, 0] = s
@@ -175,6 +181,58 @@ def read_pool(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray, l
             out.setdefault("r_sz", []).append(
                 np.ascontiguousarray(plane("rs", (d_r // g_r) * 4)).view(np.float16).reshape(L, d_r // g_r, 2))
     return out
+
+
+def pack_codes_bytes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Packed bytes from codes, the inverse of unpack_codes: element e goes to byte
+    e*bits//8 at bit (e*bits) % 8."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n = codes.shape[-1]
+    out = np.zeros(codes.shape[:-1] + (n * bits // 8,), dtype=np.uint8)
+    for e in range(n):
+        out[..., (e * bits) // 8] |= (codes[..., e] << ((e * bits) % 8)).astype(np.uint8)
+    return out
+
+
+def write_tokens(pool: np.ndarray, slots: Sequence[int], c_new: np.ndarray, k_new: np.ndarray, latent_fmt: str,
+                 rope_fmt: str, d_c: int, d_r: int, g_c: int = 0, g_r: int = 0) -> np.ndarray:
+    """The pool after writing token i (latent c_new[i], RoPE key k_new[i]) into slot slots[i] =
+    block * 64 + position; slots outside the pool are skipped.  A float cache stores the row
+    [c | k_rope] as float32 or rounded to bf16; a quantised cache stores the codes and fp16
+    (s, z) pairs of quantise_rtn, per token and group, in its four planes.  The latent at INT4
+    or INT2 with an INT4 RoPE key is the pairing the QuantMLA abstract reports; round-to-nearest
+    is the plain quantiser of the QuantMLA podcast page's comparison.  Inputs must be exact in
+    float32 for float caches.  Returns a new array shaped like pool.
+    """
+    off, bb = block_planes(latent_fmt, rope_fmt, d_c, d_r, g_c, g_r)
+    shape = np.asarray(pool).shape
+    out = np.array(pool, dtype=np.uint8, copy=True).reshape(-1, bb)
+    nblk = out.shape[0]
+    for i, slot in enumerate(np.asarray(slots, dtype=np.int64).tolist()):
+        if slot < 0 or slot >= nblk * BLOCK:
+            continue
+        blk, pos = divmod(slot, BLOCK)
+        c = np.asarray(c_new[i], dtype=np.float64)
+        k = np.asarray(k_new[i], dtype=np.float64)
+        if latent_fmt in FMT_BYTES:
+            row = np.concatenate([c, k])
+            if latent_fmt == "f32":
+                f = row.astype(np.float32)
+                if not np.array_equal(f.astype(np.float64), row):
+                    raise ValueError("float32 cache rows must be float32-exact")
+                raw = f.view(np.uint8)
+            else:
+                raw = (bf16_round(row).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16).view(np.uint8)
+            out[blk, pos * raw.size:(pos + 1) * raw.size] = raw
+            continue
+        for vec, g, fmt, pc, ps in ((c, g_c, latent_fmt, "lc", "ls"), (k, g_r, rope_fmt, "rc", "rs")):
+            bits = FMT_BITS[fmt]
+            codes, sz = quantise_rtn(vec[None, :], g, bits)
+            packed = pack_codes_bytes(codes[0], bits)
+            sz_bytes = np.ascontiguousarray(sz[0], dtype=np.float16).view(np.uint8).reshape(-1)
+            out[blk, off[pc] + pos * packed.size: off[pc] + (pos + 1) * packed.size] = packed
+            out[blk, off[ps] + pos * sz_bytes.size: off[ps] + (pos + 1) * sz_bytes.size] = sz_bytes
+    return out.reshape(shape)
 
 
 # --------------------------------------------------------------------------- attention
@@ -316,6 +374,7 @@ def exact_dequant_value(code: int, z: float, s: float) -> float:
     return float(sign * Fraction(lo, 128) * (Fraction(2) ** e))
 
 
-__all__ = ["bf16_round", "unpack_codes", "dequant", "quantise_rtn", "token_bytes", "block_planes",
+__all__ = ["bf16_round", "unpack_codes", "pack_codes_bytes", "write_tokens", "dequant", "quantise_rtn",
+           "token_bytes", "block_planes",
            "read_pool", "absorb_q", "out_proj", "attend_latent", "decode_unabsorbed", "decode_absorbed",
            "merge_partials", "dequant_cache", "exact_dequant_value"]
