@@ -219,6 +219,17 @@ def main():
     decode_ms = call_ms(g_dec, reps_dec, replays)
     proj_ms = call_ms(g_out, 8, replays)
 
+    # (3) the cache writer for this step's new tokens (the last s_q positions of every
+    # sequence), timed like the calls above after the decode timings, into one pool copy
+    pos = (x.seq_lens.astype("int64")[:, None] - s_q + np.arange(s_q)[None, :]).reshape(-1)
+    seq = np.repeat(np.arange(B), s_q)
+    slots = torch.from_numpy((x.block_table[seq, pos // 64].astype("int64") * 64 + pos % 64).astype("int32")).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    c_new = torch.randn((B * s_q, cfg.d_c), generator=gen, device=dev).to(qr.dtype)
+    k_new = torch.randn((B * s_q, cfg.d_r), generator=gen, device=dev).to(qr.dtype)
+    g_app = capture_calls(lambda i: mla.append_kv(c_new, k_new, pools[0], desc, slots), 8)
+    append_ms = call_ms(g_app, 8, replays)
+
     bpt = mla.block_bytes(desc) // 64
     alg_bytes, cache_bytes, flops, units = algorithmic(x, bpt)
     value = units / (ms_per_step * 1e-3)
@@ -266,7 +277,8 @@ def main():
            "step_launch": "eager" if args.no_graph else "hip_graph",
            "call_timing": "per-call HIP graphs of back-to-back calls, events on the launch stream",
            "decode_us": round(decode_ms * 1e3, 2), "absorb_us": round(absorb_ms * 1e3, 2),
-           "out_proj_us": round(proj_ms * 1e3, 2), "hbm_tbps": round(gbs / 1e3, 3),
+           "out_proj_us": round(proj_ms * 1e3, 2), "append_us": round(append_ms * 1e3, 2),
+           "append_tokens": B * s_q, "hbm_tbps": round(gbs / 1e3, 3),
            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "cache_bytes": cache_bytes}
     log(f"timed {K} steps: {ms_per_step * 1e3:.2f} us/step, decode {decode_ms * 1e3:.2f} us")
     if not args.no_cpu_baseline:

@@ -185,6 +185,30 @@ int32_t mla_out_proj(const void* o_lat, int64_t o_stride_n, int64_t o_stride_h, 
                      int32_t H, int32_t d_c, int32_t d_v, void* stream);
 
 /*
+ * mla_append_kv: write n new tokens (their latent c_KV and RoPE key) into their slots of a
+ *   paged cache, the step before decode that fills the cache the decode reads.
+ *   Token i: c_new[i * c_stride + 0 .. d_c) and k_rope_new[i * k_stride + 0 .. d_r), both of
+ *   in_dtype (MLA_F32 or MLA_BF16; the RoPE key already rotated), go to slot slots[i] =
+ *   block * 64 + position of cache_pool (num_blocks blocks laid out as desc says; slots is
+ *   int32 on the device).  Slots outside [0, num_blocks * 64) are skipped (padding); two
+ *   tokens with the same slot in one call race.  Nothing else in the pool is written.
+ *   Float caches store the values (fp32) or their bf16 rounding (ties to even).  Quantised
+ *   caches store codes of the plain round-to-nearest asymmetric quantiser, per token and per
+ *   group of channels (the latent at INT4 or INT2 with an INT4 RoPE key: QuantMLA English
+ *   abstract, arxivdaily QuantMLA page; round-to-nearest as the plain quantiser: QuantMLA
+ *   podcast page, comparison part), computed in float64 from the exact inputs:
+ *     s = fp16((max - min) / (2^b - 1)), 1 where that is 0 (ties to even);
+ *     z = clamp(rint(-min / s), 0, 2^b - 1), stored as fp16 (+0 when zero);
+ *     code = clamp(rint(x / s) + z, 0, 2^b - 1),  rint ties to even,
+ *   so that the decode reads back RNE_bf16((code - z) * s).  Inputs must be finite.
+ *   Quantised formats need d_c, d_r and both group sizes to be multiples of 8 with
+ *   group / 8 a power of two <= 64 (else MLA_ERR_UNSUPPORTED).  n = 0 is a no-op.
+ */
+int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,
+                      int32_t in_dtype, const int32_t* slots, int64_t n, void* cache_pool, int64_t num_blocks,
+                      const mla_cache_desc* desc, void* stream);
+
+/*
  * mla_dequant_blocks (test/debug): materialise blocks of a paged cache as bf16.
  *   out_bf16[k][t][0:d_c] = latent of token t of block block_ids[k], [d_c:d_c+d_r] = RoPE key,
  *   for k < n_blocks, t < 64.  Uses the same device unpack/dequant code as the decode

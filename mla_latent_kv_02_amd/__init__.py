@@ -19,7 +19,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FMT_BF16, MLA_FMT_F32, MLA_FMT_INT2, M
                    CacheDesc, DecodeArgs, FMT_BY_NAME)
 
 __all__ = ["MlaError", "cache_desc", "block_bytes", "plane_offsets", "absorb_q", "decode_paged", "out_proj",
-           "dequant_blocks", "decode_workspace_size", "decode_plan", "DecodeStep", "lib"]
+           "dequant_blocks", "append_kv", "decode_workspace_size", "decode_plan", "DecodeStep", "lib"]
 
 
 class MlaError(RuntimeError):
@@ -199,6 +199,30 @@ def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor)
                                         _stream(pool.device))
     _check(st, "mla_dequant_blocks")
     return out
+
+
+def append_kv(c_new: torch.Tensor, k_rope_new: torch.Tensor, pool: torch.Tensor, desc: CacheDesc,
+              slots: torch.Tensor) -> None:
+    """Write n new tokens into their cache slots (block * 64 + position), quantising for
+    INT4/INT2 caches: c_new [n, d_c] and k_rope_new [n, d_r] of one dtype (bf16 or fp32,
+    rows may be strided), slots int32 [n] (negative = skip).  pool [num_blocks, block_bytes]
+    uint8 is updated in place on the current stream."""
+    _need_cuda(c_new, k_rope_new, pool, slots)
+    if c_new.dim() != 2 or k_rope_new.dim() != 2 or c_new.shape[0] != k_rope_new.shape[0]:
+        raise ValueError("c_new and k_rope_new must be [n, d] with the same n")
+    if c_new.dtype != k_rope_new.dtype:
+        raise ValueError("c_new and k_rope_new must share a dtype")
+    if c_new.stride(1) != 1 or k_rope_new.stride(1) != 1:
+        raise ValueError("rows must be dense")
+    if slots.dtype != torch.int32 or not slots.is_contiguous() or slots.numel() != c_new.shape[0]:
+        raise ValueError("slots must be dense int32 [n]")
+    n = c_new.shape[0]
+    st = _lib.load().mla_append_kv(ctypes.c_void_p(c_new.data_ptr()), c_new.stride(0) if n > 1 else c_new.shape[1],
+                                   ctypes.c_void_p(k_rope_new.data_ptr()),
+                                   k_rope_new.stride(0) if n > 1 else k_rope_new.shape[1], _dt(c_new),
+                                   ctypes.c_void_p(slots.data_ptr()), n, ctypes.c_void_p(pool.data_ptr()),
+                                   pool.shape[0], ctypes.byref(desc), _stream(pool.device))
+    _check(st, "mla_append_kv")
 
 
 @dataclass

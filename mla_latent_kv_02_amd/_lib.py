@@ -44,6 +44,8 @@ _SIGS = {
     "mla_decode_paged": (c_int32, [POINTER(DecodeArgs), c_void_p]),
     "mla_dequant_blocks": (c_int32, [c_void_p, c_int64, POINTER(CacheDesc), c_void_p, c_int32, c_void_p,
                                      c_void_p]),
+    "mla_append_kv": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,
+                                c_int64, POINTER(CacheDesc), c_void_p]),
 }
 
 _lib = None

@@ -429,6 +429,51 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   return MLA_OK;
 }
 
+int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,
+                      int32_t in_dtype, const int32_t* slots, int64_t n, void* cache_pool, int64_t num_blocks,
+                      const mla_cache_desc* desc, void* stream) {
+  Layout lay;
+  if (n < 0 || num_blocks <= 0 || !valid_dtype(in_dtype)) return MLA_ERR_INVALID_ARG;
+  if (!cache_layout(desc, &lay)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!c_new || !k_rope_new || !slots || !cache_pool) return MLA_ERR_INVALID_ARG;
+  if (c_stride < desc->d_c || k_stride < desc->d_r) return MLA_ERR_INVALID_ARG;
+  const int esz = in_dtype == MLA_F32 ? 4 : 2;
+  if (!aligned(c_new, esz) || !aligned(k_rope_new, esz) || !aligned(slots, 4) || !aligned(cache_pool, 16))
+    return MLA_ERR_INVALID_ARG;
+  if (n > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_fmt(desc->latent_fmt)) {
+    // one lane per 8 channels; a group is a power-of-two number of lanes within a wavefront
+    auto lanes_ok = [](int d, int g) {
+      const int l = g / 8;
+      return d % 8 == 0 && g % 8 == 0 && l <= 64 && (l & (l - 1)) == 0;
+    };
+    if (!lanes_ok(desc->d_c, desc->latent_group) || !lanes_ok(desc->d_r, desc->rope_group)) return MLA_ERR_UNSUPPORTED;
+  }
+  mla::AppendParams p{};
+  p.c = c_new;
+  p.k = k_rope_new;
+  p.in_f32 = in_dtype == MLA_F32;
+  p.c_stride = c_stride;
+  p.k_stride = k_stride;
+  p.slots = slots;
+  p.n = n;
+  p.pool = (uint8_t*)cache_pool;
+  p.num_blocks = num_blocks;
+  p.block_bytes = lay.block_bytes;
+  p.off_lc = lay.off[0];
+  p.off_ls = lay.off[1];
+  p.off_rc = lay.off[2];
+  p.off_rs = lay.off[3];
+  p.d_c = desc->d_c;
+  p.d_r = desc->d_r;
+  p.g_lat = desc->latent_group > 0 ? desc->latent_group : 1;
+  p.g_rope = desc->rope_group > 0 ? desc->rope_group : 1;
+  p.fmt_lat = desc->latent_fmt;
+  p.fmt_rope = desc->rope_fmt;
+  return hip_status(mla::launch_append(p, (hipStream_t)stream));
+}
+
 int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
                            const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream) {
   Layout lay;

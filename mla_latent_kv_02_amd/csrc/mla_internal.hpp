@@ -104,11 +104,29 @@ struct DequantParams {
   uint16_t* out;            // [n][64][d_c + d_r] bf16 bits
 };
 
+// Cache writer: token i (of n) goes to slot slots[i] = block * 64 + position; slots outside
+// [0, num_blocks * 64) are skipped.  c / k rows of d_c / d_r values, c_stride / k_stride
+// elements apart, fp32 (in_f32) or bf16.
+struct AppendParams {
+  const void* c;
+  const void* k;
+  int in_f32;
+  int64_t c_stride, k_stride;
+  const int32_t* slots;
+  int64_t n;
+  uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+  int64_t off_lc, off_ls, off_rc, off_rs;
+  int d_c, d_r, g_lat, g_rope;
+  int fmt_lat, fmt_rope;    // MLA_FMT_*
+};
+
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
+hipError_t launch_append(const AppendParams& p, hipStream_t st);
 
 }  // namespace mla

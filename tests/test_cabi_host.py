@@ -140,3 +140,27 @@ def test_status_strings():
     L = mla.lib()
     for s in range(5):
         assert L.mla_status_string(s).startswith(b"MLA_")
+
+
+def test_append_validation():
+    """mla_append_kv rejects bad arguments before launching anything; n = 0 is a no-op."""
+    L = mla.lib()
+    d = mla.cache_desc(512, 64, "int2", "int4", 32, 64)
+    ok = (FAKE, 512, FAKE, 64, _lib.MLA_BF16, FAKE, 5, FAKE, 10, ctypes.byref(d), None)
+
+    def call(**kw):
+        names = ["c", "cs", "k", "ks", "dt", "slots", "n", "pool", "nb", "desc", "st"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return L.mla_append_kv(*[args[n] for n in names])
+
+    assert call(n=0) == _lib.MLA_OK                       # nothing to write: no launch
+    assert call(n=-1) == 1 and call(c=None) == 1 and call(slots=None) == 1 and call(pool=None) == 1
+    assert call(nb=0) == 1 and call(dt=7) == 1 and call(cs=511) == 1 and call(ks=63) == 1
+    assert call(c=FAKE + 1) == 1 and call(pool=FAKE + 8) == 1 and call(slots=FAKE + 2) == 1
+    bad = mla.cache_desc(512, 64, "int4", "int4", 60, 64)          # group does not divide d_c
+    assert call(desc=ctypes.byref(bad)) == 1
+    odd = mla.cache_desc(512, 64, "int4", "int4", 128, 64)         # 16 lanes per group: fine
+    assert call(desc=ctypes.byref(odd), n=0) == _lib.MLA_OK
+    odd = mla.cache_desc(480, 64, "int4", "int4", 96, 64)          # 12 lanes per group
+    assert call(desc=ctypes.byref(odd), cs=480) == _lib.MLA_ERR_UNSUPPORTED

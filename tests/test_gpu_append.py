@@ -1,0 +1,138 @@
+"""GPU parity of the cache writer mla_append_kv (marked gpu).
+
+The pool after the call must equal, byte for byte, the oracle's write_tokens applied to the
+same pool bytes, slots and inputs: the codes, (s, z) pairs and float rows are integer and
+byte results, so the bar is bit-exactness.  The pool starts as random bytes, so any byte the
+writer should not touch is checked too.  Inputs are the workloads' new-token rows with the
+edge rows of append_rows (constant, all-negative, fp16-subnormal scale, large, exact ties);
+slots are distinct with some to be skipped.  A last case appends whole sequences into an
+empty pool and decodes them with the library, against the oracle's attention over the
+dequantised quantiser output.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from mla_synth import CONFIGS, append_rows, append_slots, block_layout, to_bf16_exact  # noqa: E402
+from tests.gpu_helpers import desc_of, dev, norm_err  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+N_BLOCKS = 12
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_02_amd as m
+    m.lib()
+    return m
+
+
+def _fmt_args(cfg):
+    return (cfg.latent_fmt, cfg.rope_fmt, cfg.d_c, cfg.d_r, cfg.latent_group, cfg.rope_group)
+
+
+FORMATS = {
+    "f32": ("1", {}),
+    "bf16": ("2", {}),
+    "int4": ("4", {}),
+    "int2": ("5", {}),
+    "int4-g32": ("5", dict(latent_fmt="int4", latent_group=32, rope_group=32)),
+    "int2-g64": ("5", dict(latent_group=64)),
+}
+
+
+@pytest.mark.parametrize("n", [1, 37, 300])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_append_matches_oracle_bytes(mla, fmt, in_dtype, n):
+    name, over = FORMATS[fmt]
+    cfg = CONFIGS[name].with_(**over)
+    if cfg.latent_fmt == "f32" and in_dtype == "bf16":
+        pytest.skip("an fp32 cache is written from fp32 rows")
+    seed = 100 + n
+    print(f"[case] append {fmt} from {in_dtype}, n={n}", flush=True)
+    bb, _ = block_layout(cfg)
+    pool = np.random.default_rng(seed).integers(0, 256, (N_BLOCKS, bb), dtype=np.uint8)
+    c, k = append_rows(cfg, n, seed)
+    if in_dtype == "bf16":
+        c, k = to_bf16_exact(c), to_bf16_exact(k)
+    slots = append_slots(N_BLOCKS, n, seed + 1)
+    tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+    # rows of c are strided: a view into a wider buffer
+    cw = torch.zeros((n, cfg.d_c + 24), dtype=tdt)
+    cw[:, :cfg.d_c] = torch.from_numpy(c).to(tdt)
+    c_t = cw.to(dev())[:, :cfg.d_c]
+    k_t = torch.from_numpy(k).to(tdt).to(dev())
+    pool_t = torch.from_numpy(pool).to(dev())
+    mla.append_kv(c_t, k_t, pool_t, desc_of(cfg), torch.from_numpy(slots).to(dev()))
+    torch.cuda.synchronize()
+    got = pool_t.cpu().numpy()
+    ref = oracle.write_tokens(pool, slots, c.astype(np.float64), k.astype(np.float64), *_fmt_args(cfg))
+    diff = np.argwhere(got != ref)
+    assert len(diff) == 0, f"{len(diff)} bytes differ, first at (block, byte) {diff[:4].tolist()}"
+
+
+def test_append_nothing(mla):
+    cfg = CONFIGS["5"]
+    bb, _ = block_layout(cfg)
+    pool_t = torch.zeros((2, bb), dtype=torch.uint8, device=dev())
+    e = torch.zeros((0, 512), dtype=torch.bfloat16, device=dev())
+    r = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev())
+    mla.append_kv(e, r, pool_t, desc_of(cfg), torch.zeros(0, dtype=torch.int32, device=dev()))
+    torch.cuda.synchronize()
+    assert int(pool_t.sum()) == 0
+
+
+@pytest.mark.parametrize("name,H", [("5", 128), ("4", 16), ("2", 16)])
+def test_appended_sequences_decode(mla, name, H):
+    """Write whole sequences token by token through their block tables, then decode: the
+    result equals the oracle's attention over the dequantised quantiser output (bf16 cache:
+    over the bf16 rows), within the decode tolerance."""
+    cfg = CONFIGS[name].with_(H=H)
+    lens = np.array([300, 129, 64], dtype=np.int32)
+    B, T = len(lens), int(lens.sum())
+    print(f"[case] append then decode {cfg.name} H={H}", flush=True)
+    c, k = append_rows(cfg, T, 7)
+    c, k = to_bf16_exact(c), to_bf16_exact(k)
+    nblk = -(-lens // 64)
+    perm = np.random.default_rng(8).permutation(int(nblk.sum()) + 3).astype(np.int32)
+    table = np.zeros((B, int(nblk.max())), dtype=np.int32)
+    slots, cur = [], 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[cur:cur + nblk[b]]
+        cur += nblk[b]
+        slots += [int(table[b, t // 64]) * 64 + t % 64 for t in range(lens[b])]
+    bb, _ = block_layout(cfg)
+    pool_t = torch.zeros((len(perm), bb), dtype=torch.uint8, device=dev())
+    mla.append_kv(torch.from_numpy(c).to(torch.bfloat16).to(dev()), torch.from_numpy(k).to(torch.bfloat16).to(dev()),
+                  pool_t, desc_of(cfg), torch.tensor(slots, dtype=torch.int32, device=dev()))
+    rng = np.random.default_rng(9)
+    q_lat = to_bf16_exact(rng.standard_normal((B, 1, H, cfg.d_c), dtype=np.float32) * 0.05)
+    q_rope = to_bf16_exact(rng.standard_normal((B, 1, H, cfg.d_r), dtype=np.float32) * 0.05)
+    o, lse = mla.decode_paged(torch.from_numpy(q_lat).to(torch.bfloat16).to(dev()),
+                              torch.from_numpy(q_rope).to(torch.bfloat16).to(dev()), pool_t, desc_of(cfg),
+                              torch.from_numpy(table).to(dev()), torch.from_numpy(lens).to(dev()), int(lens.max()),
+                              cfg.sm_scale)
+    torch.cuda.synchronize()
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    cs, ks = [], []
+    for b in range(B):
+        cb = c[starts[b]:starts[b + 1]].astype(np.float64)
+        kb = k[starts[b]:starts[b + 1]].astype(np.float64)
+        if cfg.quantised:
+            cc, csz = oracle.quantise_rtn(cb, cfg.latent_group, 4 if cfg.latent_fmt == "int4" else 2)
+            rc, rsz = oracle.quantise_rtn(kb, cfg.rope_group, 4)
+            cd, kd = oracle.dequant_cache([cc], [csz], [rc], [rsz], cfg.latent_group, cfg.rope_group)
+            cb, kb = cd[0], kd[0]
+        cs.append(cb)
+        ks.append(kb)
+    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks, lens, 1,
+                                          cfg.sm_scale)
+    e = norm_err(o.float().cpu().numpy(), ref_o)
+    el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 2e-3 and el <= 2e-3
