@@ -30,6 +30,11 @@ What it computes, and where the pages fix it:
   the pages pair an INT4 or INT2 latent with an INT4 RoPE key and name
   round-to-nearest as the plain quantiser: QuantMLA abstract and podcast page).
 
+* A fixed orthogonal rotation of the latent (``hadamard``, ``rotate``,
+  ``fold_rotation``) folded into W_UK and W_UV leaves every full-precision result
+  unchanged and spreads outlier channels before quantisation (fixed rotations
+  adapted to MLA with the same quantiser: QuantMLA podcast page).
+
 Conventions (readings where the pages are silent): W_UK[h] is [d_n, d_c] with
 k_nope = W_UK[h] c; W_UV[h] is [d_c, d_v] with v = c W_UV[h]; query i of s_q
 attends cached tokens 0 .. L - s_q + i; lse is the natural log of the softmax
@@ -235,6 +240,35 @@ def write_tokens(pool: np.ndarray, slots: Sequence[int], c_new: np.ndarray, k_ne
     return out.reshape(shape)
 
 
+# --------------------------------------------------------------------------- fixed rotations
+
+def hadamard(d: int) -> np.ndarray:
+    """The normalised Walsh-Hadamard matrix H_d / sqrt(d) in Sylvester order (d a power of
+    two), built by doubling: H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]].  Orthogonal and
+    symmetric, so it is its own inverse: a data-free rotation that can be folded into the
+    weights around the cached latent (fixed rotations adapted to MLA with the same
+    quantiser: QuantMLA podcast page, comparison part)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(d)
+
+
+def rotate(x: np.ndarray, d_axis: int = -1) -> np.ndarray:
+    """x . H_d / sqrt(d) along d_axis (a library matrix product as the one step)."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float64), d_axis, -1)
+    return np.moveaxis(x @ hadamard(x.shape[-1]), -1, d_axis)
+
+
+def fold_rotation(w_uk: np.ndarray, w_uv: np.ndarray):
+    """Weights that absorb a latent rotation c -> c R, R = H / sqrt(d_c): W_UK[h] -> W_UK[h] R
+    (so that q_lat . c is unchanged) and W_UV[h] -> R^T W_UV[h] = R W_UV[h] (so that
+    o_lat W_UV is unchanged)."""
+    return rotate(w_uk, -1), rotate(w_uv, -2)
+
+
 # --------------------------------------------------------------------------- attention
 
 def _softmax_attend(s: np.ndarray, values: np.ndarray):
@@ -374,7 +408,8 @@ def exact_dequant_value(code: int, z: float, s: float) -> float:
     return float(sign * Fraction(lo, 128) * (Fraction(2) ** e))
 
 
-__all__ = ["bf16_round", "unpack_codes", "pack_codes_bytes", "write_tokens", "dequant", "quantise_rtn",
+__all__ = ["bf16_round", "unpack_codes", "pack_codes_bytes", "write_tokens", "hadamard", "rotate", "fold_rotation",
+           "dequant", "quantise_rtn",
            "token_bytes", "block_planes",
            "read_pool", "absorb_q", "out_proj", "attend_latent", "decode_unabsorbed", "decode_absorbed",
            "merge_partials", "dequant_cache", "exact_dequant_value"]
