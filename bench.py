@@ -229,6 +229,11 @@ def main():
     k_new = torch.randn((B * s_q, cfg.d_r), generator=gen, device=dev).to(qr.dtype)
     g_app = capture_calls(lambda i: mla.append_kv(c_new, k_new, pools[0], desc, slots), 8)
     append_ms = call_ms(g_app, 8, replays)
+    # (4) the fixed latent rotation folded into W_UK (an offline step), on a copy of W_UK
+    wuk_copy = wuk.clone()
+    g_rot = capture_calls(lambda i: mla.hadamard_rotate(wuk_copy, dim=2), 8)
+    rotate_ms = call_ms(g_rot, 8, replays)
+    rotate_gbs = 2 * wuk_copy.numel() * wuk_copy.element_size() / (rotate_ms * 1e-3) / 1e9
 
     bpt = mla.block_bytes(desc) // 64
     alg_bytes, cache_bytes, flops, units = algorithmic(x, bpt)
@@ -278,7 +283,8 @@ def main():
            "call_timing": "per-call HIP graphs of back-to-back calls, events on the launch stream",
            "decode_us": round(decode_ms * 1e3, 2), "absorb_us": round(absorb_ms * 1e3, 2),
            "out_proj_us": round(proj_ms * 1e3, 2), "append_us": round(append_ms * 1e3, 2),
-           "append_tokens": B * s_q, "hbm_tbps": round(gbs / 1e3, 3),
+           "append_tokens": B * s_q, "rotate_w_uk_us": round(rotate_ms * 1e3, 2),
+           "rotate_w_uk_gbs": round(rotate_gbs, 1), "hbm_tbps": round(gbs / 1e3, 3),
            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "cache_bytes": cache_bytes}
     log(f"timed {K} steps: {ms_per_step * 1e3:.2f} us/step, decode {decode_ms * 1e3:.2f} us")
     if not args.no_cpu_baseline:

@@ -209,6 +209,26 @@ int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_ne
                       const mla_cache_desc* desc, void* stream);
 
 /*
+ * mla_hadamard_rotate: in place, x <- x . H_d / sqrt(d) for a set of vectors, H_d the
+ *   Sylvester-ordered Walsh-Hadamard matrix (H_d[i][j] = (-1)^popcount(i & j)); the result
+ *   is orthogonal and its own inverse.  A fixed, data-free rotation folded into the weights
+ *   around the cached latent leaves every full-precision result unchanged and spreads large
+ *   channels over all of them before low-bit quantisation (the pages' baselines adapt fixed
+ *   rotations to MLA with the same quantiser: QuantMLA podcast page, comparison part; the
+ *   transforms are fused into the model offline: QuantMLA English abstract).  With R = H_d /
+ *   sqrt(d_c): latent rows c -> c R (before mla_append_kv), W_UK[h] rows -> W_UK[h] R, and
+ *   W_UV[h] columns -> R W_UV[h]; d = 2 on the RoPE key's pairs of both q_rope and k_rope is
+ *   the pairwise form.
+ *   Vector (o, i), o < n_outer, i < n_inner, starts at element o * outer_stride +
+ *   i * inner_stride of x and its element k sits k * elem_stride further on (all counted in
+ *   elements of dtype, MLA_F32 or MLA_BF16).  d is a power of two in [2, 4096].  Arithmetic
+ *   is fp32; bf16 vectors are rounded once (ties to even).  Vectors must not overlap.
+ *   n_outer = 0 is a no-op.
+ */
+int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stride, int64_t n_outer,
+                            int64_t outer_stride, int64_t n_inner, int64_t inner_stride, void* stream);
+
+/*
  * mla_dequant_blocks (test/debug): materialise blocks of a paged cache as bf16.
  *   out_bf16[k][t][0:d_c] = latent of token t of block block_ids[k], [d_c:d_c+d_r] = RoPE key,
  *   for k < n_blocks, t < 64.  Uses the same device unpack/dequant code as the decode

@@ -19,7 +19,8 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FMT_BF16, MLA_FMT_F32, MLA_FMT_INT2, M
                    CacheDesc, DecodeArgs, FMT_BY_NAME)
 
 __all__ = ["MlaError", "cache_desc", "block_bytes", "plane_offsets", "absorb_q", "decode_paged", "out_proj",
-           "dequant_blocks", "append_kv", "decode_workspace_size", "decode_plan", "DecodeStep", "lib"]
+           "dequant_blocks", "append_kv", "hadamard_rotate", "decode_workspace_size", "decode_plan", "DecodeStep",
+           "lib"]
 
 
 class MlaError(RuntimeError):
@@ -223,6 +224,44 @@ def append_kv(c_new: torch.Tensor, k_rope_new: torch.Tensor, pool: torch.Tensor,
                                    ctypes.c_void_p(slots.data_ptr()), n, ctypes.c_void_p(pool.data_ptr()),
                                    pool.shape[0], ctypes.byref(desc), _stream(pool.device))
     _check(st, "mla_append_kv")
+
+
+def hadamard_rotate(x: torch.Tensor, dim: int = -1) -> torch.Tensor:
+    """In place, x <- x . H_d / sqrt(d) along axis dim (d = x.shape[dim], a power of two):
+    the Walsh-Hadamard rotation, its own inverse.  x is bf16 or fp32; every other axis is
+    flattened into the vector index, so x must be a strided view whose other axes can be
+    traversed as (outer, inner) pairs: the axes before dim with one stride, those after it
+    with another (true of any contiguous tensor).  Returns x."""
+    _need_cuda(x)
+    dim = dim % x.dim()
+    d = x.shape[dim]
+    before, after = x.shape[:dim], x.shape[dim + 1:]
+    n_outer = 1
+    for v in before:
+        n_outer *= v
+    n_inner = 1
+    for v in after:
+        n_inner *= v
+    # the axes before dim must collapse to one stride, and so must those after it
+    def collapsed_stride(axes):
+        st = None
+        for a in range(len(axes) - 1, -1, -1):
+            if x.shape[axes[a]] == 1:
+                continue
+            s_a = x.stride(axes[a])
+            if st is None:
+                st, span = s_a, x.shape[axes[a]] * s_a
+            elif s_a != span:
+                raise ValueError("axes around dim do not collapse to one stride; make x contiguous")
+            else:
+                span = x.shape[axes[a]] * s_a
+        return 0 if st is None else st
+    outer_stride = collapsed_stride(list(range(dim)))
+    inner_stride = collapsed_stride(list(range(dim + 1, x.dim())))
+    st = _lib.load().mla_hadamard_rotate(ctypes.c_void_p(x.data_ptr()), _dt(x), d, x.stride(dim), n_outer,
+                                         outer_stride, max(n_inner, 1), inner_stride, _stream(x.device))
+    _check(st, "mla_hadamard_rotate")
+    return x
 
 
 @dataclass

@@ -46,6 +46,8 @@ _SIGS = {
                                      c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,
                                 c_int64, POINTER(CacheDesc), c_void_p]),
+    "mla_hadamard_rotate": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64,
+                                      c_void_p]),
 }
 
 _lib = None

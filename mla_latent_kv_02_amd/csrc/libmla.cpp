@@ -474,6 +474,32 @@ int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_ne
   return hip_status(mla::launch_append(p, (hipStream_t)stream));
 }
 
+int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stride, int64_t n_outer,
+                            int64_t outer_stride, int64_t n_inner, int64_t inner_stride, void* stream) {
+  if (!valid_dtype(dtype) || d < 2 || d > 4096 || (d & (d - 1)) != 0) return MLA_ERR_INVALID_ARG;
+  if (elem_stride < 1 || n_outer < 0 || n_inner < 1 || outer_stride < 0 || inner_stride < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (n_outer == 0) return MLA_OK;
+  if (x == nullptr || !aligned(x, dtype == MLA_F32 ? 4 : 2)) return MLA_ERR_INVALID_ARG;
+  if (n_outer > (1LL << 40) / n_inner) return MLA_ERR_UNSUPPORTED;
+  mla::RotateParams p{};
+  p.x = x;
+  p.f32 = dtype == MLA_F32;
+  p.d = d;
+  int l = 0;
+  while ((1 << l) < d) ++l;
+  p.log2d = l;
+  p.elem_stride = elem_stride;
+  p.n_inner = n_inner;
+  p.inner_stride = inner_stride;
+  p.outer_stride = outer_stride;
+  p.n_vec = n_outer * n_inner;
+  p.vecs_per_group = d >= 2048 ? 1 : 2048 / d;
+  if (ceil_div(p.n_vec, p.vecs_per_group) > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  p.scale = (float)(1.0 / std::sqrt((double)d));
+  return hip_status(mla::launch_rotate(p, (hipStream_t)stream));
+}
+
 int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
                            const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream) {
   Layout lay;

@@ -121,6 +121,20 @@ struct AppendParams {
   int fmt_lat, fmt_rope;    // MLA_FMT_*
 };
 
+// In-place rotation x <- x . H_d / sqrt(d) of n_vec = n_outer * n_inner vectors: vector
+// v = o * n_inner + i starts at x + o * outer_stride + i * inner_stride, element k at
+// + k * elem_stride (elements of the dtype).  vecs_per_group * d <= 4096.
+struct RotateParams {
+  void* x;
+  int f32;
+  int d, log2d;
+  int64_t elem_stride;
+  int64_t n_inner, inner_stride, outer_stride;
+  int64_t n_vec;
+  int vecs_per_group;
+  float scale;
+};
+
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
@@ -128,5 +142,6 @@ hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, hipStream_t st);
+hipError_t launch_rotate(const RotateParams& p, hipStream_t st);
 
 }  // namespace mla

@@ -164,3 +164,19 @@ def test_append_validation():
     assert call(desc=ctypes.byref(odd), n=0) == _lib.MLA_OK
     odd = mla.cache_desc(480, 64, "int4", "int4", 96, 64)          # 12 lanes per group
     assert call(desc=ctypes.byref(odd), cs=480) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_rotation_validation():
+    """mla_hadamard_rotate rejects bad arguments before launching anything."""
+    L = mla.lib()
+    ok = [FAKE, _lib.MLA_BF16, 512, 1, 10, 512, 1, 0, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.mla_hadamard_rotate(*a)
+
+    assert call(4, 0) == _lib.MLA_OK                        # no vectors: no launch
+    assert call(2, 3) == 1 and call(2, 1) == 1 and call(2, 8192) == 1 and call(1, 9) == 1
+    assert call(3, 0) == 1 and call(4, -1) == 1 and call(6, 0) == 1 and call(5, -2) == 1
+    assert call(0, None) == 1 and call(0, FAKE + 1) == 1
