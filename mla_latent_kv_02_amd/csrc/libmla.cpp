@@ -497,6 +497,7 @@ int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stri
   p.vecs_per_group = d >= 2048 ? 1 : 2048 / d;
   if (ceil_div(p.n_vec, p.vecs_per_group) > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
   p.scale = (float)(1.0 / std::sqrt((double)d));
+  p.vec8 = elem_stride == 1 && d >= 8 && aligned(x, 16) && outer_stride % 8 == 0 && inner_stride % 8 == 0;
   return hip_status(mla::launch_rotate(p, (hipStream_t)stream));
 }
 

@@ -133,6 +133,7 @@ struct RotateParams {
   int64_t n_vec;
   int vecs_per_group;
   float scale;
+  int vec8;                 // unit stride, 16-byte-aligned groups of 8: vector path
 };
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);

@@ -13,6 +13,9 @@
 // W_UV [H][d_c][d_v] (elem_stride d_v), latent rows of a token batch, or the pairs of the
 // RoPE key (d = 2).  A workgroup holds 2048 elements (or one vector of up to 4096) in LDS as
 // fp32 and runs the log2(d) butterfly stages there; bf16 vectors are rounded once at the end.
+// Unit-stride vectors with 16-byte-aligned groups of 8 (the host checks) move as 16-byte
+// accesses, 8 consecutive elements per lane, whose first three stages (pairs 1, 2 and 4
+// apart) stay in registers.
 #include <hip/hip_runtime.h>
 
 #include "mla_device.hpp"
@@ -35,7 +38,47 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(RotateParams p) {
     const int64_t o = v / p.n_inner, i = v % p.n_inner;
     return o * p.outer_stride + i * p.inner_stride + (int64_t)k * p.elem_stride;
   };
-  for (int e = tid; e < nel; e += kThreads) {
+  // pairs (j, j + h), h = 1, 2, 4, inside 8 registers
+  auto bfly8 = [](float r[8]) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((j & h) == 0) {
+          const float a = r[j], b = r[j + h];
+          r[j] = a + b;
+          r[j + h] = a - b;
+        }
+  };
+  const int s0 = p.vec8 ? 3 : 0;   // stages already done in registers
+  if (p.vec8) {
+    for (int e0 = 8 * tid; e0 < nel; e0 += 8 * kThreads) {
+      const int64_t v = v0 + e0 / d;
+      float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (v < p.n_vec) {
+        const int64_t a = addr(v, e0 % d);
+        if (p.f32) {
+          const f32x4 lo = *(const f32x4*)((const float*)p.x + a), hi = *(const f32x4*)((const float*)p.x + a + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[j] = lo[j];
+            r[4 + j] = hi[j];
+          }
+        } else {
+          const u32x4 w = *(const u32x4*)((const uint16_t*)p.x + a);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[2 * j] = __uint_as_float(w[j] << 16);
+            r[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+          }
+        }
+      }
+      bfly8(r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) buf[e0 + j] = r[j];
+    }
+  }
+  for (int e = tid; e < nel && !p.vec8; e += kThreads) {
     const int64_t v = v0 + e / d;
     float x = 0.f;
     if (v < p.n_vec) {
@@ -46,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(RotateParams p) {
   }
   __syncthreads();
   // stage h: pairs (j, j + h) with j & h == 0 inside each vector
-  for (int s = 0; s < log2d; ++s) {
+  for (int s = s0; s < log2d; ++s) {
     const int h = 1 << s;
     for (int q = tid; q < nel / 2; q += kThreads) {
       const int j = ((q >> s) << (s + 1)) | (q & (h - 1));
@@ -57,6 +100,24 @@ __global__ __launch_bounds__(kThreads) void hadamard_kernel(RotateParams p) {
     __syncthreads();
   }
   const float scale = p.scale;
+  if (p.vec8) {
+    for (int e0 = 8 * tid; e0 < nel; e0 += 8 * kThreads) {
+      const int64_t v = v0 + e0 / d;
+      if (v >= p.n_vec) continue;
+      const int64_t a = addr(v, e0 % d);
+      float r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = buf[e0 + j] * scale;
+      if (p.f32) {
+        *(f32x4*)((float*)p.x + a) = f32x4{r[0], r[1], r[2], r[3]};
+        *(f32x4*)((float*)p.x + a + 4) = f32x4{r[4], r[5], r[6], r[7]};
+      } else {
+        *(u32x4*)((uint16_t*)p.x + a) = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
+                                              pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
+      }
+    }
+    return;
+  }
   for (int e = tid; e < nel; e += kThreads) {
     const int64_t v = v0 + e / d;
     if (v >= p.n_vec) continue;
