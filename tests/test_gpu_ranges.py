@@ -171,3 +171,61 @@ def test_range_start_charge(mla):
                                           [c[b] for b in keep], [k[b] for b in keep], x.seq_lens[keep],
                                           x.cfg.s_q, x.cfg.sm_scale)
     _check(o[keep], lse[keep], ref_o, ref_lse)
+
+
+def test_range_max_batch(mla):
+    """The row-owner path at its largest batch, 8192 sequences (its sequence table is three LDS
+    arrays of 8193 entries), 96 heads, lengths 0..64 (one block each, some empty).  Seeded
+    bf16 rows, queries and a shuffled block table; a sample of sequences (the empty ones,
+    the longest, random others) against the oracle, which sees only those."""
+    B, H, d_c, d_r = 8192, 96, 512, 64
+    rng = np.random.default_rng(91)
+    lens = rng.integers(0, 65, size=B).astype(np.int32)
+    lens[[5, 4000]] = 0
+    lens[[17, 8191]] = 64
+    perm = rng.permutation(B + 3).astype(np.int32)
+    table = perm[:B].reshape(B, 1).copy()
+    _say("max batch", B, H)
+    rows = rng.standard_normal((B + 3, 64, d_c + d_r), dtype=np.float32)
+    rows_b = (rows.view(np.uint32) + 0x7FFF + ((rows.view(np.uint32) >> 16) & 1)) >> 16   # bf16 bits, RNE
+    pool = rows_b.astype(np.uint16).view(np.uint8).reshape(B + 3, -1)
+    del rows
+    q = rng.standard_normal((B, 1, H, d_c + d_r), dtype=np.float32) * 0.05
+    qb = ((q.view(np.uint32) + 0x7FFF + ((q.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    del q
+    q_t = torch.from_numpy(qb.view(np.int16)).to(dev()).view(torch.bfloat16)
+    cfg = CONFIGS["3"].with_(H=H)
+    o, lse = mla.decode_paged(q_t[..., :d_c].contiguous(), q_t[..., d_c:].contiguous(), torch.from_numpy(pool).to(dev()),
+                              desc_of(cfg), torch.from_numpy(table).to(dev()), torch.from_numpy(lens).to(dev()), 64,
+                              cfg.sm_scale)
+    torch.cuda.synchronize()
+    sel = sorted({5, 4000, 17, 8191, 0, 1} | {int(v) for v in rng.integers(0, B, 10)})
+    o = o[sel].float().cpu().numpy()
+    lse = lse[sel].cpu().numpy()
+    bf = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)   # noqa: E731
+    live = [i for i, b in enumerate(sel) if lens[b] > 0]
+    for i, b in enumerate(sel):
+        if lens[b] == 0:
+            assert np.all(o[i] == 0.0) and np.all(lse[i] == -np.inf)
+    c = [bf(rows_b[table[sel[i], 0], :lens[sel[i]], :d_c]) for i in live]
+    k = [bf(rows_b[table[sel[i], 0], :lens[sel[i]], d_c:]) for i in live]
+    qs = bf(qb[[sel[i] for i in live]])
+    ref_o, ref_lse = oracle.attend_latent(qs[..., :d_c], qs[..., d_c:], c, k, lens[[sel[i] for i in live]], 1,
+                                          cfg.sm_scale)
+    _check(o[live], lse[live], ref_o, ref_lse)
+
+
+@pytest.mark.parametrize("H", [128, 16])
+def test_all_sequences_empty(mla, H):
+    """Every sequence of length 0 (both decode paths): o_lat = 0 and lse = -inf everywhere."""
+    cfg = CONFIGS["3"].with_(H=H)
+    B = 5
+    _say("all empty", H)
+    q = torch.randn((B, 1, H, 512), device=dev()).to(torch.bfloat16)
+    r = torch.randn((B, 1, H, 64), device=dev()).to(torch.bfloat16)
+    pool = torch.zeros((2, mla.block_bytes(desc_of(cfg))), dtype=torch.uint8, device=dev())
+    table = torch.zeros((B, 1), dtype=torch.int32, device=dev())
+    lens = torch.zeros(B, dtype=torch.int32, device=dev())
+    o, lse = mla.decode_paged(q, r, pool, desc_of(cfg), table, lens, 1, cfg.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isinf(lse) & (lse < 0))
