@@ -187,6 +187,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = max(e0.elapsed_time(e1) / K, 1e-9)
+    # per-step spread: the same K steps again, each between its own pair of events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record(st)
+        graphs[i % rotate].replay() if graphs else step.run(qn, qr, pools[i % rotate], bt, sl)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    p10, p50, p90 = (float(v) for v in np.percentile(per_step, [10, 50, 90]))
     # (2) per-call durations: each library call is captured REPS times back to back in a HIP
     # graph (the decode cycling over the rotated pools) and the graph is replayed between two
     # events on this stream, so the figure is GPU time per call without host launch gaps
@@ -279,6 +288,7 @@ def main():
                       "tiles_per_split": tpc, "pool_copies_rotated": rotate},
            "roofline": roof,
            "us_per_step": round(ms_per_step * 1e3, 2), "wall_us_per_step": round(wall / K * 1e6, 2),
+           "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
            "step_launch": "eager" if args.no_graph else "hip_graph",
            "call_timing": "per-call HIP graphs of back-to-back calls, events on the launch stream",
            "decode_us": round(decode_ms * 1e3, 2), "absorb_us": round(absorb_ms * 1e3, 2),
