@@ -238,7 +238,24 @@ def main():
     k_new = torch.randn((B * s_q, cfg.d_r), generator=gen, device=dev).to(qr.dtype)
     g_app = capture_calls(lambda i: mla.append_kv(c_new, k_new, pools[0], desc, slots), 8)
     append_ms = call_ms(g_app, 8, replays)
-    # (4) the fixed latent rotation folded into W_UK (an offline step), on a copy of W_UK
+    # (4) quantised caches: the same decode with the history split by precision, a bf16 sink
+    # of 64 tokens and a bf16 recent window of 512 around the workload's low-bit cache
+    mixed_ms = None
+    if cfg.quantised:
+        hi_desc = mla.cache_desc(cfg.d_c, cfg.d_r, "bf16")
+        S, W = 64, 512
+        hi_pool = torch.zeros((B * (1 + W // 64), mla.block_bytes(hi_desc)), dtype=torch.uint8, device=dev)
+        hi_pool.view(torch.bfloat16).normal_(generator=gen)
+        sink_bt = torch.arange(B, dtype=torch.int32, device=dev).view(B, 1)
+        rec_bt = (B + torch.arange(B * (W // 64), dtype=torch.int32, device=dev)).view(B, W // 64)
+        sink_l = torch.full((B,), S, dtype=torch.int32, device=dev)
+        rec_l = torch.full((B,), W, dtype=torch.int32, device=dev)
+        mid_l = (sl - S - W).clamp(min=0)
+        g_mix = capture_calls(lambda i: mla.decode_mixed(
+            ql, qr, (hi_pool, hi_desc, sink_bt, sink_l, S), (pools[i % rotate], desc, bt, mid_l, max_len),
+            (hi_pool, hi_desc, rec_bt, rec_l, W), cfg.sm_scale), reps_dec)
+        mixed_ms = call_ms(g_mix, reps_dec, replays)
+    # (5) the fixed latent rotation folded into W_UK (an offline step), on a copy of W_UK
     wuk_copy = wuk.clone()
     g_rot = capture_calls(lambda i: mla.hadamard_rotate(wuk_copy, dim=2), 8)
     rotate_ms = call_ms(g_rot, 8, replays)
@@ -294,7 +311,9 @@ def main():
            "decode_us": round(decode_ms * 1e3, 2), "absorb_us": round(absorb_ms * 1e3, 2),
            "out_proj_us": round(proj_ms * 1e3, 2), "append_us": round(append_ms * 1e3, 2),
            "append_tokens": B * s_q, "rotate_w_uk_us": round(rotate_ms * 1e3, 2),
-           "rotate_w_uk_gbs": round(rotate_gbs, 1), "hbm_tbps": round(gbs / 1e3, 3),
+           "rotate_w_uk_gbs": round(rotate_gbs, 1),
+           "mixed_decode_us": round(mixed_ms * 1e3, 2) if mixed_ms is not None else None,
+           "hbm_tbps": round(gbs / 1e3, 3),
            "mfma_util": round(tflops / BF16_PEAK_TFLOPS, 4), "cache_bytes": cache_bytes}
     log(f"timed {K} steps: {ms_per_step * 1e3:.2f} us/step, decode {decode_ms * 1e3:.2f} us")
     if not args.no_cpu_baseline:

@@ -174,6 +174,30 @@ int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* n
 int32_t mla_decode_paged(const mla_decode_args* args, void* stream);
 
 /*
+ * mla_decode_mixed: one decode over a history kept at two precisions, the deployed policy of
+ *   the QuantMLA cache layout (earliest tokens and a recent window kept in BF16, the tokens
+ *   between them low-bit: QuantMLA podcast page, cache-layout part).  Sequence b's history is
+ *   sink_b ++ middle_b ++ recent_b; each part is a paged cache of its own, described by an
+ *   mla_decode_args whose cache, pool, block table, seq_lens (that part's token counts) and
+ *   max_seq_len are used; q_lat, q_rope, q_dtype, batch, s_q, num_heads, sm_scale and the
+ *   cache widths must be the same in every part (else MLA_ERR_INVALID_ARG), and num_splits
+ *   applies per part; o_lat, o_dtype, lse and workspace of the parts are ignored.  Any part
+ *   may be NULL (absent); at least one must be given.  The recent part ends with the s_q new
+ *   tokens and carries the causal mask (query i sees its tokens 0 .. L - s_q + i); every query
+ *   sees all sink and middle tokens.  Each part is decoded into fp32 partials and the parts
+ *   are merged by log-sum-exp (exactly the attention over the concatenated history, up to
+ *   rounding): o_lat [batch][s_q][H][d_c] of o_dtype, lse [batch][s_q][H] or NULL.  A part
+ *   with no token for a sequence contributes nothing; a sequence with no token at all gets
+ *   o_lat = 0 and lse = -inf.  workspace: >= mla_decode_mixed_workspace_size() bytes,
+ *   256-byte aligned, scratch.
+ */
+int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* middle, const mla_decode_args* recent,
+                         void* o_lat, int32_t o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int32_t mla_decode_mixed_workspace_size(const mla_decode_args* sink, const mla_decode_args* middle,
+                                        const mla_decode_args* recent, size_t* bytes);
+
+/*
  * mla_out_proj: up-project the latent attention output (W_UV, RAQ-MLA abstract).
  *   out[n][h][:] = sum_j o_lat[n, h, j] * W_UV[h][j][:]      (fp32 accumulation)
  *   o_lat element (n, h, j) at o_lat[n*o_stride_n + h*o_stride_h + j]; w_uv [H][d_c][d_v];

@@ -19,8 +19,8 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FMT_BF16, MLA_FMT_F32, MLA_FMT_INT2, M
                    CacheDesc, DecodeArgs, FMT_BY_NAME)
 
 __all__ = ["MlaError", "cache_desc", "block_bytes", "plane_offsets", "absorb_q", "decode_paged", "out_proj",
-           "dequant_blocks", "append_kv", "hadamard_rotate", "decode_workspace_size", "decode_plan", "DecodeStep",
-           "lib"]
+           "decode_mixed", "dequant_blocks", "append_kv", "hadamard_rotate", "decode_workspace_size",
+           "decode_plan", "DecodeStep", "lib"]
 
 
 class MlaError(RuntimeError):
@@ -185,6 +185,33 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, 
     a = _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
                      out, lse, workspace, total_seq_len)
     _check(_lib.load().mla_decode_paged(ctypes.byref(a), _stream(q_lat.device)), "mla_decode_paged")
+    return out, lse
+
+
+def decode_mixed(q_lat: torch.Tensor, q_rope: torch.Tensor, sink, middle, recent, sm_scale: float,
+                 o_dtype=torch.float32, num_splits: int = 0):
+    """One decode over a history kept in up to three caches: sink ++ middle ++ recent per
+    sequence (e.g. bf16 sink and recent window, low-bit middle).  Each part is None or
+    (pool, desc, block_table, seq_lens, max_seq_len) for that part's tokens; the recent part
+    ends with the s_q new tokens and carries the causal mask.  Returns (o_lat, lse)."""
+    parts = []
+    for part in (sink, middle, recent):
+        if part is None:
+            parts.append(None)
+            continue
+        pool, desc, bt, sl, mx = part
+        _check_decode_tensors(q_lat, q_rope, pool, desc, bt, sl)
+        parts.append(_decode_args(q_lat, q_rope, pool, desc, bt, sl, mx, sm_scale, num_splits, None, None, None))
+    refs = [ctypes.byref(a) if a is not None else None for a in parts]
+    L = _lib.load()
+    n = ctypes.c_size_t()
+    _check(L.mla_decode_mixed_workspace_size(*refs, ctypes.byref(n)), "mla_decode_mixed_workspace_size")
+    B, s_q, H, d_c = q_lat.shape
+    out = torch.empty((B, s_q, H, d_c), dtype=o_dtype, device=q_lat.device)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q_lat.device)
+    _check(L.mla_decode_mixed(*refs, ctypes.c_void_p(out.data_ptr()), _dt(out), ctypes.c_void_p(lse.data_ptr()),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q_lat.device)), "mla_decode_mixed")
     return out, lse
 
 

@@ -42,6 +42,10 @@ _SIGS = {
     "mla_decode_workspace_size": (c_int32, [POINTER(DecodeArgs), POINTER(c_size_t)]),
     "mla_decode_plan": (c_int32, [POINTER(DecodeArgs), c_int32, POINTER(c_int32), POINTER(c_int32)]),
     "mla_decode_paged": (c_int32, [POINTER(DecodeArgs), c_void_p]),
+    "mla_decode_mixed": (c_int32, [POINTER(DecodeArgs), POINTER(DecodeArgs), POINTER(DecodeArgs), c_void_p, c_int32,
+                                   c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mla_decode_mixed_workspace_size": (c_int32, [POINTER(DecodeArgs), POINTER(DecodeArgs), POINTER(DecodeArgs),
+                                                  POINTER(c_size_t)]),
     "mla_dequant_blocks": (c_int32, [c_void_p, c_int64, POINTER(CacheDesc), c_void_p, c_int32, c_void_p,
                                      c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,

@@ -226,6 +226,70 @@ int32_t run_proj(const void* x, int64_t sn, int64_t sh, int32_t xdt, const void*
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------
+// Mixed-precision history: parts[0] = sink (earliest tokens), parts[1] = middle (low-bit),
+// parts[2] = recent window (ends with the s_q new tokens); any may be null.  Workspace:
+// partial o [3][B][R][d_c] fp32, partial lse [3][B][R], then the parts' own decode workspace
+// (used by one part after the other on the stream).
+namespace {
+
+struct MixedLayout {
+  size_t o_bytes = 0, lse_off = 0, dec_off = 0, total = 0;
+};
+
+// The args a part is decoded with: its own cache and block table, the shared queries; sink
+// and middle precede every query, so with s_q = 2 the two queries are decoded as 2H heads.
+mla_decode_args part_args(const mla_decode_args* a, bool causal) {
+  mla_decode_args p = *a;
+  if (!causal && p.s_q == 2) {
+    p.s_q = 1;
+    p.num_heads *= 2;
+  }
+  p.o_dtype = MLA_F32;
+  return p;
+}
+
+int32_t mixed_layout(const mla_decode_args* const parts[3], MixedLayout* m) {
+  const mla_decode_args* ref = nullptr;
+  for (int i = 0; i < 3; ++i)
+    if (parts[i] != nullptr) {
+      ref = parts[i];
+      break;
+    }
+  if (ref == nullptr) return MLA_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i) {
+    const mla_decode_args* a = parts[i];
+    if (a == nullptr) continue;
+    if (a->batch != ref->batch || a->s_q != ref->s_q || a->num_heads != ref->num_heads || a->q_lat != ref->q_lat ||
+        a->q_rope != ref->q_rope || a->q_dtype != ref->q_dtype || a->sm_scale != ref->sm_scale ||
+        a->cache.d_c != ref->cache.d_c || a->cache.d_r != ref->cache.d_r)
+      return MLA_ERR_INVALID_ARG;
+  }
+  const int64_t rows = (int64_t)ref->batch * ref->s_q * ref->num_heads;
+  m->o_bytes = (size_t)align_up(3 * rows * ref->cache.d_c * 4, 256);
+  m->lse_off = m->o_bytes;
+  m->dec_off = m->lse_off + (size_t)align_up(3 * rows * 4, 256);
+  size_t dec = 0;
+  int cus = 0;
+  int32_t s = device_cus(&cus);
+  if (s != MLA_OK) return s;
+  for (int i = 0; i < 3; ++i) {
+    if (parts[i] == nullptr) continue;
+    mla_decode_args p = part_args(parts[i], i == 2);
+    p.o_lat = (void*)(uintptr_t)256;   // placeholders for validation only
+    p.lse = nullptr;
+    Layout lay;
+    s = validate_decode(&p, &lay);
+    if (s != MLA_OK) return s;
+    size_t lse_off = 0;
+    dec = std::max(dec, partial_bytes(&p, make_plan(&p, cus), &lse_off));
+  }
+  m->total = m->dec_off + (size_t)align_up((int64_t)dec, 256);
+  return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -427,6 +491,61 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     if (e != hipSuccess) return MLA_ERR_HIP;
   }
   return MLA_OK;
+}
+
+int32_t mla_decode_mixed_workspace_size(const mla_decode_args* sink, const mla_decode_args* middle,
+                                        const mla_decode_args* recent, size_t* bytes) {
+  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+  const mla_decode_args* parts[3] = {sink, middle, recent};
+  MixedLayout m;
+  const int32_t s = mixed_layout(parts, &m);
+  if (s != MLA_OK) return s;
+  *bytes = m.total;
+  return MLA_OK;
+}
+
+int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* middle, const mla_decode_args* recent,
+                         void* o_lat, int32_t o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const mla_decode_args* parts[3] = {sink, middle, recent};
+  MixedLayout m;
+  int32_t s = mixed_layout(parts, &m);
+  if (s != MLA_OK) return s;
+  if (o_lat == nullptr || !valid_dtype(o_dtype) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)))
+    return MLA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < m.total || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
+  const mla_decode_args* ref = sink ? sink : (middle ? middle : recent);
+  const int B = ref->batch, R = ref->s_q * ref->num_heads, d_c = ref->cache.d_c;
+  const size_t rows = (size_t)B * R;
+  float* part_o = (float*)workspace;
+  float* part_lse = (float*)((char*)workspace + m.lse_off);
+  int n = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (parts[i] == nullptr) continue;
+    mla_decode_args p = part_args(parts[i], i == 2);
+    p.o_lat = part_o + (size_t)n * rows * d_c;
+    p.lse = part_lse + (size_t)n * rows;
+    p.workspace = (char*)workspace + m.dec_off;
+    p.workspace_bytes = workspace_bytes - m.dec_off;
+    s = mla_decode_paged(&p, stream);
+    if (s != MLA_OK) return s;
+    ++n;
+  }
+  // LSE merge of the parts (a part with no token gives o = 0, lse = -inf and weight 0)
+  mla::CombineParams c{};
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.seq_lens = ref->seq_lens;
+  c.max_seq_len = ref->max_seq_len;
+  c.R = R;
+  c.d_c = d_c;
+  c.max_chunks = n;
+  c.chunk_major = 1;
+  c.B = B;
+  c.out = o_lat;
+  c.out_bf16 = o_dtype == MLA_BF16;
+  c.out_lse = lse;
+  return hip_status(mla::launch_combine(c, B, (hipStream_t)stream));
 }
 
 int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,

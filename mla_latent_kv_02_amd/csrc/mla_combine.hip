@@ -111,14 +111,20 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   const int b = blockIdx.x / R, r = blockIdx.x % R;
   const float NEG_INF = -__builtin_inff();
   int nch;
-  size_t u0;
-  if (p.meta == nullptr) {
+  size_t base, step = (size_t)R;   // partial c of this (b, row) is row base + c * step
+  if (p.chunk_major) {
+    // parts of one decode over several caches: every (b, row) has max_chunks partials,
+    // partial c at row (c * B + b) * R + r
+    nch = p.max_chunks;
+    base = (size_t)b * R + r;
+    step = (size_t)p.B * R;
+  } else if (p.meta == nullptr) {
     int L = p.seq_lens[b];
     L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
     const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
     nch = (nblk + p.tpc - 1) / p.tpc;
     nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
-    u0 = (size_t)b * p.max_chunks;
+    base = (size_t)b * p.max_chunks * R + r;
   } else {
     // sequence b's blocks are the last n_b positions of its part of the block space
     int L = p.seq_lens[b];
@@ -128,10 +134,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     const int per = p.meta[0], last = p.meta[2 + b] - 1;
     const int i0 = (last - nblk + 1) / per, i1 = last / per;
     nch = i1 - i0 + 1;
-    u0 = (size_t)b + i0;
+    base = ((size_t)b + i0) * R + r;
   }
   const int d_c = p.d_c;
-  const size_t stride = (size_t)R * d_c;          // between consecutive partials
+  const size_t stride = step * d_c;               // between consecutive partials
   const bool vec4 = (d_c & 3) == 0;               // 16-byte column groups (else element by element)
   float lse_out = NEG_INF;
   for (int d = tid * 4; d < d_c; d += 512) {
@@ -139,14 +145,14 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nch; c0 += CB) {
       const int n = min(CB, nch - c0);
-      const size_t ub = (u0 + c0) * R + r;
+      const size_t ub = base + (size_t)c0 * step;
       float lc[CB], iv[CB];
       f32x4 v[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const bool ok = j < n;
-        lc[j] = ok ? p.part_lse[ub + (size_t)j * R] : NEG_INF;
-        iv[j] = ok && p.part_inv != nullptr ? p.part_inv[ub + (size_t)j * R] : 1.f;
+        lc[j] = ok ? p.part_lse[ub + (size_t)j * step] : NEG_INF;
+        iv[j] = ok && p.part_inv != nullptr ? p.part_inv[ub + (size_t)j * step] : 1.f;
         v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (ok) {
           const float* src = p.part_o + ub * d_c + d + j * stride;

@@ -63,7 +63,8 @@ struct RowsParams {
                             // (its blocks are the last n_b positions before that of b + 1)
 };
 
-// Combine of split partials.  Partition mode (meta == null): max_chunks partitions of tpc
+// Combine of split partials.  Chunk-major mode: the parts of a decode over several caches.
+// Partition mode (meta == null): max_chunks partitions of tpc
 // blocks per sequence, slot b * max_chunks + c, o normalised.  Range mode: pieces of the
 // ranges in meta, slots b + i, o unnormalised with its factor in part_inv; every non-empty
 // sequence is combined (one piece included).
@@ -79,6 +80,8 @@ struct CombineParams {
   int out_bf16;
   float* out_lse;
   int many_parts;           // rows usually hold more than 16 partials: wider load batches
+  int chunk_major;          // max_chunks normalised partials per (b, row) at rows (c * B + b) * R + r
+  int B;                    // batch (chunk-major mode)
 };
 
 struct ProjParams {

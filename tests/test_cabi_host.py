@@ -180,3 +180,17 @@ def test_rotation_validation():
     assert call(2, 3) == 1 and call(2, 1) == 1 and call(2, 8192) == 1 and call(1, 9) == 1
     assert call(3, 0) == 1 and call(4, -1) == 1 and call(6, 0) == 1 and call(5, -2) == 1
     assert call(0, None) == 1 and call(0, FAKE + 1) == 1
+
+
+def test_mixed_validation():
+    """mla_decode_mixed needs at least one part and the same queries and shapes in every part;
+    these checks come before anything touches a device."""
+    L = mla.lib()
+    a, b = _args(), _args(num_heads=32)
+    n = ctypes.c_size_t()
+    assert L.mla_decode_mixed_workspace_size(None, None, None, ctypes.byref(n)) == 1
+    assert L.mla_decode_mixed(None, None, None, FAKE, 0, None, FAKE, 1 << 30, None) == 1
+    assert L.mla_decode_mixed(ctypes.byref(a), None, ctypes.byref(b), FAKE, 0, None, FAKE, 1 << 30, None) == 1
+    c = _args(q_lat=FAKE + 4096)
+    assert L.mla_decode_mixed(ctypes.byref(a), ctypes.byref(c), None, FAKE, 0, None, FAKE, 1 << 30, None) == 1
+    assert L.mla_decode_mixed_workspace_size(ctypes.byref(a), None, None, None) == 1
