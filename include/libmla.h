@@ -184,7 +184,9 @@ int32_t mla_decode_paged(const mla_decode_args* args, void* stream);
  *   applies per part; o_lat, o_dtype, lse and workspace of the parts are ignored.  Any part
  *   may be NULL (absent); at least one must be given.  The recent part ends with the s_q new
  *   tokens and carries the causal mask (query i sees its tokens 0 .. L - s_q + i); every query
- *   sees all sink and middle tokens.  Each part is decoded into fp32 partials and the parts
+ *   sees all sink and middle tokens (the sink and the recent window may also share one
+ *   cache, passed as the recent part with no sink part: the attention does not depend on
+ *   token order apart from that mask).  Each part is decoded into fp32 partials and the parts
  *   are merged by log-sum-exp (exactly the attention over the concatenated history, up to
  *   rounding): o_lat [batch][s_q][H][d_c] of o_dtype, lse [batch][s_q][H] or NULL.  A part
  *   with no token for a sequence contributes nothing; a sequence with no token at all gets
