@@ -112,3 +112,45 @@ def test_mixed_history_matches_oracle(mla, H, s_q, low):
     torch.cuda.synchronize()
     assert norm_err(o2.cpu().numpy(), ref2_o) <= 2e-3
     assert float(np.max(np.abs(lse2.cpu().numpy() - ref2_lse))) <= 2e-3
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_sink_and_window_in_one_cache(mla, H):
+    """The sink and the recent window stored as one bf16 cache (sink ++ window, ending with the
+    new tokens) and passed as the recent part, with no sink part: the result equals the
+    attention over sink ++ middle ++ window, since only the causal mask depends on order."""
+    s_q = 2
+    lo_cfg = CONFIGS["5"].with_(H=H)
+    hi_cfg = CONFIGS["2"].with_(H=H)
+    sink, middle, recent = [64, 3], [700, 90], [130, 66]
+    B = 2
+    print(f"[case] sink and window in one cache H={H}", flush=True)
+    rng = np.random.default_rng(300 + H)
+    T = [sink[b] + middle[b] + recent[b] for b in range(B)]
+    rows = [append_rows(lo_cfg, t + 6, 400 + b) for b, t in enumerate(T)]
+    c_all = [to_bf16_exact(r[0][6:]) for r in rows]
+    k_all = [to_bf16_exact(r[1][6:]) for r in rows]
+    hi_c = [np.concatenate([c_all[b][:sink[b]], c_all[b][sink[b] + middle[b]:]]) for b in range(B)]
+    hi_k = [np.concatenate([k_all[b][:sink[b]], k_all[b][sink[b] + middle[b]:]]) for b in range(B)]
+    p_hi = _part(mla, hi_cfg, hi_c, hi_k, rng)
+    p_mid = _part(mla, lo_cfg, [c_all[b][sink[b]:sink[b] + middle[b]] for b in range(B)],
+                  [k_all[b][sink[b]:sink[b] + middle[b]] for b in range(B)], rng)
+    q_lat = to_bf16_exact(rng.standard_normal((B, s_q, H, 512)).astype(np.float32) * 0.1)
+    q_rope = to_bf16_exact(rng.standard_normal((B, s_q, H, 64)).astype(np.float32) * 0.1)
+    o, lse = mla.decode_mixed(torch.from_numpy(q_lat).to(torch.bfloat16).to(dev()),
+                              torch.from_numpy(q_rope).to(torch.bfloat16).to(dev()), None, p_mid, p_hi,
+                              lo_cfg.sm_scale)
+    torch.cuda.synchronize()
+    cs, ks = [], []
+    for b in range(B):
+        mc, mk = _logical(lo_cfg, c_all[b][sink[b]:sink[b] + middle[b]], k_all[b][sink[b]:sink[b] + middle[b]])
+        cs.append(np.concatenate([c_all[b][:sink[b]].astype(np.float64), mc,
+                                  c_all[b][sink[b] + middle[b]:].astype(np.float64)]))
+        ks.append(np.concatenate([k_all[b][:sink[b]].astype(np.float64), mk,
+                                  k_all[b][sink[b] + middle[b]:].astype(np.float64)]))
+    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks,
+                                          np.array(T), s_q, lo_cfg.sm_scale)
+    e = norm_err(o.cpu().numpy(), ref_o)
+    el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 2e-3 and el <= 2e-3
