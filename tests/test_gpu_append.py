@@ -87,15 +87,15 @@ def test_append_nothing(mla):
     assert int(pool_t.sum()) == 0
 
 
-@pytest.mark.parametrize("name,H", [("5", 128), ("4", 16), ("2", 16)])
-def test_appended_sequences_decode(mla, name, H):
+@pytest.mark.parametrize("name,H,s_q", [("5", 128, 1), ("4", 16, 1), ("2", 16, 1), ("5", 128, 2), ("4", 16, 2)])
+def test_appended_sequences_decode(mla, name, H, s_q):
     """Write whole sequences token by token through their block tables, then decode: the
     result equals the oracle's attention over the dequantised quantiser output (bf16 cache:
     over the bf16 rows), within the decode tolerance."""
     cfg = CONFIGS[name].with_(H=H)
     lens = np.array([300, 129, 64], dtype=np.int32)
     B, T = len(lens), int(lens.sum())
-    print(f"[case] append then decode {cfg.name} H={H}", flush=True)
+    print(f"[case] append then decode {cfg.name} H={H} s_q={s_q}", flush=True)
     c, k = append_rows(cfg, T, 7)
     c, k = to_bf16_exact(c), to_bf16_exact(k)
     nblk = -(-lens // 64)
@@ -111,8 +111,8 @@ def test_appended_sequences_decode(mla, name, H):
     mla.append_kv(torch.from_numpy(c).to(torch.bfloat16).to(dev()), torch.from_numpy(k).to(torch.bfloat16).to(dev()),
                   pool_t, desc_of(cfg), torch.tensor(slots, dtype=torch.int32, device=dev()))
     rng = np.random.default_rng(9)
-    q_lat = to_bf16_exact(rng.standard_normal((B, 1, H, cfg.d_c), dtype=np.float32) * 0.05)
-    q_rope = to_bf16_exact(rng.standard_normal((B, 1, H, cfg.d_r), dtype=np.float32) * 0.05)
+    q_lat = to_bf16_exact(rng.standard_normal((B, s_q, H, cfg.d_c), dtype=np.float32) * 0.05)
+    q_rope = to_bf16_exact(rng.standard_normal((B, s_q, H, cfg.d_r), dtype=np.float32) * 0.05)
     o, lse = mla.decode_paged(torch.from_numpy(q_lat).to(torch.bfloat16).to(dev()),
                               torch.from_numpy(q_rope).to(torch.bfloat16).to(dev()), pool_t, desc_of(cfg),
                               torch.from_numpy(table).to(dev()), torch.from_numpy(lens).to(dev()), int(lens.max()),
@@ -130,7 +130,7 @@ def test_appended_sequences_decode(mla, name, H):
             cb, kb = cd[0], kd[0]
         cs.append(cb)
         ks.append(kb)
-    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks, lens, 1,
+    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks, lens, s_q,
                                           cfg.sm_scale)
     e = norm_err(o.float().cpu().numpy(), ref_o)
     el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
