@@ -4,12 +4,15 @@
 A step is the whole hot path on one synthetic batch already resident in HBM:
   mla_absorb_q (q_nope . W_UK) -> mla_decode_paged (paged latent attention, split
   partitions + log-sum-exp combine) -> mla_out_proj (o_lat . W_UV).
-Default workload: DeepSeek-V2-Lite-shaped bf16 decode, 32 sequences x 4096 cached
-tokens, 16 heads, d_c 512 + d_r 64, 64-token paged blocks in a shuffled block table.
+Default workload: DeepSeek-V3-shaped bf16 decode, 64 sequences of 1024..8192 cached tokens
+(uniform), 128 heads, d_c 512 + d_r 64, 64-token paged blocks in a shuffled block table, one
+query token per sequence.  The other workloads (V2-Lite bf16, V3 with two query tokens, the
+INT4 32K and INT2 128K caches, the tiny fp32 case) are selected with --workload.
 
 value = cached-token.heads per second of step time, i.e. sum_b sum_i (L_b - s_q + i + 1) * H
-divided by the mean step time.  Several independent copies of the cache pool are
-rotated from step to step so the 256 MB Infinity Cache cannot serve the cache reads.
+divided by the mean step time.  Independent copies of the cache pool and of the weights are
+rotated from step to step (and from call to call in the per-call timings), so the 256 MB
+Infinity Cache cannot serve the cache or weight reads.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -53,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="v2lite-bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="v3-bf16-sq1", choices=sorted(WORKLOADS))
     ap.add_argument("--num-splits", type=int, default=0, help="context partitions (0 = library plan)")
     ap.add_argument("--rotate", type=int, default=0, help="cache pool copies to rotate (0 = enough to exceed 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -147,21 +150,30 @@ def main():
     qr = torch.from_numpy(x.q_rope).to(dt).to(dev)
     wuk = torch.from_numpy(x.w_uk).to(dt).to(dev)
     wuv = torch.from_numpy(x.w_uv).to(dt).to(dev)
+    # weight copies: enough that a call cycling over them reads more than 512 MB before it
+    # comes back to one (W_UK and W_UV of the V3 shapes are 16.8 MB each)
+    w_bytes = wuk.numel() * wuk.element_size()
+    n_w = max(rotate, min(256, math.ceil(512e6 / w_bytes) + 1))
+    wuks = [wuk] + [wuk.clone() for _ in range(n_w - 1)]
+    wuvs = [wuv] + [wuv.clone() for _ in range(n_w - 1)]
     max_len = int(x.seq_lens.max())
     total_len = int(x.seq_lens.astype("int64").sum())
-    step = mla.DecodeStep(wuk, wuv, desc, len(x.seq_lens), cfg.s_q, max_len, cfg.sm_scale,
-                          num_splits=args.num_splits, q_lat_dtype=dt, total_seq_len=total_len)
+    # one step object per rotated pool, each with its own weight copy
+    steps = [mla.DecodeStep(wuks[i], wuvs[i], desc, len(x.seq_lens), cfg.s_q, max_len, cfg.sm_scale,
+                            num_splits=args.num_splits, q_lat_dtype=dt, total_seq_len=total_len)
+             for i in range(rotate)]
+    step = steps[0]
     B, s_q, H = len(x.seq_lens), cfg.s_q, cfg.H
     ql = step.q_lat.view(B, s_q, H, cfg.d_c)
 
     for i in range(args.warmup):
-        step.run(qn, qr, pools[i % rotate], bt, sl)
+        steps[i % rotate].run(qn, qr, pools[i % rotate], bt, sl)
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps, {rotate} pool copies)")
+    log(f"warmup done ({args.warmup} steps, {rotate} pool copies, {n_w} weight copies)")
 
     if args.profile_run:
         for i in range(args.steps):
-            step.run(qn, qr, pools[i % rotate], bt, sl)
+            steps[i % rotate].run(qn, qr, pools[i % rotate], bt, sl)
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)          # calibration copy: 256 MiB read + 256 MiB written
@@ -174,15 +186,15 @@ def main():
     splits, tpc = mla.decode_plan(ql, qr, pools[0], desc, bt, sl, max_len, cfg.sm_scale, args.num_splits,
                                   total_seq_len=total_len)
     # (1) the step: absorb -> decode -> out_proj, one HIP graph per rotated cache pool
-    graphs = None if args.no_graph else [step.capture(qn, qr, pools[i], bt, sl) for i in range(rotate)]
+    graphs = None if args.no_graph else [steps[i].capture(qn, qr, pools[i], bt, sl) for i in range(rotate)]
     for i in range(args.warmup):
-        graphs[i % rotate].replay() if graphs else step.run(qn, qr, pools[i % rotate], bt, sl)
+        graphs[i % rotate].replay() if graphs else steps[i % rotate].run(qn, qr, pools[i % rotate], bt, sl)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(st)
     for i in range(K):
-        graphs[i % rotate].replay() if graphs else step.run(qn, qr, pools[i % rotate], bt, sl)
+        graphs[i % rotate].replay() if graphs else steps[i % rotate].run(qn, qr, pools[i % rotate], bt, sl)
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -191,7 +203,7 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
         evs[i][0].record(st)
-        graphs[i % rotate].replay() if graphs else step.run(qn, qr, pools[i % rotate], bt, sl)
+        graphs[i % rotate].replay() if graphs else steps[i % rotate].run(qn, qr, pools[i % rotate], bt, sl)
         evs[i][1].record(st)
     torch.cuda.synchronize()
     per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
@@ -218,15 +230,15 @@ def main():
         return a.elapsed_time(b) / (replays * reps)
 
     reps_dec = rotate * max(1, math.ceil(8 / rotate))
-    g_abs = capture_calls(lambda i: mla.absorb_q(qn.view(B * s_q, H, cfg.d_n), wuk, out=step.q_lat), 8)
+    g_abs = capture_calls(lambda i: mla.absorb_q(qn.view(B * s_q, H, cfg.d_n), wuks[i], out=step.q_lat), n_w)
     g_dec = capture_calls(lambda i: mla.decode_paged(ql, qr, pools[i % rotate], desc, bt, sl, max_len, cfg.sm_scale,
                                                      args.num_splits, out=step.o_lat, lse=step.lse,
                                                      workspace=step.workspace, total_seq_len=total_len), reps_dec)
-    g_out = capture_calls(lambda i: mla.out_proj(step.o_lat.view(B * s_q, H, cfg.d_c), wuv, out=step.out), 8)
+    g_out = capture_calls(lambda i: mla.out_proj(step.o_lat.view(B * s_q, H, cfg.d_c), wuvs[i], out=step.out), n_w)
     replays = max(2, math.ceil(K / 8))
-    absorb_ms = call_ms(g_abs, 8, replays)
+    absorb_ms = call_ms(g_abs, n_w, replays)
     decode_ms = call_ms(g_dec, reps_dec, replays)
-    proj_ms = call_ms(g_out, 8, replays)
+    proj_ms = call_ms(g_out, n_w, replays)
 
     # (3) the cache writer for this step's new tokens (the last s_q positions of every
     # sequence), timed like the calls above after the decode timings, into one pool copy
@@ -310,7 +322,7 @@ def main():
                       "d_r": cfg.d_r, "d_n": cfg.d_n, "d_v": cfg.d_v, "cache": cfg.latent_fmt + "/" + cfg.rope_fmt,
                       "seq_len": cfg.lens[1] if cfg.lens[0] == "fixed" else list(cfg.lens[1:]),
                       "mean_seq_len": float(x.seq_lens.mean()), "block_tokens": 64, "splits": splits,
-                      "tiles_per_split": tpc, "pool_copies_rotated": rotate},
+                      "tiles_per_split": tpc, "pool_copies_rotated": rotate, "weight_copies_rotated": n_w},
            "roofline": roof,
            "us_per_step": round(ms_per_step * 1e3, 2), "wall_us_per_step": round(wall / K * 1e6, 2),
            "step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],

@@ -145,6 +145,13 @@ typedef struct mla_decode_args {
  * and are scratch between calls (calls that overlap on one workspace race). */
 int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes);
 
+/* The same size for the plan made for num_cus compute units (0 = the current device).  With
+ * num_cus > 0, or an explicit num_splits, this is pure host logic and touches no device.  The
+ * size is that of the split partials, O(batch + ranges) x s_q x H x d_c fp32 values, and does
+ * not grow with the context while the batch's blocks fit one round of ranges (at most 256
+ * blocks per range); it is never a copy of the cached history. */
+int32_t mla_decode_workspace_size_for(const mla_decode_args* args, int32_t num_cus, size_t* bytes);
+
 /* The work split mla_decode_paged will use.  Fewer than 96 query rows per sequence
  * (s_q * num_heads): *num_splits partitions of the longest sequence of *tiles_per_split
  * 64-token blocks each.  96 rows or more: the batch's blocks, sequence after sequence, each
@@ -182,7 +189,8 @@ int32_t mla_decode_paged(const mla_decode_args* args, void* stream);
  *   max_seq_len are used; q_lat, q_rope, q_dtype, batch, s_q, num_heads, sm_scale and the
  *   cache widths must be the same in every part (else MLA_ERR_INVALID_ARG), and num_splits
  *   applies per part; o_lat, o_dtype, lse and workspace of the parts are ignored.  Any part
- *   may be NULL (absent); at least one must be given.  The recent part ends with the s_q new
+ *   may be NULL (absent); at least one must be given, and with s_q = 2 the recent part must be
+ *   (it holds the two new tokens, else MLA_ERR_INVALID_ARG).  The recent part ends with the s_q new
  *   tokens and carries the causal mask (query i sees its tokens 0 .. L - s_q + i); every query
  *   sees all sink and middle tokens (the sink and the recent window may also share one
  *   cache, passed as the recent part with no sink part: the attention does not depend on

@@ -132,6 +132,20 @@ def _decode_args(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, 
     return a
 
 
+def _check_out(t, shape, dtypes, device, name):
+    """An output the kernels write densely: exact shape, dtype, dense, on the inputs' device."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous():
+        raise ValueError(f"{name} must be a dense {list(shape)} tensor of {[str(d) for d in dtypes]}, "
+                         f"got {list(t.shape)} {t.dtype}")
+
+
+def _check_pool(pool, desc, name):
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or not pool.is_contiguous() or pool.shape[1] != block_bytes(desc):
+        raise ValueError(f"{name}: pool must be a dense uint8 [num_blocks, {block_bytes(desc)}] tensor")
+
+
 def _check_decode_tensors(q_lat, q_rope, pool, desc, block_table, seq_lens):
     _need_cuda(q_lat, q_rope, pool, block_table, seq_lens)
     if q_lat.dim() != 4 or q_rope.dim() != 4 or q_lat.shape[:3] != q_rope.shape[:3]:
@@ -178,6 +192,9 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, 
         out = torch.empty((B, s_q, H, d_c), dtype=o_dtype, device=q_lat.device)
     if lse is None and want_lse:
         lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
+    _check_out(out, (B, s_q, H, d_c), (torch.float32, torch.bfloat16), q_lat.device, "o_lat")
+    if lse is not None:
+        _check_out(lse, (B, s_q, H), (torch.float32,), q_lat.device, "lse")
     if workspace is None:
         n = decode_workspace_size(q_lat, q_rope, pool, desc, block_table, seq_lens, max_seq_len, sm_scale,
                                   num_splits, total_seq_len)
@@ -218,6 +235,7 @@ def decode_mixed(q_lat: torch.Tensor, q_rope: torch.Tensor, sink, middle, recent
 def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor) -> torch.Tensor:
     """bf16 [n, 64, d_c + d_r] view of cache blocks, from the decode kernel's own reader."""
     _need_cuda(pool, block_ids)
+    _check_pool(pool, desc, "dequant_blocks")
     if block_ids.dtype != torch.int32 or not block_ids.is_contiguous():
         raise ValueError("block_ids must be dense int32")
     n = block_ids.numel()
@@ -236,8 +254,11 @@ def append_kv(c_new: torch.Tensor, k_rope_new: torch.Tensor, pool: torch.Tensor,
     rows may be strided), slots int32 [n] (negative = skip).  pool [num_blocks, block_bytes]
     uint8 is updated in place on the current stream."""
     _need_cuda(c_new, k_rope_new, pool, slots)
+    _check_pool(pool, desc, "append_kv")
     if c_new.dim() != 2 or k_rope_new.dim() != 2 or c_new.shape[0] != k_rope_new.shape[0]:
         raise ValueError("c_new and k_rope_new must be [n, d] with the same n")
+    if c_new.shape[1] != desc.d_c or k_rope_new.shape[1] != desc.d_r:
+        raise ValueError(f"c_new [n, {desc.d_c}] and k_rope_new [n, {desc.d_r}] expected by the descriptor")
     if c_new.dtype != k_rope_new.dtype:
         raise ValueError("c_new and k_rope_new must share a dtype")
     if c_new.stride(1) != 1 or k_rope_new.stride(1) != 1:

@@ -257,6 +257,8 @@ int32_t mixed_layout(const mla_decode_args* const parts[3], MixedLayout* m) {
       break;
     }
   if (ref == nullptr) return MLA_ERR_INVALID_ARG;
+  // with two query tokens the new tokens sit in the recent part, the only one with the causal mask
+  if (ref->s_q == 2 && parts[2] == nullptr) return MLA_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i) {
     const mla_decode_args* a = parts[i];
     if (a == nullptr) continue;
@@ -345,26 +347,35 @@ int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* n
   return MLA_OK;
 }
 
-int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes) {
+int32_t mla_decode_workspace_size_for(const mla_decode_args* args, int32_t num_cus, size_t* bytes) {
   Layout lay;
   int32_t s = validate_decode(args, &lay);
   if (s != MLA_OK) return s;
-  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
-  int cus = 0;
-  s = device_cus(&cus);
-  if (s != MLA_OK) return s;
+  if (bytes == nullptr || num_cus < 0) return MLA_ERR_INVALID_ARG;
+  int cus = num_cus;
+  if (cus == 0 && args->num_splits == 0) {
+    s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+  }
   size_t lse_off = 0;
   *bytes = partial_bytes(args, make_plan(args, cus), &lse_off);
   return MLA_OK;
+}
+
+int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes) {
+  return mla_decode_workspace_size_for(args, 0, bytes);
 }
 
 int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   Layout lay;
   int32_t s = validate_decode(a, &lay);
   if (s != MLA_OK) return s;
+  // an explicit split count fixes the plan without the device's CU count
   int cus = 0;
-  s = device_cus(&cus);
-  if (s != MLA_OK) return s;
+  if (a->num_splits == 0) {
+    s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+  }
   const Plan plan = make_plan(a, cus);
   size_t lse_off = 0;
   const size_t need = partial_bytes(a, plan, &lse_off);

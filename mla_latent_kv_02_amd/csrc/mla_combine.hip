@@ -45,9 +45,11 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
   for (int t0 = tok_begin; t0 < tok_end; t0 += 16) {
     const int tok = t0 + (tid >> 3), sub = tid & 7;
     float part = 0.f;
+    bool live = false;   // a token past the range, or of a block-table entry outside the pool, is not attended
     if (tok < tok_end) {
       const int id = btab[tok / BLOCK_TOKENS];
       if (id >= 0 && (int64_t)id < p.num_blocks) {
+        live = true;
         const float* row = (const float*)(p.pool + (size_t)id * p.block_bytes) + (size_t)(tok % BLOCK_TOKENS) * dk;
         for (int d = sub; d < dk; d += 8) part += qs[d] * row[d];
       }
@@ -55,22 +57,23 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeParams p) {
     part += __shfl_xor(part, 1, 8);
     part += __shfl_xor(part, 2, 8);
     part += __shfl_xor(part, 4, 8);
-    if (sub == 0) sc[tid >> 3] = tok < tok_end ? part * scale : -__builtin_inff();
+    if (sub == 0) sc[tid >> 3] = live ? part * scale : -__builtin_inff();
     __syncthreads();
     float tm = sc[0];
     for (int j = 1; j < 16; ++j) tm = fmaxf(tm, sc[j]);
     const float mn = fmaxf(m, tm);
-    const float alpha = expf(m - mn);
+    // while nothing has been attended (mn = -inf) there is nothing to rescale
+    const float alpha = mn == -__builtin_inff() ? 1.f : expf(m - mn);
     l *= alpha;
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[k] *= alpha;
     m = mn;
     for (int j = 0; j < 16 && t0 + j < tok_end; ++j) {
+      if (sc[j] == -__builtin_inff()) continue;
       const float pj = expf(sc[j] - mn);
       l += pj;
       const int tk = t0 + j;
       const int id = btab[tk / BLOCK_TOKENS];
-      if (id < 0 || (int64_t)id >= p.num_blocks) continue;
       const float* row = (const float*)(p.pool + (size_t)id * p.block_bytes) + (size_t)(tk % BLOCK_TOKENS) * dk;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {

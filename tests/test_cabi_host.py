@@ -194,3 +194,69 @@ def test_mixed_validation():
     c = _args(q_lat=FAKE + 4096)
     assert L.mla_decode_mixed(ctypes.byref(a), ctypes.byref(c), None, FAKE, 0, None, FAKE, 1 << 30, None) == 1
     assert L.mla_decode_mixed_workspace_size(ctypes.byref(a), None, None, None) == 1
+
+
+def test_mixed_two_queries_need_the_recent_part():
+    """With s_q = 2 the new tokens (and the causal mask) live in the recent part: a call
+    without it is rejected before anything touches a device."""
+    L = mla.lib()
+    a = _args(s_q=2, cache=mla.cache_desc(512, 64, "int4", "int4", 64, 64))
+    n = ctypes.c_size_t()
+    assert L.mla_decode_mixed_workspace_size(ctypes.byref(a), ctypes.byref(a), None, ctypes.byref(n)) == 1
+    assert L.mla_decode_mixed(ctypes.byref(a), ctypes.byref(a), None, FAKE, 0, None, FAKE, 1 << 30, None) == 1
+
+
+def _ws(a, cus=256):
+    n = ctypes.c_size_t()
+    st = mla.lib().mla_decode_workspace_size_for(ctypes.byref(a), cus, ctypes.byref(n))
+    assert st == 0
+    return n.value
+
+
+@pytest.mark.parametrize("B,H,s_q", [(32, 16, 1), (16, 16, 1), (64, 128, 1), (64, 128, 2), (4, 128, 1)])
+def test_workspace_is_split_partials_not_history(B, H, s_q):
+    """The workspace holds the split partials, O((B + ranges) s_q H d_c) fp32 values: it does not
+    grow with the context (1K .. 128K tokens per sequence, while the batch's blocks fit one
+    round of ranges), is never as large as an fp32 copy of the cached history, and equals the
+    size of the plan's partial layout."""
+    cus = 256
+    R = s_q * H
+    sizes = {}
+    for Lmax in (1024, 8192, 32768, 131072):
+        a = _args(batch=B, num_heads=H, s_q=s_q, max_seq_len=Lmax, block_table_stride=-(-Lmax // 64))
+        blocks = B * -(-Lmax // 64)
+        if R >= 96 and blocks + 3 * B > 256 * (cus // -(-R // 128)):
+            continue   # ranges of more than 256 blocks would be needed: more ranges, more partials
+        ws = _ws(a, cus)
+        st, splits, _tpc = _plan(a, cus)
+        assert st == 0
+        if R >= 96:
+            slots = B + splits - 1
+            expect_o = slots * R * 512 * 4
+            assert expect_o <= ws <= expect_o + 2 * slots * R * 4 + 3 * 256 + 4 * (B + 2)
+        else:
+            expect_o = B * splits * R * 512 * 4 if splits > 1 else 0
+            assert expect_o <= ws <= expect_o + B * splits * R * 4 + 512
+        assert ws < B * Lmax * 576 * 4 or Lmax == 1024
+        sizes[Lmax] = ws
+    # a short batch has fewer blocks than workgroups, so fewer partials; from one round of
+    # ranges on, the size stays put however long the context grows
+    top = sizes[max(sizes)]
+    assert all(v <= top for v in sizes.values()), sizes
+    assert len({v for k, v in sizes.items() if k >= 8192}) == 1, sizes
+
+
+def test_workspace_too_small_is_rejected_before_any_launch():
+    """MLA_ERR_WORKSPACE for a missing, short or misaligned workspace.  An explicit split count
+    fixes the plan without querying the device, so these calls run on the CPU."""
+    L = mla.lib()
+    for H in (16, 128):
+        a = _args(num_heads=H, num_splits=2)
+        need = _ws(a, 0)
+        assert need > 0
+        a.workspace, a.workspace_bytes = None, need
+        assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE
+        a.workspace, a.workspace_bytes = FAKE, need - 1
+        assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE
+        a.workspace, a.workspace_bytes = FAKE + 128, need
+        assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE

@@ -13,7 +13,7 @@ torch = pytest.importorskip("torch")
 import oracle  # noqa: E402
 from mla_synth import CONFIGS, make_inputs  # noqa: E402
 from tests.gpu_helpers import bf16_exact, desc_of, dev, logical_cache, norm_err, to_device  # noqa: E402
-from tests.test_gpu_parity import TOL_BF16, _decode_stage, assert_bf16_output  # noqa: E402
+from tests.test_gpu_parity import TOL_BF16, TOL_F32, _decode_stage, assert_bf16_output  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -31,12 +31,12 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _check(o, lse, ref_o, ref_lse):
+def _check(o, lse, ref_o, ref_lse, tol=TOL_BF16):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     e = norm_err(o, ref_o)
     el = float(np.max(np.abs(lse - ref_lse)))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
-    assert e <= TOL_BF16 and el <= TOL_BF16
+    assert e <= tol and el <= tol
 
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
@@ -100,8 +100,12 @@ def test_range_deterministic(mla):
 def _run(mla, x, seq_lens, block_table, splits=0):
     cfg = x.cfg
     t = to_device(x)
-    q_lat64 = bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))
-    q = torch.from_numpy(q_lat64).to(torch.bfloat16).to(dev())
+    if cfg.dtype == "f32":
+        q_lat64 = oracle.absorb_q(x.q_nope, x.w_uk).astype(np.float32).astype(np.float64)
+        q = torch.from_numpy(q_lat64.astype(np.float32)).to(dev())
+    else:
+        q_lat64 = bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))
+        q = torch.from_numpy(q_lat64).to(torch.bfloat16).to(dev())
     o, l = mla.decode_paged(q, t["q_rope"], t["pool"], desc_of(cfg), torch.from_numpy(block_table).to(dev()),
                             torch.from_numpy(seq_lens).to(dev()), int(x.seq_lens.max()), cfg.sm_scale,
                             num_splits=splits)
@@ -109,9 +113,10 @@ def _run(mla, x, seq_lens, block_table, splits=0):
     return q_lat64, o.float().cpu().numpy(), l.cpu().numpy()
 
 
-@pytest.mark.parametrize("name,H", [("2", 16), ("3", 128)])
+@pytest.mark.parametrize("name,H", [("1", 8), ("2", 16), ("3", 128)])
 def test_empty_sequences(mla, name, H):
-    """A sequence of length 0 attends to nothing: o = 0, lse = -inf; the others are unaffected."""
+    """A sequence of length 0 attends to nothing: o = 0, lse = -inf; the others are unaffected
+    (fp32 cache kernel, partition kernel, row-owner kernel)."""
     x = make_inputs(CONFIGS[name], 52, lens=[100, 1, 300, 1, 65], H=H)
     lens = x.seq_lens.copy()
     lens[[1, 3]] = 0
@@ -124,10 +129,14 @@ def test_empty_sequences(mla, name, H):
         ref_o, ref_lse = oracle.attend_latent(q_lat64[keep], x.q_rope[keep].astype(np.float64),
                                               [c[b] for b in keep], [k[b] for b in keep], x.seq_lens[keep],
                                               x.cfg.s_q, x.cfg.sm_scale)
-        _check(o[keep], lse[keep], ref_o, ref_lse)
+        _check(o[keep], lse[keep], ref_o, ref_lse, _tol(x))
 
 
-@pytest.mark.parametrize("name,H", [("2", 16), ("3", 128)])
+def _tol(x):
+    return TOL_F32 if x.cfg.dtype == "f32" else TOL_BF16
+
+
+@pytest.mark.parametrize("name,H", [("1", 8), ("2", 16), ("3", 128)])
 def test_out_of_range_block_ids_are_skipped(mla, name, H):
     """Tokens of a block-table entry outside [0, num_blocks) take no part in the softmax:
     the result equals attention over the sequence with that block's tokens removed."""
@@ -145,7 +154,7 @@ def test_out_of_range_block_ids_are_skipped(mla, name, H):
     k2 = [k[0][keep0], k[1][keep1]]
     ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c2, k2,
                                           np.array([len(keep0), len(keep1)]), x.cfg.s_q, x.cfg.sm_scale)
-    _check(o, lse, ref_o, ref_lse)
+    _check(o, lse, ref_o, ref_lse, _tol(x))
 
 
 def test_range_start_charge(mla):
