@@ -19,10 +19,10 @@
 //   * scores S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T held in
 //     registers for the whole partition), 2*RT waves each own one 16-row x
 //     16-token tile; per-row maxima are exchanged through LDS; P = exp2(x - m)
-//     is written to LDS in bf16;
-//   * O += P . C on the same MFMA: wave w owns latent columns [64w, 64w + 64)
-//     of all rows; the C operand comes from the token-major stage with
-//     ds_read_b64_tr_b16.
+//     is written to LDS as two bf16 terms (hi + lo, ~16 significant bits);
+//   * O += P . C on the same MFMA, once per P term: wave w owns latent columns
+//     [64w, 64w + 64) of all rows; the C operand comes from the token-major
+//     stage with ds_read_b64_tr_b16 and feeds both MFMAs.
 // Partials (o, lse) of the partitions are merged by combine_kernel.
 #include <hip/hip_runtime.h>
 
@@ -128,14 +128,22 @@ struct Producer<FMT_BF16> {
 
 // Quantised latent (INT4 or INT2) + INT4 rope: the four code planes of a half block are
 // copied into a flat, token-major code stage [lc | ls | rc | rs], padded to SLOTS pieces.
-template <int FMT>
+// A half block holds 256 (INT4) or 128 (INT2) latent code slots, 4096 / latent_group scale
+// slots, 64 RoPE code slots and 512 / rope_group RoPE scale slots: at most 720 (INT4) and
+// 464 (INT2).  INT4: waves 0 .. WLO-1 issue two DMA instructions per stage, the others one
+// (WLO = 4: 768 slots, every layout; WLO = 3: 704 slots, latent groups of 64 or more).
+template <int FMT, int WLO = 4>
 struct QuantProducer {
   static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
   static constexpr int LB = 512 * BITS / 8;        // latent code bytes per token
-  // code stage capacity in 16-byte slots: INT4 waves 0-3 issue 2 instructions, waves 4-7 one
-  static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;
-  static constexpr int LOADS_HI = 1;
-  static constexpr int SLOTS = FMT == FMT_INT4 ? 768 : 512;
+  static constexpr int LOADS_LO = FMT == FMT_INT4 ? 2 : 1;   // instructions of waves 0 .. WAVES_LO-1
+  static constexpr int LOADS_HI = 1;                          // of the other waves
+  static constexpr int WAVES_LO = FMT == FMT_INT4 ? WLO : 8;
+  static constexpr int SLOTS = 64 * (WAVES_LO * LOADS_LO + (8 - WAVES_LO) * LOADS_HI);
+  // code stage slots a layout needs (groups = 512 / latent_group, rgroups = 64 / rope_group)
+  __host__ __device__ static constexpr int slots_needed(int groups, int rgroups) {
+    return ST_TOK * LB / 16 + ST_TOK * groups * 4 / 16 + ST_TOK * 32 / 16 + (ST_TOK * rgroups * 4 + 15) / 16;
+  }
   __device__ __forceinline__ static void issue(const uint8_t* blk, int half, const QuantPlanes& pl, int groups,
                                                int rgroups, uint8_t* cstage, int tid) {
     issue_with(half, pl, groups, rgroups, tid, [&](int off, int i, int wbase) {
@@ -155,7 +163,7 @@ struct QuantProducer {
     const int wbase = tid & ~63;
 #pragma unroll
     for (int i = 0; i < LOADS_LO; ++i) {
-      if (i == LOADS_HI && tid >= 256) break;
+      if (i == LOADS_HI && tid >= 64 * WAVES_LO) break;
       const int slot = i * NT + tid;
       // padding slots re-load a real piece (spread over the stage, never one shared address)
       int p = slot < n_all ? slot : slot - n_all;
@@ -262,10 +270,10 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t C5[CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C6[SPLIT ? 16 : CBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t C7[SPLIT ? 16 : CBYTES];
-  __shared__ __attribute__((aligned(16))) bf16_t Ps[ROWS * PROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Ps[ROWS * PROW];   // P, high bf16 term
+  __shared__ __attribute__((aligned(16))) bf16_t Pl[ROWS * PROW];   // P, low bf16 term
   __shared__ float red[2][ROWS];
-  __shared__ float redl[2][ROWS];   // row sums of the bf16-rounded P (normalise o)
-  __shared__ float redx[2][ROWS];   // row sums of the unrounded P (lse)
+  __shared__ float redx[2][ROWS];   // row sums of P (normalisation and lse)
   __shared__ float mfin[ROWS];
   __shared__ __attribute__((aligned(16))) float alpha[ROWS];
   __shared__ int bids[MAX_TPC];
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   }
 
   const float NEG_INF = -__builtin_inff();
-  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
+  float m_s = NEG_INF, l_x = 0.f;
   f32x4 acc[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -355,7 +363,8 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
   auto wait_stage = [&](int later) {
     constexpr int LA = QUANT ? QP::LOADS_LO : Producer<FMT_BF16>::LOADS_LO;
     constexpr int LB = QUANT ? QP::LOADS_HI : Producer<FMT_BF16>::LOADS_HI;
-    const int n = w < 4 ? LA : LB;
+    constexpr int WA = QUANT ? QP::WAVES_LO : 4;   // waves issuing LA instructions per stage
+    const int n = w < WA ? LA : LB;
     auto wait_n = [&](auto K) {
       if (n == LA) __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * LA));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * LB));
@@ -454,19 +463,20 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
       const float mu = mn == NEG_INF ? 0.f : mn;
       const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
-      l_s *= al;
       l_x *= al;
       m_s = mn;
       if (sc_tt == 0 && lg == 0) alpha[row_s] = al;
-      uint32_t pb[4];
+      float pf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pf = __builtin_amdgcn_exp2f(sv[i] - mu);
-        pb[i] = f32_to_bf16_bits(pf);
-        l_s += bf16_bits_to_f32(pb[i]);
-        l_x += pf;
+        pf[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+        l_x += pf[i];
       }
-      *(uint2*)&Ps[row_s * PROW + sc_tt * 16 + lg * 4] = uint2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+      uint32_t h0, l0, h1, l1;
+      split_pair(pf[0], pf[1], h0, l0);
+      split_pair(pf[2], pf[3], h1, l1);
+      *(uint2*)&Ps[row_s * PROW + sc_tt * 16 + lg * 4] = uint2{h0, h1};
+      *(uint2*)&Pl[row_s * PROW + sc_tt * 16 + lg * 4] = uint2{l0, l1};
     }
   };
   auto pv_phase = [&](const bf16_t* KS) {
@@ -486,11 +496,14 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       }
     }
 
-    // ---- O[rows][64w .. 64w+63] += P . C over the 32 tokens of the stage
+    // ---- O[rows][64w .. 64w+63] += (P_hi + P_lo) . C over the 32 tokens of the stage
     {
-      bf16x8 a[RT];
+      bf16x8 a[RT], al_[RT];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) a[rt] = *(const bf16x8*)&Ps[(rt * 16 + lr) * PROW + lg * 8];
+      for (int rt = 0; rt < RT; ++rt) {
+        a[rt] = *(const bf16x8*)&Ps[(rt * 16 + lr) * PROW + lg * 8];
+        al_[rt] = *(const bf16x8*)&Pl[(rt * 16 + lr) * PROW + lg * 8];
+      }
       const int t0 = lg * 8 + (lr >> 2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -501,6 +514,9 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], bv, acc[rt][nt], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al_[rt], bv, acc[rt][nt], 0, 0, 0);
       }
     }
   };
@@ -600,10 +616,8 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
 
   // ---- finish: row sums over lanes and token tiles, normalise, write
   if (scorer) {
-    l_s = wave_sum_16_32(l_s);
     l_x = wave_sum_16_32(l_x);
     if (lg == 0) {
-      redl[sc_tt][row_s] = l_s;
       redx[sc_tt][row_s] = l_x;
       if (sc_tt == 0) mfin[row_s] = m_s;
     }
@@ -617,7 +631,7 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
       const int row = rt * 16 + lg * 4 + i;
       const int rgl = r0 + row;
       if (rgl >= R) continue;
-      const float lt = redl[0][row] + redl[1][row];
+      const float lt = redx[0][row] + redx[1][row];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const size_t obase = (unit_row0 + rgl) * 512 + w * 64 + lr;
       if (p.out_bf16) {
@@ -645,22 +659,27 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
 // the 64 output columns it owns, and wavefronts 1-7 dequantise stage s + 2 into the third
 // bf16 buffer, so the dequantisation (VALU), the scores (MFMA) and the HBM reads of later
 // code stages overlap.  Code stage k sits in ring slot k mod 4, bf16 stage k in buffer k mod 3,
-// P and the rescale factors of stage k in buffer k mod 2.  The DMA is inline asm (each wait
-// for it is explicit), so one LDS array holds every buffer.
+// P (two bf16 terms) and the rescale factors of stage k in buffer k mod 2.  The DMA is inline
+// asm (each wait for it is explicit), so one LDS array holds every buffer.  The INT4 code
+// stages take 704 slots (latent groups of 64 or more; the launcher sends group 32 elsewhere),
+// which leaves the LDS room for both P terms.
 // ---------------------------------------------------------------------------------------
+template <int FMT>
+using PipeQP = QuantProducer<FMT, 3>;
+
 template <int FMT, bool QF32>
 __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
-  using QP = QuantProducer<FMT>;
+  using QP = PipeQP<FMT>;
   constexpr int DEPTH = 4;                         // code ring slots
   constexpr int CBYTES = QP::SLOTS * 16;
   constexpr int BF = ST_ELEMS * 2;                 // bytes of a bf16 stage
   constexpr int OFF_C = 3 * BF;
   constexpr int OFF_P = OFF_C + DEPTH * CBYTES;
-  constexpr int PBYTES = 16 * PROW * 2;
-  constexpr int SMEM = OFF_P + 2 * PBYTES;
+  constexpr int PBYTES = 16 * PROW * 2;            // one P term of one stage
+  constexpr int SMEM = OFF_P + 4 * PBYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ __attribute__((aligned(16))) float alpha[2][16];
-  __shared__ float fin[3][16];                     // row sums of bf16 P, of unrounded P, maximum
+  __shared__ float fin[2][16];                     // row sums of P, maximum
   __shared__ int bids[MAX_TPC];
 
   const int tid = threadIdx.x;
@@ -695,7 +714,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     for (int ks = 0; ks < 2; ++ks)
       qreg[16 + ks] = qrow ? load_q8(p.q_rope, qbase * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
   }
-  float m_s = NEG_INF, l_s = 0.f, l_x = 0.f;
+  float m_s = NEG_INF, l_x = 0.f;
   // output columns: wave w owns column group w
   f32x4 acc[4];
 #pragma unroll
@@ -726,7 +745,8 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   const uint32_t sbase = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto bbuf = [&](int k) { return (bf16_t*)(smem + (k % 3) * BF); };
   auto cslot = [&](int k) { return smem + OFF_C + (k % DEPTH) * CBYTES; };
-  auto pbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * PBYTES); };
+  auto pbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * 2 * PBYTES); };            // high term
+  auto plbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * 2 * PBYTES + PBYTES); };  // low term
   // every thread issues its LOADS_LO / LOADS_HI pieces of a code stage
   auto issue = [&](int k) {
     int half, valid;
@@ -739,7 +759,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   // wait until code stage k has landed, `later` code stages having been issued after it
   auto wait_later = [&](int later) {
     auto wait_n = [&](auto K) {
-      if (w < 4)
+      if (w < QP::WAVES_LO)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * QP::LOADS_LO));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(K)::value * QP::LOADS_HI));
@@ -820,26 +840,28 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     const float mn = mt > m_s + RESCALE_SLACK ? mt : m_s;
     const float mu = mn == NEG_INF ? 0.f : mn;
     const float al = mn == m_s ? 1.f : __builtin_amdgcn_exp2f(m_s - mu);
-    l_s *= al;
     l_x *= al;
     m_s = mn;
     bf16_t* P = pbuf(s);
+    bf16_t* PL = plbuf(s);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      uint32_t pb[4];
+      float pf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pf = __builtin_amdgcn_exp2f(sv[tt][i] - mu);
-        pb[i] = f32_to_bf16_bits(pf);
-        l_s += bf16_bits_to_f32(pb[i]);
-        l_x += pf;
+        pf[i] = __builtin_amdgcn_exp2f(sv[tt][i] - mu);
+        l_x += pf[i];
       }
-      *(uint2*)&P[lr * PROW + tt * 16 + lg * 4] = uint2{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+      uint32_t h0, l0, h1, l1;
+      split_pair(pf[0], pf[1], h0, l0);
+      split_pair(pf[2], pf[3], h1, l1);
+      *(uint2*)&P[lr * PROW + tt * 16 + lg * 4] = uint2{h0, h1};
+      *(uint2*)&PL[lr * PROW + tt * 16 + lg * 4] = uint2{l0, l1};
     }
     if (lg == 0) alpha[s & 1][lr] = al;
   };
 
-  // O[16 rows][64 cg .. 64 cg + 63] = alpha(s) O + P(s) . C(s) into accumulators o
+  // O[16 rows][64 cg .. 64 cg + 63] = alpha(s) O + (P_hi(s) + P_lo(s)) . C(s) into accumulators o
   auto pv = [&](int s, int cg, f32x4 (&o)[4]) {
     const bf16_t* KS = bbuf(s);
     const f32x4 al = *(const f32x4*)&alpha[s & 1][lg * 4];
@@ -849,6 +871,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     }
     f32x4* acc = o;
     const bf16x8 a = *(const bf16x8*)&pbuf(s)[lr * PROW + lg * 8];
+    const bf16x8 al_ = *(const bf16x8*)&plbuf(s)[lr * PROW + lg * 8];
     const int t0 = lg * 8 + (lr >> 2);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -857,6 +880,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[st_off(t0 + 4, d)]);
       const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al_, bv, acc[nt], 0, 0, 0);
     }
   };
 
@@ -901,11 +925,10 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   // ---- finish: wavefront 0 publishes the row sums and maxima; every wavefront normalises and
   // writes its 64 columns
   if (w == 0) {
-    const float ls = wave_sum_16_32(l_s), lx = wave_sum_16_32(l_x);
+    const float lx = wave_sum_16_32(l_x);
     if (lg == 0) {
-      fin[0][lr] = ls;
-      fin[1][lr] = lx;
-      fin[2][lr] = m_s;
+      fin[0][lr] = lx;
+      fin[1][lr] = m_s;
     }
   }
   lds_barrier();
@@ -932,8 +955,8 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   };
   write_cols(w, acc);
   if (p.out_lse != nullptr && tid < 16 && tid < R) {
-    const float lt = fin[1][tid];
-    p.out_lse[unit_row0 + tid] = lt > 0.f ? (fin[2][tid] + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
+    const float lt = fin[0][tid];
+    p.out_lse[unit_row0 + tid] = lt > 0.f ? (fin[1][tid] + __log2f(lt)) * 0.69314718055994531f : NEG_INF;
   }
 }
 
@@ -943,7 +966,9 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
 template <int RT, int FMT>
 static hipError_t launch_mfma(const DecodeParams& p, int grid, hipStream_t st) {
   if constexpr (RT == 1 && FMT != FMT_BF16) {
-    // quantised cache, at most 16 rows: the pipelined kernel
+    // quantised cache, at most 16 rows: the pipelined kernel when its code stage holds the
+    // layout, else the split kernel with 32-row tiles (same grid: one row group either way)
+    if (PipeQP<FMT>::slots_needed(512 / p.g_lat, 64 / p.g_rope) > PipeQP<FMT>::SLOTS) return launch_mfma<2, FMT>(p, grid, st);
     if (p.q_f32)
       hipLaunchKernelGGL((decode_pipe_kernel<FMT, true>), dim3(grid), dim3(NT), 0, st, p);
     else

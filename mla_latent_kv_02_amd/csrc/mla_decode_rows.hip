@@ -16,8 +16,9 @@
 //   * O^T += V^T . P^T: the score accumulators are already the P^T operand once the token
 //     order inside the 32-token step is taken as (4 tokens of tile 0, 4 of tile 1) per lane
 //     group, and V^T fragments come from the token-major stage with ds_read_b64_tr_b16 in the
-//     same order; each V^T fragment feeds two MFMAs; O^T (32 rows x 512) stays in AGPRs,
-//     touched only by inline asm (MFMAs, a rare LDS round-trip rescale, stores).
+//     same order.  P is split into two bf16 terms (hi + lo, ~16 significant bits), so each
+//     V^T fragment feeds four MFMAs (two row tiles x two terms); O^T (32 rows x 512) stays in
+//     AGPRs, touched only by inline asm (MFMAs, a rare LDS round-trip rescale, stores).
 // There is no cross-wave dependency inside a step: one barrier per 32-token stage guards the
 // ring of LDS stages.
 //
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   // ---- per-wave state: rows row0 + 16 rt, row0 = rg * 128 + 32 w + lr
   const int row0 = rg * ROWS + 32 * w + lr;
   bf16x8 qreg[RT][18];
-  float m_s[RT], l_s[RT], l_x[RT];
+  float m_s[RT], l_x[RT];
   int lim[RT];
   int lim_all = -1;   // every query row of the piece attends tokens 0 .. lim_all (L - s_q)
   f32x4 acc[RT][32];
@@ -534,7 +535,6 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         qreg[rt][16 + ks] = ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
       lim[rt] = ok ? L - p.s_q + row / p.H : -1;
       m_s[rt] = NEG_INF;
-      l_s[rt] = 0.f;
       l_x[rt] = 0.f;
     }
     lim_all = L - p.s_q;
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
 
     // ---- softmax of rows row0 + 16 rt (this lane holds tokens 16 tt + 4 lg + i).  On most
     // steps every token of the stage is visible to every row: no per-token mask.
-    bf16x8 pt[RT];
+    bf16x8 pt[RT], ptl[RT];   // P^T operands: high and low bf16 terms
     float al[RT];
     auto softmax = [&](auto FULL) {
       constexpr bool F = decltype(FULL)::value;
@@ -780,24 +780,22 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         const float mu = mn == NEG_INF ? 0.f : mn;
         // while m_s = -inf every P so far was 0 and the accumulators hold zeros: nothing to scale
         al[rt] = (mn == m_s[rt] || m_s[rt] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_s[rt] - mu);
-        l_s[rt] *= al[rt];
         l_x[rt] *= al[rt];
         m_s[rt] = mn;
-        uint32_t pw[4];
+        uint32_t pw[4], pl[4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          uint32_t pb[4];
+          float pf[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pf = __builtin_amdgcn_exp2f(sc[tt][rt][i] - mu);
-            pb[i] = f32_to_bf16_bits(pf);
-            l_s[rt] += bf16_bits_to_f32(pb[i]);
-            l_x[rt] += pf;
+            pf[i] = __builtin_amdgcn_exp2f(sc[tt][rt][i] - mu);
+            l_x[rt] += pf[i];
           }
-          pw[2 * tt] = pb[0] | (pb[1] << 16);
-          pw[2 * tt + 1] = pb[2] | (pb[3] << 16);
+          split_pair(pf[0], pf[1], pw[2 * tt], pl[2 * tt]);
+          split_pair(pf[2], pf[3], pw[2 * tt + 1], pl[2 * tt + 1]);
         }
         pt[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        ptl[rt] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
       }
     };
     if (valid == ST_TOK && stok + (ST_TOK - 1) <= lim_all) softmax(std::true_type{});
@@ -852,8 +850,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
           else pv1<F, false, false>(acc[0][nt], v, pt[0]);
           __builtin_amdgcn_sched_barrier(0);
           if (nt + PD < 32) hi[nx] = rhi(nt + PD);
-          if (nt == 31) pv1<F, false, true>(acc[1][nt], v, pt[1]);
-          else pv1<F, false, false>(acc[1][nt], v, pt[1]);
+          pv1<F, false, false>(acc[1][nt], v, pt[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          pv1<false, false, false>(acc[0][nt], v, ptl[0]);
+          if (nt == 31) pv1<false, false, true>(acc[1][nt], v, ptl[1]);
+          else pv1<false, false, false>(acc[1][nt], v, ptl[1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -869,14 +870,14 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int row = row0 + 16 * rt;
-        const float ls = sum_lg(l_s[rt]), lx = sum_lg(l_x[rt]);
+        const float lx = sum_lg(l_x[rt]);
         if (row < R) {
           float* o = p.part_o + (slot * R + row) * 512 + 4 * lg;
 #pragma unroll
           for (int nt = 0; nt < 32; ++nt) store_tile(o + nt * 16, acc[rt][nt]);
           if (lg == 0) {
             p.part_lse[slot * R + row] = lx > 0.f ? (m_s[rt] + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
-            p.part_inv[slot * R + row] = ls > 0.f ? 1.f / ls : 0.f;
+            p.part_inv[slot * R + row] = lx > 0.f ? 1.f / lx : 0.f;
           }
         }
       }

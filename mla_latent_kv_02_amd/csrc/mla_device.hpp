@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Softmax weights for the P.V MFMA as two bf16 terms: hi = RNE_bf16(p) and lo = RNE_bf16(p - hi),
+// both packed in pairs (p0 in the low half).  p - hi is exact in fp32, so hi + lo keeps about 16
+// significant bits of p; one bf16 P (8 bits) moves o_lat by up to ~2^-9 relative, as much as the
+// whole error budget of an fp32-accumulated decode.
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(p0, p1);
+  lo = pack_bf16x2(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
   return (float)v;
