@@ -32,10 +32,11 @@
  *
  * Ownership and streams
  *   The caller owns all memory (device pointers unless stated).  libmla never
- *   allocates, frees or keeps pointers after a call returns.  Every compute call
+ *   calls an allocator, frees or keeps pointers after a call returns.  Every compute call
  *   is asynchronous on the caller's stream (a hipStream_t passed as void*, NULL =
  *   the null stream); buffers must stay valid until that stream has completed.
- *   The only process-wide state is a cached per-device CU count.
+ *   The only process-wide state is a cached per-device CU count, and the per-device scratch
+ *   array (and its looked-up address) of mla_decode_paged_noalloc.
  *
  * Errors
  *   Every entry point returns an mla_status (int32_t).  Arguments are validated
@@ -179,6 +180,20 @@ int32_t mla_decode_plan(const mla_decode_args* args, int32_t num_cus, int32_t* n
  *   fp32 kernel for F32 caches (d_c <= 1024, d_r <= 256).
  */
 int32_t mla_decode_paged(const mla_decode_args* args, void* stream);
+
+/*
+ * mla_decode_paged_noalloc: mla_decode_paged that allocates nothing and takes no workspace, for
+ *   callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid allocation).  args->workspace and args->workspace_bytes are
+ *   ignored: the split partials go to a scratch array of 128 MiB that the library holds on each
+ *   device it runs on until the process ends (its address is looked up on the first call on a
+ *   device).  A call whose partials need more than that (mla_decode_workspace_size() above
+ *   128 MiB, e.g. 256 query rows per sequence over a V3-sized batch) returns MLA_ERR_WORKSPACE
+ *   and launches nothing.  Every call on a device shares that device's array and leaves its
+ *   contents behind: calls that overlap on one device (two streams, two threads) race.  Same
+ *   results, bit for bit, as mla_decode_paged with the same arguments.
+ */
+int32_t mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
 
 /*
  * mla_decode_mixed: one decode over a history kept at two precisions, the deployed policy of

@@ -366,7 +366,13 @@ int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes) {
   return mla_decode_workspace_size_for(args, 0, bytes);
 }
 
-int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode with its split partials in `ws`: the caller's workspace (mla_decode_paged) or
+// the library's per-device scratch array (mla_decode_paged_noalloc, ws == nullptr on entry).
+int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream) {
   Layout lay;
   int32_t s = validate_decode(a, &lay);
   if (s != MLA_OK) return s;
@@ -379,8 +385,14 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   const Plan plan = make_plan(a, cus);
   size_t lse_off = 0;
   const size_t need = partial_bytes(a, plan, &lse_off);
-  if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need || !aligned(a->workspace, 256)))
+  void* ws = a->workspace;
+  if (noalloc) {
+    if (need > mla::kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+    ws = nullptr;
+    if (need > 0 && mla::noalloc_scratch(&ws) != hipSuccess) return MLA_ERR_HIP;
+  } else if (need > 0 && (ws == nullptr || a->workspace_bytes < need || !aligned(ws, 256))) {
     return MLA_ERR_WORKSPACE;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   if (plan.rows) {
@@ -417,10 +429,10 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
     r.out = a->o_lat;
     r.out_bf16 = a->o_dtype == MLA_BF16;
     r.out_lse = a->lse;
-    r.meta = (int32_t*)a->workspace;
-    r.part_o = (float*)((char*)a->workspace + rows_meta_bytes(a));
-    r.part_lse = (float*)((char*)a->workspace + lse_off);
-    r.part_inv = (float*)((char*)a->workspace + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
+    r.meta = (int32_t*)ws;
+    r.part_o = (float*)((char*)ws + rows_meta_bytes(a));
+    r.part_lse = (float*)((char*)ws + lse_off);
+    r.part_inv = (float*)((char*)ws + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
     hipError_t e = mla::launch_decode_rows(r, a->cache.latent_fmt, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
     {
@@ -472,8 +484,8 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.tpc = plan.tpc;
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
   const bool split = plan.splits > 1;
-  float* part_o = split ? (float*)a->workspace : nullptr;
-  float* part_lse = split ? (float*)((char*)a->workspace + lse_off) : nullptr;
+  float* part_o = split ? (float*)ws : nullptr;
+  float* part_lse = split ? (float*)((char*)ws + lse_off) : nullptr;
   p.out = split ? (void*)part_o : a->o_lat;
   p.out_bf16 = split ? 0 : (a->o_dtype == MLA_BF16);
   p.out_lse = split ? part_lse : a->lse;
@@ -503,6 +515,14 @@ int32_t mla_decode_paged(const mla_decode_args* a, void* stream) {
   }
   return MLA_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode_paged(const mla_decode_args* a, void* stream) { return decode_paged(a, false, stream); }
+
+int32_t mla_decode_paged_noalloc(const mla_decode_args* a, void* stream) { return decode_paged(a, true, stream); }
 
 int32_t mla_decode_mixed_workspace_size(const mla_decode_args* sink, const mla_decode_args* middle,
                                         const mla_decode_args* recent, size_t* bytes) {

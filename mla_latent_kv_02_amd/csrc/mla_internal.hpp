@@ -139,6 +139,11 @@ struct RotateParams {
   int vec8;                 // unit stride, 16-byte-aligned groups of 8: vector path
 };
 
+// Bytes of the per-device scratch array of mla_decode_paged_noalloc, and the device address
+// of the current device's copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
