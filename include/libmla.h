@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 /* Status codes. */
 #define MLA_OK 0
@@ -277,15 +277,25 @@ int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_ne
 int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stride, int64_t n_outer,
                             int64_t outer_stride, int64_t n_inner, int64_t inner_stride, void* stream);
 
+/* Decode kernel families whose in-loop dequantisation mla_dequant_blocks runs. */
+#define MLA_DEQUANT_PARTITION 0  /* the partition and pipelined kernels (fewer than 96 query rows) */
+#define MLA_DEQUANT_ROWS 1       /* the row-owner kernel (96 query rows or more) */
+
 /*
- * mla_dequant_blocks (test/debug): materialise blocks of a paged cache as bf16.
- *   out_bf16[k][t][0:d_c] = latent of token t of block block_ids[k], [d_c:d_c+d_r] = RoPE key,
- *   for k < n_blocks, t < 64.  Uses the same device unpack/dequant code as the decode
- *   kernel, so its output is bit-identical to what the decode consumes.  F32 caches are
- *   rounded to bf16 (ties to even).  Ids outside [0, num_blocks) give zero rows.
+ * mla_dequant_blocks (test/debug): materialise blocks of a paged cache as bf16, as a decode
+ *   kernel sees them.  out_bf16[k][t][0:d_c] = latent of token t of block block_ids[k],
+ *   [d_c:d_c+d_r] = RoPE key, for k < n_blocks, t < 64.  Quantised caches (the in-attention
+ *   unpacking of the QuantMLA English abstract, arxivdaily QuantMLA page) run the chosen
+ *   family's own code: its DMA of the code planes into an LDS code stage and its dequantisation
+ *   routine into its swizzled bf16 stage, then the stage is copied out in logical order; each
+ *   element is RNE_bf16((code - zero) * scale).  Every layout the decode accepts for that
+ *   family is supported.  BF16 caches are copied (the decode streams their rows as they are);
+ *   F32 caches are rounded to bf16 (ties to even).  Ids outside [0, num_blocks) give zero
+ *   rows.  family: MLA_DEQUANT_PARTITION or MLA_DEQUANT_ROWS (ignored for float caches).
  */
 int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
-                           const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream);
+                           const int32_t* block_ids, int32_t n_blocks, int32_t family, void* out_bf16,
+                           void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* mla_status_string(int32_t status);

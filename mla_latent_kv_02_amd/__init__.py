@@ -232,8 +232,9 @@ def decode_mixed(q_lat: torch.Tensor, q_rope: torch.Tensor, sink, middle, recent
     return out, lse
 
 
-def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor) -> torch.Tensor:
-    """bf16 [n, 64, d_c + d_r] view of cache blocks, from the decode kernel's own reader."""
+def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor, family: str = "partition") -> torch.Tensor:
+    """bf16 [n, 64, d_c + d_r] view of cache blocks as a decode kernel family ('partition' or
+    'rows') dequantises them in its attention loop (its own DMA and dequant routine)."""
     _need_cuda(pool, block_ids)
     _check_pool(pool, desc, "dequant_blocks")
     if block_ids.dtype != torch.int32 or not block_ids.is_contiguous():
@@ -241,8 +242,8 @@ def dequant_blocks(pool: torch.Tensor, desc: CacheDesc, block_ids: torch.Tensor)
     n = block_ids.numel()
     out = torch.empty((n, 64, desc.d_c + desc.d_r), dtype=torch.bfloat16, device=pool.device)
     st = _lib.load().mla_dequant_blocks(ctypes.c_void_p(pool.data_ptr()), pool.shape[0], ctypes.byref(desc),
-                                        ctypes.c_void_p(block_ids.data_ptr()), n, ctypes.c_void_p(out.data_ptr()),
-                                        _stream(pool.device))
+                                        ctypes.c_void_p(block_ids.data_ptr()), n, _lib.DEQUANT_FAMILY[family],
+                                        ctypes.c_void_p(out.data_ptr()), _stream(pool.device))
     _check(st, "mla_dequant_blocks")
     return out
 

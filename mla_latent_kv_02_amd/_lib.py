@@ -13,6 +13,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "libmla.h")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, 1, 2, 3, 4
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FMT_F32, MLA_FMT_BF16, MLA_FMT_INT4, MLA_FMT_INT2 = 0, 1, 2, 3
+MLA_DEQUANT_PARTITION, MLA_DEQUANT_ROWS = 0, 1
+DEQUANT_FAMILY = {"partition": MLA_DEQUANT_PARTITION, "rows": MLA_DEQUANT_ROWS}
 FMT_BY_NAME = {"f32": MLA_FMT_F32, "bf16": MLA_FMT_BF16, "int4": MLA_FMT_INT4, "int2": MLA_FMT_INT2}
 
 
@@ -48,8 +50,8 @@ _SIGS = {
                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "mla_decode_mixed_workspace_size": (c_int32, [POINTER(DecodeArgs), POINTER(DecodeArgs), POINTER(DecodeArgs),
                                                   POINTER(c_size_t)]),
-    "mla_dequant_blocks": (c_int32, [c_void_p, c_int64, POINTER(CacheDesc), c_void_p, c_int32, c_void_p,
-                                     c_void_p]),
+    "mla_dequant_blocks": (c_int32, [c_void_p, c_int64, POINTER(CacheDesc), c_void_p, c_int32, c_int32,
+                                     c_void_p, c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,
                                 c_int64, POINTER(CacheDesc), c_void_p]),
     "mla_hadamard_rotate": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64,

@@ -652,9 +652,11 @@ int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stri
 }
 
 int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,
-                           const int32_t* block_ids, int32_t n_blocks, void* out_bf16, void* stream) {
+                           const int32_t* block_ids, int32_t n_blocks, int32_t family, void* out_bf16,
+                           void* stream) {
   Layout lay;
   if (!cache_pool || !block_ids || !out_bf16 || n_blocks <= 0 || num_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (family != MLA_DEQUANT_PARTITION && family != MLA_DEQUANT_ROWS) return MLA_ERR_INVALID_ARG;
   if (!cache_layout(desc, &lay)) return MLA_ERR_INVALID_ARG;
   if (!aligned(cache_pool, 16) || !aligned(out_bf16, 16) || !aligned(block_ids, 4)) return MLA_ERR_INVALID_ARG;
   if (desc->latent_fmt != MLA_FMT_F32 && !decode_supported(desc, MLA_BF16)) return MLA_ERR_UNSUPPORTED;
@@ -673,6 +675,8 @@ int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla
   p.ids = block_ids;
   p.n = n_blocks;
   p.out = (uint16_t*)out_bf16;
+  p.family = family;
+  if ((int64_t)n_blocks * 2 > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
   return hip_status(mla::launch_dequant(p, desc->latent_fmt, (hipStream_t)stream));
 }
 

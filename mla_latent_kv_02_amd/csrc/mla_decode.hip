@@ -961,6 +961,50 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// The in-loop dequantisation of the kernels above, on its own (test/debug): one workgroup per
+// half block streams the code planes into a code stage with the decode's DMA producer,
+// dequantises them with the decode's own QuantProducer::dequant into a swizzled bf16 stage,
+// and copies the stage out un-swizzled.  Block ids outside the pool give zero rows, as the
+// decode's zero scales for them do.
+// ---------------------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(NT) void dequant_stage_kernel(DequantParams p) {
+  using QP = QuantProducer<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t cst[QP::SLOTS * 16];
+  __shared__ __attribute__((aligned(16))) bf16_t stage[ST_ELEMS];
+  const int tid = threadIdx.x;
+  const int k = blockIdx.x >> 1, half = blockIdx.x & 1;
+  int id = p.ids[k], valid = ST_TOK;
+  if (id < 0 || (int64_t)id >= p.num_blocks) {
+    id = 0;
+    valid = 0;
+  }
+  id = __builtin_amdgcn_readfirstlane(id);
+  valid = __builtin_amdgcn_readfirstlane(valid);
+  const QuantPlanes pl{(int)p.off_lc, (int)p.off_ls, (int)p.off_rc, (int)p.off_rs};
+  QP::issue(p.pool + (size_t)id * (size_t)p.block_bytes, half, pl, 512 / p.g_lat, 64 / p.g_rope, cst, tid);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  QP::dequant(cst, valid, 31 - __builtin_clz(p.g_lat), 31 - __builtin_clz(p.g_rope), stage, tid);
+  lds_barrier();
+  uint16_t* out = p.out + ((size_t)k * BLOCK_TOKENS + half * ST_TOK) * 576;
+  for (int q = tid; q < ST_TOK * 72; q += NT) {
+    const int t = q / 72, c8 = q % 72;
+    *(u32x4*)(out + t * 576 + c8 * 8) = *(const u32x4*)&stage[st_off(t, c8 * 8)];
+  }
+}
+
+hipError_t launch_dequant_partition(const DequantParams& p, int fmt, hipStream_t st) {
+  if (fmt == FMT_INT4)
+    hipLaunchKernelGGL(dequant_stage_kernel<FMT_INT4>, dim3(2 * p.n), dim3(NT), 0, st, p);
+  else if (fmt == FMT_INT2)
+    hipLaunchKernelGGL(dequant_stage_kernel<FMT_INT2>, dim3(2 * p.n), dim3(NT), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------
 template <int RT, int FMT>

@@ -906,6 +906,41 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   }
 }
 
+// The in-loop dequantisation of this kernel on its own (test/debug): one workgroup per half
+// block streams the code planes with QuantStage's DMA (the same per-lane offsets), dequantises
+// them with QuantStage::dequant into a bf16 stage of this kernel's swizzle, and copies the
+// stage out un-swizzled.  Block ids outside the pool give zero rows (zero scales).
+template <int FMT>
+__global__ __launch_bounds__(NT) void dequant_stage_rows_kernel(DequantParams p) {
+  using QS = QuantStage<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t cst[QS::SLOTS * 16];
+  __shared__ __attribute__((aligned(16))) bf16_t stage[ST_ELEMS];
+  const int tid = threadIdx.x;
+  const int k = blockIdx.x >> 1, half = blockIdx.x & 1;
+  int id = p.ids[k], valid = ST_TOK;
+  if (id < 0 || (int64_t)id >= p.num_blocks) {
+    id = 0;
+    valid = 0;
+  }
+  id = __builtin_amdgcn_readfirstlane(id);
+  valid = __builtin_amdgcn_readfirstlane(valid);
+  const QuantPlanes pl{(int)p.off_lc, (int)p.off_ls, (int)p.off_rc, (int)p.off_rs};
+  const auto offs = QS::offsets(pl, 512 / p.g_lat, 64 / p.g_rope, tid);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(cst) + (tid & ~63) * 16);
+  const uint8_t* blk = p.pool + (size_t)id * (size_t)p.block_bytes;
+#pragma unroll
+  for (int i = 0; i < QS::LOADS; ++i) QS::issue_one(i, offs, blk, half, lds);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  QS::dequant(cst, valid, 31 - __builtin_clz(p.g_lat), 31 - __builtin_clz(p.g_rope), stage, tid);
+  lds_barrier();
+  uint16_t* out = p.out + ((size_t)k * BLOCK_TOKENS + half * ST_TOK) * 576;
+  for (int q = tid; q < ST_TOK * 72; q += NT) {
+    const int t = q / 72, c8 = q % 72;
+    *(u32x4*)(out + t * 576 + c8 * 8) = *(const u32x4*)&stage[rst_off(t, c8 * 8)];
+  }
+}
+
 template <int FMT>
 static hipError_t launch_fmt(const RowsParams& p, hipStream_t st) {
   const int grid = 8 * p.units_per_xcd;
@@ -917,6 +952,16 @@ static hipError_t launch_fmt(const RowsParams& p, hipStream_t st) {
 }
 
 }  // namespace rows
+
+hipError_t launch_dequant_rows(const DequantParams& p, int fmt, hipStream_t st) {
+  if (fmt == FMT_INT4)
+    hipLaunchKernelGGL(rows::dequant_stage_rows_kernel<FMT_INT4>, dim3(2 * p.n), dim3(rows::NT), 0, st, p);
+  else if (fmt == FMT_INT2)
+    hipLaunchKernelGGL(rows::dequant_stage_rows_kernel<FMT_INT2>, dim3(2 * p.n), dim3(rows::NT), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st) {
   switch (fmt) {

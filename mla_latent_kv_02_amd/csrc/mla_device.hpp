@@ -1,12 +1,9 @@
 // Device-side building blocks shared by the libmla kernels (gfx950 / CDNA4).
 //
 // - vector types for the bf16 MFMA operands,
-// - round-to-nearest-even fp32 -> bf16,
-// - the cache-tile reader: loads one 64-token block of a paged cache into
-//   registers (bf16 rows, or INT4/INT2 codes with their fp16 scale/zero) and
-//   later emits it as bf16 8-element pieces, dequantising codes on the way.
-//   The decode kernel and the mla_dequant_blocks kernel both use this reader,
-//   so what the debug entry point returns is exactly what attention consumes.
+// - round-to-nearest-even fp32 -> bf16, and the two-term bf16 split of softmax weights,
+// - the element-wise dequantisation of INT4 / INT2 codes that every decode kernel's
+//   in-loop dequant routine (QuantProducer::dequant_task, rows::QuantStage) is built from.
 //
 // Dequantisation (QuantMLA: unpack and dequantise inside attention): a code q
 // of group (scale s, integer zero-point z) becomes RNE_bf16((q - z) * s).  With
@@ -127,147 +124,5 @@ __device__ __forceinline__ void scale_zero(uint32_t sz, float& s, float& zs) {
 struct QuantPlanes {
   int32_t lc, ls, rc, rs;
 };
-
-// --------------------------------------------------------------------------------------
-// Tile reader.  NT threads cooperate on one 64-token block of d_c = 512, d_r = 64.
-// load(): issue the global loads into registers (tokens >= valid are not read).
-// emit(f): call f(token, col8, u32x4 bf16x8) for every 8-element piece of the block, in
-//          the latent-then-rope column order (col8 in 0..71), zeros for tokens >= valid.
-// --------------------------------------------------------------------------------------
-template <int FMT, int NT>
-struct TileReader;
-
-// bf16 rows [c(512) | k_rope(64)] = 72 pieces of 16 bytes per token, 4608 per block.
-template <int NT>
-struct TileReader<FMT_BF16, NT> {
-  static constexpr int PIECES = BLOCK_TOKENS * 72;
-  static constexpr int PER = PIECES / NT;
-  static_assert(PIECES % NT == 0, "thread count must divide the block");
-  u32x4 v[PER];
-
-  __device__ __forceinline__ void load(const uint8_t* blk, int valid, int tid, const QuantPlanes&, int, int) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      int p = tid + k * NT;
-      int tok = p / 72;
-      if (tok < valid) {
-        v[k] = __builtin_nontemporal_load((const u32x4*)(blk + (size_t)p * 16));
-      } else {
-        v[k] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  template <class F>
-  __device__ __forceinline__ void emit(F&& f, int valid, int tid) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      int p = tid + k * NT;
-      f(p / 72, p % 72, v[k]);
-    }
-  }
-};
-
-// Quantised latent (INT4 or INT2) + INT4 RoPE key.
-// Latent codes are read 16 bytes at a time: 32 INT4 or 64 INT2 elements per piece.
-template <int FMT, int NT>
-struct QuantTileReader {
-  static constexpr int BITS = FMT == FMT_INT4 ? 4 : 2;
-  static constexpr int LAT_BYTES = 512 * BITS / 8;              // per token
-  static constexpr int LAT_PIECES = BLOCK_TOKENS * LAT_BYTES / 16;
-  static constexpr int ELEMS = 128 / BITS;                       // elements per 16-byte piece
-  static constexpr int PIECES_PER_TOK = LAT_BYTES / 16;
-  static constexpr int PER = LAT_PIECES / NT;
-  static constexpr int ROPE_PIECES = BLOCK_TOKENS * 2;           // 64 INT4 codes = 2 pieces/token
-  static_assert(LAT_PIECES % NT == 0, "thread count must divide the latent plane");
-  static_assert(ROPE_PIECES <= NT, "one rope piece per thread at most");
-  u32x4 c[PER];
-  uint32_t sz[PER][2];   // (scale, zero) words for the piece's first and second half
-  u32x4 rc;
-  uint32_t rsz;
-
-  __device__ __forceinline__ void load(const uint8_t* blk, int valid, int tid, const QuantPlanes& pl,
-                                       int g_lat, int g_rope) {
-    const int groups = 512 / g_lat;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      int p = tid + k * NT;
-      int tok = p / PIECES_PER_TOK;
-      int e0 = (p % PIECES_PER_TOK) * ELEMS;
-      if (tok < valid) {
-        c[k] = __builtin_nontemporal_load((const u32x4*)(blk + pl.lc + (size_t)p * 16));
-        const uint32_t* szp = (const uint32_t*)(blk + pl.ls) + tok * groups;
-        sz[k][0] = szp[e0 / g_lat];
-        sz[k][1] = szp[(e0 + ELEMS / 2) / g_lat];
-      } else {
-        c[k] = u32x4{0, 0, 0, 0};
-        sz[k][0] = sz[k][1] = 0;
-      }
-    }
-    if (tid < ROPE_PIECES) {
-      int tok = tid >> 1;
-      if (tok < valid) {
-        rc = __builtin_nontemporal_load((const u32x4*)(blk + pl.rc + (size_t)tid * 16));
-        const uint32_t* szp = (const uint32_t*)(blk + pl.rs) + tok * (64 / g_rope);
-        rsz = szp[((tid & 1) * 32) / g_rope];
-      } else {
-        rc = u32x4{0, 0, 0, 0};
-        rsz = 0;
-      }
-    }
-  }
-
-  template <class F>
-  __device__ __forceinline__ void emit(F&& f, int valid, int tid) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      int p = tid + k * NT;
-      int tok = p / PIECES_PER_TOK;
-      int col8 = (p % PIECES_PER_TOK) * (ELEMS / 8);
-      if (tok >= valid) {
-#pragma unroll
-        for (int j = 0; j < ELEMS / 8; ++j) f(tok, col8 + j, u32x4{0, 0, 0, 0});
-        continue;
-      }
-      float s0, zs0, s1, zs1;
-      scale_zero(sz[k][0], s0, zs0);
-      scale_zero(sz[k][1], s1, zs1);
-      if (BITS == 4) {
-        // 4 words x 8 codes; first two words in the first half of the piece
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f(tok, col8 + j, dequant_int4x8(c[k][j], j < 2 ? s0 : s1, j < 2 ? zs0 : zs1));
-      } else {
-        // 4 words x 16 codes; each word gives two 8-element pieces
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float s = j < 2 ? s0 : s1, zs = j < 2 ? zs0 : zs1;
-          uint32_t t_lo, t_hi;
-          int2_table(s, zs, t_lo, t_hi);
-          u32x4 lo, hi;
-          dequant_int2x16(c[k][j], t_lo, t_hi, lo, hi);
-          f(tok, col8 + 2 * j, lo);
-          f(tok, col8 + 2 * j + 1, hi);
-        }
-      }
-    }
-    if (tid < ROPE_PIECES) {
-      int tok = tid >> 1;
-      int col8 = 64 + (tid & 1) * 4;
-      if (tok >= valid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f(tok, col8 + j, u32x4{0, 0, 0, 0});
-      } else {
-        float s, zs;
-        scale_zero(rsz, s, zs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f(tok, col8 + j, dequant_int4x8(rc[j], s, zs));
-      }
-    }
-  }
-};
-
-template <int NT>
-struct TileReader<FMT_INT4, NT> : QuantTileReader<FMT_INT4, NT> {};
-template <int NT>
-struct TileReader<FMT_INT2, NT> : QuantTileReader<FMT_INT2, NT> {};
 
 }  // namespace mla

@@ -105,6 +105,7 @@ struct DequantParams {
   const int32_t* ids;
   int n;
   uint16_t* out;            // [n][64][d_c + d_r] bf16 bits
+  int family;               // quantised caches: MLA_DEQUANT_PARTITION or MLA_DEQUANT_ROWS
 };
 
 // Cache writer: token i (of n) goes to slot slots[i] = block * 64 + position; slots outside
@@ -150,6 +151,8 @@ hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
+hipError_t launch_dequant_partition(const DequantParams& p, int fmt, hipStream_t st);
+hipError_t launch_dequant_rows(const DequantParams& p, int fmt, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, hipStream_t st);
 hipError_t launch_rotate(const RotateParams& p, hipStream_t st);
 

@@ -17,7 +17,7 @@ def test_library_exports_every_header_function():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.mla_abi_version() == 1
+    assert L.mla_abi_version() == 2
 
 
 def test_block_layout_matches_generator_and_survey_sizes():
@@ -130,10 +130,11 @@ def test_projection_and_dequant_validation():
     assert L.mla_absorb_q(FAKE, 0, 0, 1, FAKE, 1, FAKE, 1, 0, 1, 128, 512, None) == 1
     assert L.mla_out_proj(FAKE, 0, 0, 9, FAKE, 1, FAKE, 1, 1, 1, 512, 128, None) == 1
     d = mla.cache_desc(512, 64, "int4", "int4", 64, 64)
-    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), None, 1, FAKE, None) == 1
-    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), FAKE, 0, FAKE, None) == 1
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), None, 1, 0, FAKE, None) == 1
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), FAKE, 0, 0, FAKE, None) == 1
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d), FAKE, 1, 2, FAKE, None) == 1   # no such family
     d2 = mla.cache_desc(256, 64, "int4", "int4", 64, 64)
-    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d2), FAKE, 1, FAKE, None) == 2
+    assert L.mla_dequant_blocks(FAKE, 10, ctypes.byref(d2), FAKE, 1, 0, FAKE, None) == 2
 
 
 def test_status_strings():

@@ -62,14 +62,16 @@ def _decode_stage(m, x, num_splits=0, o_dtype=torch.float32):
 
 # ------------------------------------------------------------------------------------ dequant
 
+@pytest.mark.parametrize("family", ["partition", "rows"])
 @pytest.mark.parametrize("name", ["2", "4", "5"])
-def test_dequant_blocks_bit_exact(mla, name):
+def test_dequant_blocks_bit_exact(mla, name, family):
+    """Both decode families' own in-loop dequantisation, bit for bit against the oracle."""
     cfg = CONFIGS[name]
     x = make_inputs(cfg, 31, lens=[1, 63, 64, 65, 200], H=2)
-    _say("dequant_blocks", name)
+    _say("dequant_blocks", name, family)
     t = to_device(x)
     ids = torch.from_numpy(x.block_table.reshape(-1).copy()).to(dev())
-    got = mla.dequant_blocks(t["pool"], desc_of(cfg), ids).view(torch.int16).cpu().numpy().view(np.uint16)
+    got = mla.dequant_blocks(t["pool"], desc_of(cfg), ids, family).view(torch.int16).cpu().numpy().view(np.uint16)
     torch.cuda.synchronize()
     c, k = logical_cache(x)
     nb = x.block_table.shape[1]
@@ -80,9 +82,11 @@ def test_dequant_blocks_bit_exact(mla, name):
         np.testing.assert_array_equal(blk, ref_bits)
 
 
+@pytest.mark.parametrize("family", ["partition", "rows"])
 @pytest.mark.parametrize("fmt,bits,group", [("int4", 4, 64), ("int2", 2, 32), ("int4", 4, 32), ("int2", 2, 64)])
-def test_dequant_every_code_zero_and_scale(mla, fmt, bits, group):
-    """Every code x every zero-point x fp16 scales (subnormal .. max) through the GPU reader."""
+def test_dequant_every_code_zero_and_scale(mla, fmt, bits, group, family):
+    """Every code x every zero-point x fp16 scales (subnormal .. max) through each decode
+    family's in-loop dequantisation."""
     qmax = 2 ** bits - 1
     d_c, d_r = 512, 64
     ng = d_c // group
@@ -109,9 +113,9 @@ def test_dequant_every_code_zero_and_scale(mla, fmt, bits, group):
         pool[blk, off[1]:off[1] + 64 * ng * 4] = sz[sl].view(np.uint8).reshape(-1)
         pool[blk, off[2]:off[2] + 64 * 32] = pack_codes(rcodes[sl], 4).reshape(-1)
         pool[blk, off[3]:off[3] + 64 * 4] = rsz[sl].view(np.uint8).reshape(-1)
-    _say("dequant every code", fmt, group)
+    _say("dequant every code", fmt, group, family)
     got = mla.dequant_blocks(torch.from_numpy(pool).to(dev()), desc,
-                             torch.arange(4, dtype=torch.int32, device=dev()))
+                             torch.arange(4, dtype=torch.int32, device=dev()), family)
     got = got.view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, d_c + d_r)
     ref = np.concatenate([oracle.dequant(codes, sz, group), oracle.dequant(rcodes, rsz, 64)], axis=1)
     ref_bits = (ref.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
