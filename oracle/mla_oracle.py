@@ -30,6 +30,10 @@ What it computes, and where the pages fix it:
   the pages pair an INT4 or INT2 latent with an INT4 RoPE key and name
   round-to-nearest as the plain quantiser: QuantMLA abstract and podcast page).
 
+* GQLA's second decode path (``group_weights``, ``expand_groups``, ``attend_groups``): with
+  head groups sharing their key/value up-projections, the latent is expanded once per group
+  and decoded as grouped-query attention (GQLA abstract, thelatestinai.com paper-cards page).
+
 * A fixed orthogonal rotation of the latent (``hadamard``, ``rotate``,
   ``fold_rotation``) folded into W_UK and W_UV leaves every full-precision result
   unchanged and spreads outlier channels before quantisation (fixed rotations
@@ -365,6 +369,72 @@ def decode_absorbed(q_nope, q_rope, w_uk, w_uv, c, k_rope, seq_lens, s_q: int, s
     return {"q_lat": q_lat, "o_lat": o_lat, "lse": lse, "out": out_proj(o_lat, w_uv)}
 
 
+# --------------------------------------------------------------------------- GQLA per-group path
+#
+# GQLA (GQLA abstract, thelatestinai.com paper-cards page) modifies MLA so that the same
+# weights expose two algebraically equivalent decode paths: the absorbed MQA path above and a
+# GQA path over a per-group expanded cache.  Reading (the abstract gives no formula): the H heads
+# form G groups of H/G consecutive heads, and the heads of a group share their key and value
+# up-projections, W_UK[h] = W_UK^g and W_UV[h] = W_UV^g for g = h // (H/G).  The GQA path then
+# expands the cached latent once per group, k_nope_g = W_UK^g c and v_g = c W_UV^g, next to the
+# shared RoPE key, and decodes as grouped-query attention with G key/value heads.
+
+def group_weights(w_g: np.ndarray, H: int) -> np.ndarray:
+    """Per-head weights of a model whose G groups of H/G consecutive heads share one matrix:
+    W[h] = W_g[h // (H/G)].  w_g [G, ...] -> [H, ...]."""
+    w_g = np.asarray(w_g)
+    G = w_g.shape[0]
+    if H % G:
+        raise ValueError("the head count must be a multiple of the group count")
+    return np.repeat(w_g, H // G, axis=0)
+
+
+def expand_groups(c: np.ndarray, w_uk_g: np.ndarray, w_uv_g: np.ndarray):
+    """The per-group expanded cache of one sequence's latent c [L, d_c]: keys k_nope[g] =
+    c W_UK^g^T [L, d_n] and values v[g] = c W_UV^g [L, d_v] for every group (float64).
+    w_uk_g [G, d_n, d_c], w_uv_g [G, d_c, d_v].  Returns (k_nope [G, L, d_n], v [G, L, d_v])."""
+    c = np.asarray(c, np.float64)
+    w_uk_g = np.asarray(w_uk_g, np.float64)
+    w_uv_g = np.asarray(w_uv_g, np.float64)
+    k = np.stack([c @ w_uk_g[g].T for g in range(w_uk_g.shape[0])])
+    v = np.stack([c @ w_uv_g[g] for g in range(w_uv_g.shape[0])])
+    return k, v
+
+
+def attend_groups(q_nope, q_rope, k_nope, k_rope, v, seq_lens, s_q: int, sm_scale: float,
+                  rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Grouped-query attention over per-group caches (the GQLA GQA decode).
+
+    Head h belongs to group g = h // (H/G) and, for query i of sequence b, attends tokens
+    t <= L - s_q + i with s_t = sm_scale (q_nope[b,i,h] . k_nope[b][g, t] + q_rope[b,i,h] .
+    k_rope[b][t]); out = softmax(s) @ v[b][g], lse = log-sum-exp of s.
+    q_nope [B, s_q, H, d_n], q_rope [B, s_q, H, d_r]; per sequence k_nope[b] [G, L, d_n],
+    k_rope[b] [L, d_r], v[b] [G, L, d_v].  Returns out [B, s_q, H, d_v], lse [B, s_q, H].
+    """
+    q_nope = np.asarray(q_nope, np.float64)
+    q_rope = np.asarray(q_rope, np.float64)
+    B, S, H, _ = q_nope.shape
+    G = np.asarray(k_nope[0]).shape[0]
+    d_v = np.asarray(v[0]).shape[-1]
+    out = np.full((B, S, H, d_v), np.nan)
+    lse = np.full((B, S, H), np.nan)
+    sel = None if rows is None else set(rows)
+    for b in range(B):
+        L = int(seq_lens[b])
+        kn = np.asarray(k_nope[b], np.float64)[:, :L]
+        kr = np.asarray(k_rope[b], np.float64)[:L]
+        vb = np.asarray(v[b], np.float64)[:, :L]
+        for h in range(H):
+            g = h // (H // G)
+            for i in range(S):
+                if sel is not None and (b, i, h) not in sel:
+                    continue
+                n = L - s_q + i + 1
+                s = sm_scale * (kn[g, :n] @ q_nope[b, i, h] + kr[:n] @ q_rope[b, i, h])
+                out[b, i, h], lse[b, i, h] = _softmax_attend(s, vb[g, :n])
+    return out, lse
+
+
 def merge_partials(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
     """Combine attention results over disjoint token subsets: lse = log sum exp(lse_u),
     o = sum_u exp(lse_u - lse) o_u.  Parts with lse = -inf contribute nothing."""
@@ -412,4 +482,5 @@ __all__ = ["bf16_round", "unpack_codes", "pack_codes_bytes", "write_tokens", "ha
            "dequant", "quantise_rtn",
            "token_bytes", "block_planes",
            "read_pool", "absorb_q", "out_proj", "attend_latent", "decode_unabsorbed", "decode_absorbed",
-           "merge_partials", "dequant_cache", "exact_dequant_value"]
+           "merge_partials", "dequant_cache", "exact_dequant_value", "group_weights", "expand_groups",
+           "attend_groups"]
