@@ -32,7 +32,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode cached-token·heads/s, HBM TB/s + MFMA util, µs/decode step"
 UNIT = "cached-token·heads/s"
 WORKLOADS = {"tiny-f32": "1", "v2lite-bf16": "2", "v3-bf16-sq1": "3", "v3-bf16-sq2": "3b",
-             "v2lite-int4-32k": "4", "v3-int2-128k": "5"}
+             "v2lite-int4-32k": "4", "v3-int2-128k": "5", "v3-gqa-sq2": "3b"}
+# GQLA's per-group GQA path on the V3 batch with two query tokens: head groups sharing their
+# key/value up-projections, the latent expanded per group
+GQA_GROUPS = {"v3-gqa-sq2": 8}
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 KERNEL_SOURCES = ["mla_latent_kv_02_amd/csrc/mla_decode.hip", "mla_latent_kv_02_amd/csrc/mla_decode_rows.hip",
@@ -117,6 +120,88 @@ def cpu_baseline(x, seconds: float):
             "seconds": round(t_used, 2)}
 
 
+def bench_gqa(args, x, cfg, G, dev):
+    """GQLA's GQA decode path: the batch's latent expanded per group (mla_gqa_expand, group g
+    taking head g's W_UK / W_UV), then grouped-query attention over the expanded cache
+    (mla_gqa_decode_paged), timed like the MLA decode.  Output is already in value space."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_02_amd as mla
+    B, s_q, H = len(x.seq_lens), cfg.s_q, cfg.H
+    L = x.seq_lens
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(dev)  # noqa: E731
+    w_uk_g, w_uv_g = bf(x.w_uk[:G]), bf(x.w_uv[:G])
+    nb = x.pool.shape[0]
+    bb = mla.gqa_block_bytes(G)
+    rotate = args.rotate or max(2, math.ceil(512e6 / (nb * bb)) + 1)
+    bt = torch.from_numpy(x.block_table).to(dev)
+    sl = torch.from_numpy(L).to(dev)
+    pos = np.concatenate([np.arange(Lb) for Lb in L])
+    seq = np.repeat(np.arange(B), L)
+    slots = torch.from_numpy((x.block_table[seq, pos // 64].astype("int64") * 64 + pos % 64).astype("int32")).to(dev)
+    rows = bf(np.concatenate([x.c[b, :Lb] for b, Lb in enumerate(L)]))
+    krows = bf(np.concatenate([x.k_rope[b, :Lb] for b, Lb in enumerate(L)]))
+    pools = []
+    for _ in range(rotate):
+        gp = torch.zeros((nb, bb), dtype=torch.uint8, device=dev)
+        mla.gqa_expand(rows, krows, w_uk_g, w_uv_g, gp, slots)
+        pools.append(gp)
+    torch.cuda.synchronize()
+    del rows, krows
+    qn, qr = bf(x.q_nope), bf(x.q_rope)
+    max_len, total_len = int(L.max()), int(L.astype("int64").sum())
+    out = torch.empty((B, s_q, H, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=dev)
+    mla.gqa_decode_paged(qn, qr, pools[0], G, bt, sl, max_len, cfg.sm_scale, args.num_splits, out=out, lse=lse,
+                         total_seq_len=total_len)
+    a = mla._gqa_args(qn, qr, pools[0], G, bt, sl, max_len, cfg.sm_scale, args.num_splits, out, lse, None, total_len)
+    import ctypes
+    n = ctypes.c_size_t()
+    mla._check(mla.lib().mla_gqa_workspace_size(ctypes.byref(a), ctypes.byref(n)), "mla_gqa_workspace_size")
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    call = lambda i: mla.gqa_decode_paged(qn, qr, pools[i % rotate], G, bt, sl, max_len, cfg.sm_scale,  # noqa: E731
+                                          args.num_splits, out=out, lse=lse, workspace=ws, total_seq_len=total_len)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream(dev)
+    reps = rotate * max(1, math.ceil(8 / rotate))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    replays = max(2, math.ceil(K / reps))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(replays):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * reps)
+    Ll = L.astype("int64")
+    cache_bytes = int(Ll.sum()) * (G * 512 + 128)
+    io_bytes = B * s_q * H * ((128 + 64) * 2 + 128 * 4 + 4)
+    attended = sum(int((Ll - s_q + i + 1).sum()) for i in range(s_q))
+    flops = attended * H * 2 * (192 + 128)
+    units = attended * H
+    gbs = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "mla_gqa_decode_paged (gqa_decode_kernel + combine_kernel)",
+            "algorithmic_bytes_per_launch": cache_bytes + io_bytes, "flops_per_launch": flops, "traffic": None}
+    return {"metric": METRIC, "value": units / (ms * 1e-3), "unit": UNIT, "n_gpus": 1, "steps": replays * reps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": args.workload, "batch": B, "heads": H, "groups": G, "s_q": s_q, "d_n": 128,
+                       "d_v": 128, "d_r": 64, "cache": "bf16 per-group expanded",
+                       "mean_seq_len": float(L.mean()), "block_tokens": 64, "pool_copies_rotated": rotate},
+            "roofline": roof, "us_per_step": round(ms * 1e3, 2), "decode_us": round(ms * 1e3, 2),
+            "step_launch": "hip_graph", "hbm_tbps": round(gbs / 1e3, 3), "cache_bytes": cache_bytes,
+            "note": "a step is the GQA path's whole decode: no absorption or up-projection on this path"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -139,6 +224,11 @@ def main():
     log(f"generating {args.workload} inputs")
     x = make_inputs(cfg, SEEDS[name])
     log("inputs ready; uploading")
+    if args.workload in GQA_GROUPS:
+        rec = bench_gqa(args, x, cfg, GQA_GROUPS[args.workload], dev)
+        log(f"gqa decode {rec['decode_us']:.2f} us")
+        print(json.dumps(rec), flush=True)
+        return
     desc = mla.cache_desc(cfg.d_c, cfg.d_r, cfg.latent_fmt, cfg.rope_fmt, cfg.latent_group, cfg.rope_group)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     pool_bytes = x.pool.nbytes

@@ -297,6 +297,72 @@ int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla
                            const int32_t* block_ids, int32_t n_blocks, int32_t family, void* out_bf16,
                            void* stream);
 
+/*
+ * GQLA per-group path (GQLA abstract, thelatestinai.com paper-cards page).  GQLA ties the H heads
+ * of each of num_groups groups (H / num_groups consecutive heads) to one key and one value
+ * up-projection, W_UK^g [d_n][d_c] and W_UV^g [d_c][d_v], so the same weights decode two
+ * algebraically equivalent ways: the absorbed MQA path above (with W_UK[h] = W_UK^g, W_UV[h] =
+ * W_UV^g for g = h / (H / num_groups)), or grouped-query attention over a per-group expanded
+ * cache, chosen per hardware.  On the GQA path the output is already in value space: no
+ * absorption and no up-projection.
+ *
+ * Expanded cache, paged in blocks of 64 tokens: num_groups planes [64][k_nope (d_n) | v (d_v)]
+ * bf16, then one RoPE-key plane [64][d_r] bf16 shared by the groups.  Kernels exist for
+ * d_n = d_v = 128, d_r = 64 (the DeepSeek shapes); other widths give MLA_ERR_UNSUPPORTED.
+ */
+
+/* Bytes of one expanded block, or -1 if a size is not positive. */
+int64_t mla_gqa_block_bytes(int32_t num_groups, int32_t d_n, int32_t d_v, int32_t d_r);
+
+/*
+ * mla_gqa_expand: write n new tokens into the expanded cache.  For token i (latent
+ *   c_new[i * c_stride + 0 .. d_c), RoPE key k_rope_new[i * k_stride + 0 .. d_r), both bf16, the
+ *   latent as the MLA cache holds it) and every group g, slot slots[i] = block * 64 + position
+ *   receives k_nope_g = RNE_bf16(W_UK^g c) and v_g = RNE_bf16(c W_UV^g) (fp32 accumulation) in
+ *   plane g, and the RoPE key in the shared plane.  w_uk_g [num_groups][d_n][d_c] and
+ *   w_uv_g [num_groups][d_c][d_v] bf16.  c_new, k_rope_new, the weights and the pool 16-byte
+ *   aligned, strides multiples of 8 elements, d_c a multiple of 32.  Slots outside
+ *   [0, num_blocks * 64) are skipped; n = 0 is a no-op.
+ */
+int32_t mla_gqa_expand(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,
+                       const void* w_uk_g, const void* w_uv_g, int32_t num_groups, int32_t d_c, int32_t d_n,
+                       int32_t d_v, int32_t d_r, const int32_t* slots, int64_t n, void* cache_pool,
+                       int64_t num_blocks, void* stream);
+
+/* Arguments of mla_gqa_decode_paged (device pointers except the struct itself). */
+typedef struct mla_gqa_args {
+  const void* q_nope;         /* [batch][s_q][H][d_n] bf16, 16-byte aligned */
+  const void* q_rope;         /* [batch][s_q][H][d_r] bf16, already rotated */
+  const void* cache_pool;     /* num_blocks expanded blocks, 16-byte aligned */
+  int64_t num_blocks;
+  int32_t num_groups, d_n, d_v, d_r;
+  const int32_t* block_table; /* [batch][block_table_stride] */
+  int32_t block_table_stride; /* >= ceil(max_seq_len / 64) */
+  const int32_t* seq_lens;    /* [batch], each in [s_q, max_seq_len]; counts the s_q new tokens */
+  int32_t max_seq_len;
+  int64_t total_seq_len;      /* optional host-side sum of seq_lens (0 = unknown) */
+  int32_t batch, s_q, num_heads;
+  float sm_scale;
+  int32_t num_splits;         /* context partitions per longest sequence, 0 = automatic */
+  float* out;                 /* [batch][s_q][H][d_v] fp32 */
+  float* lse;                 /* [batch][s_q][H] natural-log LSE, or NULL */
+  void* workspace;            /* >= mla_gqa_workspace_size() bytes, 256-byte aligned, scratch */
+  size_t workspace_bytes;
+} mla_gqa_args;
+
+/* Workspace for the split partials of mla_gqa_decode_paged (0 when the plan needs no split). */
+int32_t mla_gqa_workspace_size(const mla_gqa_args* args, size_t* bytes);
+
+/*
+ * mla_gqa_decode_paged: grouped-query attention over the expanded cache.  Head h is in group
+ *   g = h / (H / num_groups); its query i of sequence b attends tokens t <= L_b - s_q + i with
+ *   s_t = sm_scale (q_nope . k_nope_g[t] + q_rope . k_rope[t]):  out = softmax(s) . v_g,
+ *   lse = log sum_t exp(s_t).  s_q in {1, 2} (causal within the pair); num_groups divides H and
+ *   s_q * H / num_groups <= 64.  Block-table entries outside the pool take no part; a sequence
+ *   of length 0 gets out = 0 and lse = -inf.  Deterministic for fixed arguments.
+ */
+int32_t mla_gqa_decode_paged(const mla_gqa_args* args, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mla_status_string(int32_t status);
 

@@ -20,7 +20,7 @@ from ._lib import (MLA_BF16, MLA_F32, MLA_FMT_BF16, MLA_FMT_F32, MLA_FMT_INT2, M
 
 __all__ = ["MlaError", "cache_desc", "block_bytes", "plane_offsets", "absorb_q", "decode_paged", "out_proj",
            "decode_mixed", "dequant_blocks", "append_kv", "hadamard_rotate", "decode_workspace_size",
-           "decode_plan", "DecodeStep", "lib"]
+           "decode_plan", "DecodeStep", "gqa_block_bytes", "gqa_expand", "gqa_decode_paged", "lib"]
 
 
 class MlaError(RuntimeError):
@@ -273,6 +273,101 @@ def append_kv(c_new: torch.Tensor, k_rope_new: torch.Tensor, pool: torch.Tensor,
                                    ctypes.c_void_p(slots.data_ptr()), n, ctypes.c_void_p(pool.data_ptr()),
                                    pool.shape[0], ctypes.byref(desc), _stream(pool.device))
     _check(st, "mla_append_kv")
+
+
+def gqa_block_bytes(num_groups: int, d_n: int = 128, d_v: int = 128, d_r: int = 64) -> int:
+    """Bytes of one 64-token block of the GQLA per-group expanded cache."""
+    return int(_lib.load().mla_gqa_block_bytes(num_groups, d_n, d_v, d_r))
+
+
+def gqa_expand(c_new: torch.Tensor, k_rope_new: torch.Tensor, w_uk_g: torch.Tensor, w_uv_g: torch.Tensor,
+               pool: torch.Tensor, slots: torch.Tensor) -> None:
+    """Write n new tokens into the per-group expanded cache: c_new [n, d_c] and k_rope_new [n, d_r]
+    bf16 (rows may be strided), w_uk_g [G, d_n, d_c], w_uv_g [G, d_c, d_v] bf16, slots int32 [n]
+    (block * 64 + position; outside the pool = skip).  pool [num_blocks, block_bytes] uint8."""
+    _need_cuda(c_new, k_rope_new, w_uk_g, w_uv_g, pool, slots)
+    G, d_n, d_c = w_uk_g.shape
+    d_v = w_uv_g.shape[2]
+    d_r = k_rope_new.shape[1]
+    if w_uv_g.shape[:2] != (G, d_c) or c_new.dim() != 2 or c_new.shape[1] != d_c:
+        raise ValueError("gqa_expand: c_new [n, d_c], w_uk_g [G, d_n, d_c] and w_uv_g [G, d_c, d_v] expected")
+    if c_new.shape[0] != k_rope_new.shape[0] or slots.numel() != c_new.shape[0]:
+        raise ValueError("gqa_expand: one slot and one RoPE key per token")
+    for t in (c_new, k_rope_new, w_uk_g, w_uv_g):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("gqa_expand: bf16 inputs")
+    if c_new.stride(1) != 1 or k_rope_new.stride(1) != 1 or not w_uk_g.is_contiguous() or not w_uv_g.is_contiguous():
+        raise ValueError("gqa_expand: rows and weights must be dense")
+    if slots.dtype != torch.int32 or not slots.is_contiguous():
+        raise ValueError("gqa_expand: slots must be dense int32")
+    bb = gqa_block_bytes(G, d_n, d_v, d_r)
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or not pool.is_contiguous() or pool.shape[1] != bb:
+        raise ValueError(f"gqa_expand: pool must be a dense uint8 [num_blocks, {bb}] tensor")
+    n = c_new.shape[0]
+    st = _lib.load().mla_gqa_expand(ctypes.c_void_p(c_new.data_ptr()), c_new.stride(0) if n > 1 else d_c,
+                                    ctypes.c_void_p(k_rope_new.data_ptr()), k_rope_new.stride(0) if n > 1 else d_r,
+                                    ctypes.c_void_p(w_uk_g.data_ptr()), ctypes.c_void_p(w_uv_g.data_ptr()), G, d_c,
+                                    d_n, d_v, d_r, ctypes.c_void_p(slots.data_ptr()), n,
+                                    ctypes.c_void_p(pool.data_ptr()), pool.shape[0], _stream(pool.device))
+    _check(st, "mla_gqa_expand")
+
+
+def _gqa_args(q_nope, q_rope, pool, num_groups, block_table, seq_lens, max_seq_len, sm_scale, num_splits, out, lse,
+              workspace, total_seq_len, d_v=128):
+    B, s_q, H, d_n = q_nope.shape
+    a = _lib.GqaArgs()
+    a.q_nope, a.q_rope, a.cache_pool = q_nope.data_ptr(), q_rope.data_ptr(), pool.data_ptr()
+    a.num_blocks = pool.shape[0]
+    a.num_groups, a.d_n, a.d_v, a.d_r = num_groups, d_n, d_v, q_rope.shape[3]
+    a.block_table, a.block_table_stride = block_table.data_ptr(), block_table.shape[1]
+    a.seq_lens, a.max_seq_len, a.total_seq_len = seq_lens.data_ptr(), int(max_seq_len), int(total_seq_len)
+    a.batch, a.s_q, a.num_heads = B, s_q, H
+    a.sm_scale, a.num_splits = float(sm_scale), int(num_splits)
+    a.out = out.data_ptr() if out is not None else 1 << 12
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    return a
+
+
+def gqa_decode_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool: torch.Tensor, num_groups: int,
+                     block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                     num_splits: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, total_seq_len: int = 0, d_v: int = 128):
+    """GQLA's GQA decode over the per-group expanded cache: q_nope [B, s_q, H, d_n], q_rope
+    [B, s_q, H, d_r] bf16; returns (out [B, s_q, H, d_v] fp32, lse [B, s_q, H])."""
+    _need_cuda(q_nope, q_rope, pool, block_table, seq_lens)
+    if q_nope.dim() != 4 or q_rope.dim() != 4 or q_nope.shape[:3] != q_rope.shape[:3]:
+        raise ValueError("q_nope [B, s_q, H, d_n] and q_rope [B, s_q, H, d_r] expected")
+    if q_nope.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16:
+        raise ValueError("bf16 queries expected")
+    if not q_nope.is_contiguous() or not q_rope.is_contiguous():
+        raise ValueError("queries must be dense")
+    bb = gqa_block_bytes(num_groups, q_nope.shape[3], d_v, q_rope.shape[3])
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or not pool.is_contiguous() or pool.shape[1] != bb:
+        raise ValueError(f"pool must be a dense uint8 [num_blocks, {bb}] tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be dense int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q_nope.shape[0],):
+        raise ValueError("seq_lens must be int32 [B]")
+    B, s_q, H, _ = q_nope.shape
+    if out is None:
+        out = torch.empty((B, s_q, H, d_v), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_nope.device)
+    _check_out(out, (B, s_q, H, d_v), (torch.float32,), q_nope.device, "out")
+    _check_out(lse, (B, s_q, H), (torch.float32,), q_nope.device, "lse")
+    L = _lib.load()
+    if workspace is None:
+        a = _gqa_args(q_nope, q_rope, pool, num_groups, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                      out, lse, None, total_seq_len, d_v)
+        n = ctypes.c_size_t()
+        _check(L.mla_gqa_workspace_size(ctypes.byref(a), ctypes.byref(n)), "mla_gqa_workspace_size")
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q_nope.device)
+    a = _gqa_args(q_nope, q_rope, pool, num_groups, block_table, seq_lens, max_seq_len, sm_scale, num_splits,
+                  out, lse, workspace, total_seq_len, d_v)
+    _check(L.mla_gqa_decode_paged(ctypes.byref(a), _stream(q_nope.device)), "mla_gqa_decode_paged")
+    return out, lse
 
 
 def hadamard_rotate(x: torch.Tensor, dim: int = -1) -> torch.Tensor:

@@ -32,6 +32,15 @@ class DecodeArgs(ctypes.Structure):
                 ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
 
 
+class GqaArgs(ctypes.Structure):
+    _fields_ = [("q_nope", c_void_p), ("q_rope", c_void_p), ("cache_pool", c_void_p), ("num_blocks", c_int64),
+                ("num_groups", c_int32), ("d_n", c_int32), ("d_v", c_int32), ("d_r", c_int32),
+                ("block_table", c_void_p), ("block_table_stride", c_int32), ("seq_lens", c_void_p),
+                ("max_seq_len", c_int32), ("total_seq_len", c_int64), ("batch", c_int32), ("s_q", c_int32),
+                ("num_heads", c_int32), ("sm_scale", c_float), ("num_splits", c_int32), ("out", c_void_p),
+                ("lse", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
+
+
 _SIGS = {
     "mla_abi_version": (c_int32, []),
     "mla_status_string": (c_char_p, [c_int32]),
@@ -54,6 +63,11 @@ _SIGS = {
                                      c_void_p, c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_void_p,
                                 c_int64, POINTER(CacheDesc), c_void_p]),
+    "mla_gqa_block_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32]),
+    "mla_gqa_expand": (c_int32, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                 c_int32, c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p]),
+    "mla_gqa_workspace_size": (c_int32, [POINTER(GqaArgs), POINTER(c_size_t)]),
+    "mla_gqa_decode_paged": (c_int32, [POINTER(GqaArgs), c_void_p]),
     "mla_hadamard_rotate": (c_int32, [c_void_p, c_int32, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64,
                                       c_void_p]),
 }

@@ -224,6 +224,58 @@ int32_t run_proj(const void* x, int64_t sn, int64_t sh, int32_t xdt, const void*
   return hip_status(mla::launch_proj(p, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------------------
+// GQLA per-group path: validation, plan (partitions of the longest sequence, one workgroup per
+// (sequence, partition, group), two workgroups per CU) and the partial layout.
+struct GqaPlan {
+  int rt, splits, tpc;
+};
+
+int32_t validate_gqa(const mla_gqa_args* a) {
+  if (a == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!a->q_nope || !a->q_rope || !a->cache_pool || !a->block_table || !a->seq_lens || !a->out)
+    return MLA_ERR_INVALID_ARG;
+  if (a->batch <= 0 || a->num_heads <= 0 || a->num_groups <= 0 || (a->s_q != 1 && a->s_q != 2))
+    return MLA_ERR_INVALID_ARG;
+  if (a->max_seq_len < a->s_q || a->num_blocks <= 0 || a->num_splits < 0 || !std::isfinite(a->sm_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (a->d_n <= 0 || a->d_v <= 0 || a->d_r <= 0 || a->num_heads % a->num_groups) return MLA_ERR_INVALID_ARG;
+  if (a->block_table_stride < ceil_div(a->max_seq_len, kBlock)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(a->q_nope, 16) || !aligned(a->q_rope, 16) || !aligned(a->cache_pool, 16) || !aligned(a->out, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) || (a->lse && !aligned(a->lse, 4)))
+    return MLA_ERR_INVALID_ARG;
+  if (a->d_n != 128 || a->d_v != 128 || a->d_r != 64) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->s_q * a->num_heads / a->num_groups > 64) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)a->batch * a->s_q * a->num_heads > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+GqaPlan gqa_plan(const mla_gqa_args* a, int cus) {
+  GqaPlan p{};
+  const int rg = a->s_q * a->num_heads / a->num_groups;
+  p.rt = rg <= 16 ? 1 : (rg <= 32 ? 2 : 4);
+  const int nblk = (int)ceil_div(a->max_seq_len, kBlock);
+  const int64_t target = 2 * (int64_t)cus;   // two workgroups per CU: a single round of partitions
+  int tpc;
+  if (a->num_splits > 0) {
+    tpc = (int)ceil_div(nblk, a->num_splits < nblk ? a->num_splits : nblk);
+  } else {
+    const int64_t blocks = a->total_seq_len > 0 ? ceil_div(a->total_seq_len, kBlock) : (int64_t)nblk * a->batch;
+    tpc = (int)ceil_div(blocks * a->num_groups, target);
+  }
+  tpc = std::max(1, std::min(tpc, std::min(nblk, kMaxTilesPerSplit)));
+  p.tpc = tpc;
+  p.splits = (int)ceil_div(nblk, tpc);
+  return p;
+}
+
+size_t gqa_partial_bytes(const mla_gqa_args* a, const GqaPlan& p) {
+  if (p.splits <= 1) return 0;
+  const int64_t rows = (int64_t)a->batch * p.splits * a->s_q * a->num_heads;
+  return (size_t)(align_up(rows * a->d_v * 4, 256) + align_up(rows * 4, 256));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -649,6 +701,119 @@ int32_t mla_hadamard_rotate(void* x, int32_t dtype, int32_t d, int64_t elem_stri
   p.scale = (float)(1.0 / std::sqrt((double)d));
   p.vec8 = elem_stride == 1 && d >= 8 && aligned(x, 16) && outer_stride % 8 == 0 && inner_stride % 8 == 0;
   return hip_status(mla::launch_rotate(p, (hipStream_t)stream));
+}
+
+int64_t mla_gqa_block_bytes(int32_t num_groups, int32_t d_n, int32_t d_v, int32_t d_r) {
+  if (num_groups <= 0 || d_n <= 0 || d_v <= 0 || d_r <= 0) return -1;
+  return (int64_t)kBlock * 2 * ((int64_t)num_groups * (d_n + d_v) + d_r);
+}
+
+int32_t mla_gqa_expand(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,
+                       const void* w_uk_g, const void* w_uv_g, int32_t num_groups, int32_t d_c, int32_t d_n,
+                       int32_t d_v, int32_t d_r, const int32_t* slots, int64_t n, void* cache_pool,
+                       int64_t num_blocks, void* stream) {
+  if (n < 0 || num_blocks <= 0 || num_groups <= 0 || d_c <= 0) return MLA_ERR_INVALID_ARG;
+  const int64_t bb = mla_gqa_block_bytes(num_groups, d_n, d_v, d_r);
+  if (bb < 0) return MLA_ERR_INVALID_ARG;
+  if (d_n != 128 || d_v != 128 || d_r != 64 || d_c % 32 != 0) return MLA_ERR_UNSUPPORTED;
+  if (n == 0) return MLA_OK;
+  if (!c_new || !k_rope_new || !w_uk_g || !w_uv_g || !slots || !cache_pool) return MLA_ERR_INVALID_ARG;
+  if (c_stride < d_c || k_stride < d_r || c_stride % 8 || k_stride % 8) return MLA_ERR_INVALID_ARG;
+  if (!aligned(c_new, 16) || !aligned(k_rope_new, 16) || !aligned(w_uk_g, 16) || !aligned(w_uv_g, 16) ||
+      !aligned(slots, 4) || !aligned(cache_pool, 16))
+    return MLA_ERR_INVALID_ARG;
+  if (ceil_div(n, 16) * num_groups > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  mla::GqaExpandParams p{};
+  p.c = c_new;
+  p.k = k_rope_new;
+  p.c_stride = c_stride;
+  p.k_stride = k_stride;
+  p.w_uk = w_uk_g;
+  p.w_uv = w_uv_g;
+  p.G = num_groups;
+  p.d_c = d_c;
+  p.slots = slots;
+  p.n = n;
+  p.pool = (uint8_t*)cache_pool;
+  p.num_blocks = num_blocks;
+  p.block_bytes = bb;
+  return hip_status(mla::launch_gqa_expand(p, (hipStream_t)stream));
+}
+
+int32_t mla_gqa_workspace_size(const mla_gqa_args* a, size_t* bytes) {
+  const int32_t s = validate_gqa(a);
+  if (s != MLA_OK) return s;
+  if (bytes == nullptr) return MLA_ERR_INVALID_ARG;
+  int cus = 0;
+  if (a->num_splits == 0) {
+    const int32_t e = device_cus(&cus);
+    if (e != MLA_OK) return e;
+  }
+  *bytes = gqa_partial_bytes(a, gqa_plan(a, cus));
+  return MLA_OK;
+}
+
+int32_t mla_gqa_decode_paged(const mla_gqa_args* a, void* stream) {
+  int32_t s = validate_gqa(a);
+  if (s != MLA_OK) return s;
+  int cus = 0;
+  if (a->num_splits == 0) {
+    s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+  }
+  const GqaPlan plan = gqa_plan(a, cus);
+  const size_t need = gqa_partial_bytes(a, plan);
+  if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need || !aligned(a->workspace, 256)))
+    return MLA_ERR_WORKSPACE;
+  const int R = a->s_q * a->num_heads;
+  const bool split = plan.splits > 1;
+  mla::GqaParams p{};
+  p.q_nope = a->q_nope;
+  p.q_rope = a->q_rope;
+  p.pool = (const uint8_t*)a->cache_pool;
+  p.num_blocks = a->num_blocks;
+  p.block_bytes = mla_gqa_block_bytes(a->num_groups, a->d_n, a->d_v, a->d_r);
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.seq_lens = a->seq_lens;
+  p.max_seq_len = a->max_seq_len;
+  p.B = a->batch;
+  p.s_q = a->s_q;
+  p.H = a->num_heads;
+  p.G = a->num_groups;
+  p.max_chunks = plan.splits;
+  p.tpc = plan.tpc;
+  const int64_t units = (int64_t)a->batch * plan.splits * a->num_groups;
+  if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  p.total_units = (int)units;
+  p.units_per_xcd = (int)ceil_div(units, 8);
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  float* part_o = split ? (float*)a->workspace : nullptr;
+  float* part_lse = split ? (float*)((char*)a->workspace + align_up((int64_t)a->batch * plan.splits * R * a->d_v * 4, 256))
+                          : nullptr;
+  p.out = split ? part_o : a->out;
+  p.out_lse = split ? part_lse : a->lse;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = mla::launch_gqa_decode(p, plan.rt, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (split) {
+    mla::CombineParams c{};
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.seq_lens = a->seq_lens;
+    c.max_seq_len = a->max_seq_len;
+    c.R = R;
+    c.d_c = a->d_v;
+    c.max_chunks = plan.splits;
+    c.tpc = plan.tpc;
+    c.out = a->out;
+    c.out_bf16 = 0;
+    c.out_lse = a->lse;
+    c.many_parts = plan.splits > 16;
+    e = mla::launch_combine(c, a->batch, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
 }
 
 int32_t mla_dequant_blocks(const void* cache_pool, int64_t num_blocks, const mla_cache_desc* desc,

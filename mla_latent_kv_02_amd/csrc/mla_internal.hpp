@@ -140,6 +140,41 @@ struct RotateParams {
   int vec8;                 // unit stride, 16-byte-aligned groups of 8: vector path
 };
 
+// GQLA per-group path.  Expanded pool block: G planes [64][k_nope 128 | v 128] bf16, then one
+// RoPE plane [64][64] bf16.  Decode rows per unit: the group's s_q * H / G query rows.
+struct GqaParams {
+  const void* q_nope;       // [B][s_q][H][128] bf16
+  const void* q_rope;       // [B][s_q][H][64] bf16
+  const uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  int B, s_q, H, G;
+  int max_chunks, tpc;      // partitions per sequence (upper bound) and 64-token blocks per partition
+  int total_units, units_per_xcd;
+  float scale_log2;
+  float* out;               // partials [B * max_chunks][s_q H][128], or out when max_chunks == 1
+  float* out_lse;           // [B * max_chunks][s_q H] (may be null when writing out directly)
+};
+
+struct GqaExpandParams {
+  const void* c;            // [n] rows of d_c bf16, c_stride elements apart
+  const void* k;            // [n] rows of 64 bf16, k_stride elements apart
+  int64_t c_stride, k_stride;
+  const void* w_uk;         // [G][128][d_c] bf16
+  const void* w_uv;         // [G][d_c][128] bf16
+  int G, d_c;
+  const int32_t* slots;
+  int64_t n;
+  uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+};
+
+hipError_t launch_gqa_expand(const GqaExpandParams& p, hipStream_t st);
+hipError_t launch_gqa_decode(const GqaParams& p, int rt, hipStream_t st);
+
 // Bytes of the per-device scratch array of mla_decode_paged_noalloc, and the device address
 // of the current device's copy (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;

@@ -261,3 +261,47 @@ def test_workspace_too_small_is_rejected_before_any_launch():
         assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE
         a.workspace, a.workspace_bytes = FAKE + 128, need
         assert L.mla_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE
+
+
+def _gqa_args(**kw):
+    a = _lib.GqaArgs()
+    a.q_nope = a.q_rope = a.cache_pool = a.block_table = a.seq_lens = a.out = FAKE
+    a.num_blocks = 100
+    a.num_groups, a.d_n, a.d_v, a.d_r = 8, 128, 128, 64
+    a.block_table_stride = 64
+    a.max_seq_len = 4096
+    a.batch, a.s_q, a.num_heads = 4, 2, 128
+    a.sm_scale = 0.07
+    a.num_splits = 2
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_gqa_layout_and_validation():
+    """GQLA per-group path: block size, argument checks and unsupported shapes, all before any
+    device is touched (an explicit split count plans without the device)."""
+    L = mla.lib()
+    assert L.mla_gqa_block_bytes(8, 128, 128, 64) == 64 * 2 * (8 * 256 + 64)
+    assert L.mla_gqa_block_bytes(0, 128, 128, 64) == -1
+    n = ctypes.c_size_t()
+    assert L.mla_gqa_workspace_size(ctypes.byref(_gqa_args()), ctypes.byref(n)) == 0
+    rows = 4 * 2 * 2 * 128                                   # batch x splits x s_q x heads
+    assert n.value == rows * 128 * 4 + rows * 4
+    for kw, st in [(dict(num_groups=3), 1), (dict(s_q=3), 1), (dict(q_nope=None), 1), (dict(q_rope=FAKE + 8), 1),
+                   (dict(block_table_stride=10), 1), (dict(num_heads=0), 1), (dict(d_v=64), 2),
+                   (dict(num_groups=2), 2)]:                 # 2 groups x 2 queries: 128 rows per group
+        a = _gqa_args(**kw)
+        assert L.mla_gqa_decode_paged(ctypes.byref(a), None) == st, kw
+    a = _gqa_args()
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert L.mla_gqa_decode_paged(ctypes.byref(a), None) == _lib.MLA_ERR_WORKSPACE
+    # expansion: n = 0 is a no-op; misaligned rows and unsupported widths are rejected
+    ok = [FAKE, 512, FAKE, 64, FAKE, FAKE, 8, 512, 128, 128, 64, FAKE, 5, FAKE, 10, None]
+    assert L.mla_gqa_expand(*(ok[:12] + [0] + ok[13:])) == 0
+    bad = list(ok)
+    bad[1] = 515
+    assert L.mla_gqa_expand(*bad) == 1
+    bad = list(ok)
+    bad[8] = 96
+    assert L.mla_gqa_expand(*bad) == 2
