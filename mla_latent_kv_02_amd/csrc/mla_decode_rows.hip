@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
@@ -52,6 +53,42 @@ namespace rows {
 // measured lane-set model), and rsw(t + 16) = rsw(t).
 __device__ __forceinline__ int rsw(int t) { return t & 7; }
 __device__ __forceinline__ int rst_off(int t, int d) { return t * 576 + (((d >> 3) ^ rsw(t)) << 3) + (d & 7); }
+
+// lambdas of the kernel body are inlined whatever their size: a call would put the accumulator
+// array, which they reach by reference, in memory
+#define MLA_INLINE __attribute__((always_inline))
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>) in order: an unrolled
+// loop whose index is a compile-time constant in the body
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// Keeps the computation of x at this point of the instruction stream: an empty volatile asm
+// that takes and redefines x is ordered with the MFMA asm around it, so the compiler can
+// neither sink the work that produced x to its later uses nor hoist it.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Float maxima as single instructions: fmaxf would first quiet possible signalling NaNs of
+// operands the compiler cannot trace (permlane results, pinned values), one instruction each.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int NT = 256;                  // 4 wavefronts, one per SIMD
 constexpr int ROWS = 128;                // query rows per workgroup
@@ -128,6 +165,17 @@ __device__ __forceinline__ void pv1(f32x4& c, const bf16x8& v, const bf16x8& pp)
 #undef MLA_PV_ACC
 #undef MLA_PV_NEW
 #undef MLA_PV_DRAIN
+}
+
+// c = 0 for an AGPR tile: an MFMA of zero operands (z holds zeros).  NOP: two wait states
+// first for the VALU that may have just written z; DRAIN: the MFMA latency waited out after.
+// The tile is an in-out operand: its registers stay where they are (a fresh output would let
+// the register allocator move the accumulators between branches, through copies and spills).
+template <bool NOP, bool DRAIN>
+__device__ __forceinline__ void zero_tile(f32x4& c, const bf16x8& z) {
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "+a"(c) : "v"(z));
+  else if constexpr (DRAIN) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(c) : "v"(z));
+  else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "+a"(c) : "v"(z));
 }
 
 // c *= a (a per lane) for an AGPR tile, through 16 bytes per lane of this wave's LDS scratch:
@@ -520,19 +568,21 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   // new piece: this sequence's queries, fresh softmax state
   int cur_b = -1;
   bool fresh = true;
-  auto start_piece = [&](int b, int L, bool wait) {
+  auto start_piece = [&](int b, int L, bool wait) MLA_INLINE {
     cur_b = b;
+    int r0 = row0, lg_ = lg;
+    asm volatile("" : "+v"(r0), "+v"(lg_));   // addresses recomputed here rather than held across the loop
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int row = row0 + 16 * rt;
+      const int row = r0 + 16 * rt;
       const bool ok = row < R;
       const size_t qb = (size_t)cur_b * R + (ok ? row : 0);
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks)
-        qreg[rt][ks] = ok ? load_q8(p.q_lat, qb * 512 + ks * 32 + lg * 8, QF32) : bf16x8{};
+        qreg[rt][ks] = ok ? load_q8(p.q_lat, qb * 512 + ks * 32 + lg_ * 8, QF32) : bf16x8{};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        qreg[rt][16 + ks] = ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg * 8, QF32) : bf16x8{};
+        qreg[rt][16 + ks] = ok ? load_q8(p.q_rope, qb * 64 + ks * 32 + lg_ * 8, QF32) : bf16x8{};
       lim[rt] = ok ? L - p.s_q + row / p.H : -1;
       m_s[rt] = NEG_INF;
       l_x[rt] = 0.f;
@@ -661,13 +711,394 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   };
   static_assert((QUANT ? DEPTH - 1 : 2) <= 7 && 7 * LOADS <= 63, "stage waits out of range");
 
-  // prologue.  bf16: stages 0..2 in flight, stage 0 landed.  Quantised: codes 0..DEPTH-1 in
-  // flight, code 0 dequantised into bf16 stage 0, code 1 landed.
+  // ---- shared stage kernels of the two loops below
+
+  // scores S^T[token][row] of the stage at KS for token tiles tt and row tiles rt; hook(ks)
+  // runs after k-step ks
+  auto score_stage = [&](const bf16_t* KS, f32x4(&sc)[2][RT], auto&& hook) MLA_INLINE {
+    const bf16_t* kb[2][2];
+    int lr_ = lr;
+    asm volatile("" : "+v"(lr_));   // recomputed per stage rather than held across the loop
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = tt * 16 + lr_;
+      const int f = rsw(t);
+      kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
+      kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
+    }
+    constexpr int KD = 1;   // prefetch depth in k-steps (deeper gains nothing: the loop is MFMA-issue bound)
+    bf16x8 a[KD + 1][2];
+#pragma unroll
+    for (int i = 0; i < KD; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) a[i][tt] = *(const bf16x8*)(kb[tt][i & 1] + i * 32);
+    // per k-step: read, MFMA pair (token tile 0), read, MFMA pair (token tile 1): reads issued
+    // between MFMAs keep the matrix pipe busier than reads grouped before four MFMAs
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int nx = (ks + KD) % (KD + 1), cu = ks % (KD + 1);
+      if (ks + KD < 18) a[nx][0] = *(const bf16x8*)(kb[0][(ks + KD) & 1] + (ks + KD) * 32);
+      if (ks == 0) score2<true, true, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
+      else score2<false, false, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + KD < 18) a[nx][1] = *(const bf16x8*)(kb[1][(ks + KD) & 1] + (ks + KD) * 32);
+      if (ks == 0) score2<true, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
+      else if (ks == 17) score2<false, false, true>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
+      else score2<false, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
+      __builtin_amdgcn_sched_barrier(0);
+      hook(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // O^T[col][row] += V^T[col][token] . P^T[token][row] over the stage at KS (FRESH: the first
+  // stage of a piece, the accumulators start from zero); P^T is the pair of bf16 terms pp, ppl.
+  // hook(j) (j a compile-time constant) runs after MFMA j of the 128.  The 8 tokens of lane
+  // group lg are 4 lg .. 4 lg + 3 (first read) and 16 + 4 lg .. 16 + 4 lg + 3 (second read).
+  auto pv_stage = [&](auto FRESH, const bf16_t* KS, const bf16x8(&pp)[RT], const bf16x8(&ppl)[RT], auto&& hook) MLA_INLINE {
+    constexpr bool F = decltype(FRESH)::value;
+    // column d = 16 nt + 4 (lr & 3) of token t is element rst_off(t, d); with nt = 4 q + r its
+    // piece is (2 nt + h) ^ rsw(t) = 8 q + ((2 r + h) ^ rsw(t)), h = (lr & 3) / 2, since
+    // rsw < 8: four per-lane bases (r) and an immediate offset of 64 q elements.  Token
+    // tb = ta + 16 has rsw(tb) = rsw(ta): its pieces sit exactly 16 rows further on (db).
+    int lane_ = lane;
+    asm volatile("" : "+v"(lane_));   // recomputed per stage rather than held across the loop
+    const int lrp = lane_ & 15, lgp = lane_ >> 4;
+    const int ta = 4 * lgp + (lrp >> 2);
+    const int h = (lrp & 3) >> 1, fa = rsw(ta);
+    constexpr int db = 16 * 576;
+    int oa[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
+    // software pipeline: the two halves of the V^T fragment of tile nt + PD are read between
+    // the MFMAs of tile nt
+    auto rlo = [&](int nt) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + 64 * (nt >> 2)]);
+    };
+    auto rhi = [&](int nt) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + db + 64 * (nt >> 2)]);
+    };
+    constexpr int PD = 2;   // prefetch depth
+    i16x4 lo[PD + 1], hi[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      lo[i] = rlo(i);
+      hi[i] = rhi(i);
+    }
+    static_for<32>([&](auto NT_) MLA_INLINE {
+      constexpr int nt = decltype(NT_)::value;
+      constexpr int cu = nt % (PD + 1), nx = (nt + PD) % (PD + 1);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[cu], hi[cu], 0, 1, 2, 3, 4, 5, 6, 7));
+      if constexpr (nt + PD < 32) lo[nx] = rlo(nt + PD);
+      pv1<F, nt == 0, false>(acc[0][nt], v, pp[0]);
+      hook(std::integral_constant<int, 4 * nt>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (nt + PD < 32) hi[nx] = rhi(nt + PD);
+      pv1<F, false, false>(acc[1][nt], v, pp[1]);
+      hook(std::integral_constant<int, 4 * nt + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      pv1<false, false, false>(acc[0][nt], v, ppl[0]);
+      hook(std::integral_constant<int, 4 * nt + 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      pv1<false, false, nt == 31>(acc[1][nt], v, ppl[1]);
+      hook(std::integral_constant<int, 4 * nt + 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto no_hook = [](auto) {};
+
+  // acc[rt] *= a[rt] (a row's running maximum moved)
+  auto rescale = [&](const float(&a)[RT]) MLA_INLINE {
+    const uint32_t sa = lds_addr(&resc[tid]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt) scale_tile(acc[rt][nt], a[rt], sa);
+  };
+
+  // acc = 0 (the bf16 loop starts every piece from zeroed accumulators)
+  auto zero_acc = [&]() MLA_INLINE {
+    bf16x8 zz{};
+    asm volatile("" : "+v"(zz));   // materialised once, here
+    static_for<2 * 32>([&](auto K) MLA_INLINE {
+      constexpr int k = decltype(K)::value;
+      zero_tile<k == 0, k == 63>(acc[k >> 5][k & 31], zz);
+    });
+  };
+
+  // end of a piece of sequence b: this wave's rows, unnormalised, with 1 / sum(P) and the lse
+  // (m: running maximum, l: this lane's share of sum(P)), to slot b + range; the combine
+  // normalises (a range's pieces have distinct slots)
+  auto store_piece = [&](int b, const float(&m)[RT], const float(&l)[RT]) MLA_INLINE {
+    const size_t slot = (size_t)b + range;
+    int r0 = row0;
+    asm volatile("" : "+v"(r0));   // addresses recomputed here rather than held across the loop
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = r0 + 16 * rt;
+      const float lx = sum_lg(l[rt]);
+      if (row < R) {
+        float* o = p.part_o + (slot * R + row) * 512 + 4 * lg;
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) store_tile(o + nt * 16, acc[rt][nt]);
+        if (lg == 0) {
+          p.part_lse[slot * R + row] = lx > 0.f ? (m[rt] + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
+          p.part_inv[slot * R + row] = lx > 0.f ? 1.f / lx : 0.f;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
+  };
+
+  // softmax of rows row0 + 16 rt over one stage's scores sc (this lane holds tokens 16 tt +
+  // 4 lg + i) in one piece: P^T operands pt (high bf16 terms) and ptl (low terms), the
+  // accumulator factor al, the running maximum m_s and sum l_x updated.  MASK: token k of the
+  // stage is kept if k < valid and stok + k <= lim (otherwise every token of the stage is
+  // visible to every row).
+  auto softmax = [&](auto MASK, f32x4(&sc)[2][RT], int valid, int stok, bf16x8(&pt)[RT], bf16x8(&ptl)[RT],
+                     float(&al)[RT]) MLA_INLINE {
+    constexpr bool M = decltype(MASK)::value;
+    float mt[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int kb4 = 4 * lg;
+      const int lim_k = min(valid - 1, lim[rt] - stok);
+      mt[rt] = NEG_INF;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (!M) {
+            sc[tt][rt][i] *= p.scale_log2;
+          } else {
+            const bool ok = kb4 <= lim_k - (16 * tt + i);
+            sc[tt][rt][i] = ok ? sc[tt][rt][i] * p.scale_log2 : NEG_INF;
+          }
+          mt[rt] = fmaxf(mt[rt], sc[tt][rt][i]);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mt[rt] = max_lg(mt[rt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mn = mt[rt] > m_s[rt] + ROWS_SLACK ? mt[rt] : m_s[rt];
+      const float mu = mn == NEG_INF ? 0.f : mn;
+      // while m_s = -inf every P so far was 0 and the accumulators hold zeros: nothing to scale
+      al[rt] = (mn == m_s[rt] || m_s[rt] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_s[rt] - mu);
+      l_x[rt] *= al[rt];
+      m_s[rt] = mn;
+      uint32_t pw[4], pl[4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float pf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pf[i] = __builtin_amdgcn_exp2f(sc[tt][rt][i] - mu);
+          l_x[rt] += pf[i];
+        }
+        split_pair(pf[0], pf[1], pw[2 * tt], pl[2 * tt]);
+        split_pair(pf[2], pf[3], pw[2 * tt + 1], pl[2 * tt + 1]);
+      }
+      pt[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      ptl[rt] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+    }
+  };
+  // rows past the sequence end in ring slot k came from a stand-in address: zero them
+  auto zero_tail = [&](int k, int valid) MLA_INLINE {
+    bf16_t* Z = bf_stage(k);
+    for (int q = tid; q < (ST_TOK - valid) * 72; q += NT)
+      *(u32x4*)&Z[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
+    lds_barrier();
+  };
+
   if constexpr (!QUANT) {
+    // ---- bf16: a software pipeline over the 4-slot ring.  Step s scores stage s + 1, then
+    // takes the P.V products of stage s with the softmax of stage s + 1 spread between its
+    // MFMAs: a SIMD issues for one wave here, and vector-ALU work overlaps the matrix pipe
+    // only when it sits between independent MFMAs.  Stage s + 3 is issued into the slot of
+    // stage s - 1 (free since the barrier closing step s - 1) during the scores; the step
+    // ends once stage s + 2 has landed.
     for (int s = 0; s < 3 && s < nst; ++s) issue(s);
+    zero_acc();   // while the first stages are in flight
     wait_stage(min(nst - 1, 2));
     lds_barrier();
+    int info_c = __builtin_amdgcn_readfirstlane(st_info[0]);
+    f32x4 sc[2][RT];
+    bf16x8 pt[RT], ptl[RT];
+    {
+      const int valid0 = (info_c >> 20) & 63;
+      const int stok0 = __builtin_amdgcn_readfirstlane(st_tok[0]);
+      if (valid0 < ST_TOK) zero_tail(0, valid0);
+      score_stage(bf_stage(0), sc, no_hook);
+      float al0[RT];   // a piece's first stage: nothing to rescale
+      if (valid0 == ST_TOK && stok0 + (ST_TOK - 1) <= lim_all) softmax(std::false_type{}, sc, valid0, stok0, pt, ptl, al0);
+      else softmax(std::true_type{}, sc, valid0, stok0, pt, ptl, al0);
+    }
+    if (nst > 1) wait_stage(min(nst - 1, 2) - 1);
+    lds_barrier();
+    // stage-table entries of the next step, read at the end of the step before
+    int n_info = st_info[min(nst - 1, 1)], n_tok = st_tok[min(nst - 1, 1)];
+    int n_bid = st_bid[min(nst - 1, 3)], n_btok = st_tok[min(nst - 1, 3)];
+    float m_e[RT], l_e[RT];   // state of the piece ending with stage s
+    for (int s = 0; s < nst; ++s) {
+      const bool has_n = s + 1 < nst;
+      const int info_n = __builtin_amdgcn_readfirstlane(n_info);
+      const int valid_n = (info_n >> 20) & 63;
+      const int stok_n = __builtin_amdgcn_readfirstlane(n_tok);
+      const bool refill = s + 3 < nst;
+      const Src sr_new{p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
+                       (__builtin_amdgcn_readfirstlane(n_btok) / ST_TOK) & 1};
+      if (s > 0 && (info_c & INFO_START)) zero_acc();   // a new piece starts from zero
+      if (info_c & INFO_END) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          m_e[rt] = m_s[rt];
+          l_e[rt] = l_x[rt];
+        }
+      }
+      if (has_n) {
+        if (valid_n < ST_TOK) zero_tail((s + 1) & 3, valid_n);
+        // a new piece: its queries and a fresh softmax state (the ending piece's is in m_e, l_e)
+        if (info_n & INFO_START) start_piece(info_n & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s + 1]), true);
+        score_stage(bf_stage((s + 1) & 3), sc, [&](int ks) {
+          if ((ks & 1) && refill) issue_one(s + 3, sr_new, ks >> 1);
+        });
+      }
+
+      // Softmax of stage s + 1 in steps of one or two vector instructions, step c after P.V
+      // MFMA c (MASK: after MFMA c + 1; the masking, when needed, after MFMA 0).  An MFMA holds
+      // its wave's issue for most of its cycles: about one vector instruction per MFMA comes for
+      // free, so the steps are spread thinly.  Steps 0..7: row maxima (r alternating); 8..15:
+      // the lane-group reductions; 16..29: new running maximum and accumulator factor; then six
+      // steps per pair of tokens (e0, e1) = (2 jj, 2 jj + 1) of row tile r, pairs in the order
+      // (jj, r): two exponentials, the sums and the high term, the residuals, the low term.  A
+      // pair's scores die as its P^T words are made, so the register peak stays low.
+      float aln[RT], mt[RT], thr[RT], mn[RT], mu[RT], ex[RT], pf0[RT], pf1[RT], d0[RT], d1[RT], sw0[RT], sw1[RT];
+      uint32_t pw[RT][4], pl[RT][4];
+      auto X = [&](int r, int e) -> float { return sc[e >> 2][r][e & 3]; };
+      auto chunk = [&](auto C) MLA_INLINE {
+        constexpr int c = decltype(C)::value;
+        if constexpr (c < 8) {
+          constexpr int r = c & 1, k = c >> 1;
+          if constexpr (k == 0) mt[r] = vmax3(X(r, 0), X(r, 1), X(r, 2));
+          else if constexpr (k == 1) mt[r] = vmax3(mt[r], X(r, 3), X(r, 4));
+          else if constexpr (k == 2) mt[r] = vmax3(mt[r], X(r, 5), X(r, 6));
+          else mt[r] = vmax(mt[r], X(r, 7));
+          pin(mt[r]);
+        } else if constexpr (c < 16) {
+          constexpr int r = (c >> 1) & 1, lvl = (c - 8) >> 2;
+          if constexpr ((c & 1) == 0) {
+            const auto t = lvl == 0 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[r]), __float_as_uint(mt[r]), false, false)
+                                    : __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[r]), __float_as_uint(mt[r]), false, false);
+            sw0[r] = __uint_as_float(t[0]);
+            sw1[r] = __uint_as_float(t[1]);
+            pin(sw0[r]);
+            pin(sw1[r]);
+          } else {
+            mt[r] = vmax(sw0[r], sw1[r]);
+            pin(mt[r]);
+          }
+        } else if constexpr (c < 30) {
+          constexpr int r = c & 1, k = (c - 16) >> 1;
+          if constexpr (k == 0) {
+            mt[r] *= p.scale_log2;
+            thr[r] = m_s[r] + ROWS_SLACK;
+            pin(mt[r]);
+            pin(thr[r]);
+          } else if constexpr (k == 1) {
+            mn[r] = mt[r] > thr[r] ? mt[r] : m_s[r];
+            pin(mn[r]);
+          } else if constexpr (k == 2) {
+            mu[r] = mn[r] == NEG_INF ? 0.f : mn[r];
+            pin(mu[r]);
+          } else if constexpr (k == 3) {
+            ex[r] = __builtin_amdgcn_exp2f(m_s[r] - mu[r]);
+            pin(ex[r]);
+          } else if constexpr (k == 4) {
+            aln[r] = mn[r] == m_s[r] ? 1.f : ex[r];
+            pin(aln[r]);
+          } else if constexpr (k == 5) {
+            // while m_s = -inf every P so far was 0 and the accumulators hold zeros
+            aln[r] = m_s[r] == NEG_INF ? 1.f : aln[r];
+            pin(aln[r]);
+          } else {
+            l_x[r] *= aln[r];
+            m_s[r] = mn[r];
+            pin(l_x[r]);
+            pin(m_s[r]);
+          }
+        } else {
+          constexpr int q = (c - 30) / 6, k = (c - 30) % 6;
+          constexpr int r = q & 1, jj = q >> 1;
+          if constexpr (k == 0) {
+            pf0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(X(r, 2 * jj), p.scale_log2, -mu[r]));
+            pin(pf0[r]);
+          } else if constexpr (k == 1) {
+            pf1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(X(r, 2 * jj + 1), p.scale_log2, -mu[r]));
+            pin(pf1[r]);
+          } else if constexpr (k == 2) {
+            l_x[r] += pf0[r];
+            pw[r][jj] = pack_bf16x2(pf0[r], pf1[r]);
+            pin(l_x[r]);
+            pin(pw[r][jj]);
+          } else if constexpr (k == 3) {
+            l_x[r] += pf1[r];
+            d0[r] = pf0[r] - __uint_as_float(pw[r][jj] << 16);
+            pin(l_x[r]);
+            pin(d0[r]);
+          } else if constexpr (k == 4) {
+            d1[r] = pf1[r] - __uint_as_float(pw[r][jj] & 0xFFFF0000u);
+            pin(d1[r]);
+          } else {
+            pl[r][jj] = pack_bf16x2(d0[r], d1[r]);
+            pin(pl[r][jj]);
+          }
+        }
+      };
+      constexpr int NCHUNK = 30 + 6 * 8;
+      const bool mask_n = !(valid_n == ST_TOK && stok_n + (ST_TOK - 1) <= lim_all);
+      auto hook = [&](auto J) MLA_INLINE {
+        constexpr int j = decltype(J)::value;
+        if constexpr (j == 0) {
+          if (mask_n) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+              const int d = min(valid_n - 1, lim[r] - stok_n) - 4 * lg;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sc[e >> 2][r][e & 3] = d >= 16 * (e >> 2) + (e & 3) ? X(r, e) : NEG_INF;
+              pin(sc[0][r]);
+              pin(sc[1][r]);
+            }
+          }
+        } else if constexpr (j <= NCHUNK) {
+          chunk(std::integral_constant<int, j - 1>{});
+        }
+      };
+      pv_stage(std::false_type{}, bf_stage(s & 3), pt, ptl, hook);
+      if (info_c & INFO_END) store_piece(info_c & 0xFFFFF, m_e, l_e);
+      if (has_n) {
+        if (!(info_n & INFO_START) && __any(aln[0] != 1.f || aln[1] != 1.f)) rescale(aln);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          pt[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[rt][0], pw[rt][1], pw[rt][2], pw[rt][3]});
+          ptl[rt] = __builtin_bit_cast(bf16x8, u32x4{pl[rt][0], pl[rt][1], pl[rt][2], pl[rt][3]});
+        }
+      }
+      info_c = info_n;
+      if (s + 2 < nst) {
+        n_info = st_info[s + 2];
+        n_tok = st_tok[s + 2];
+        n_bid = st_bid[min(nst - 1, s + 4)];
+        n_btok = st_tok[min(nst - 1, s + 4)];
+        // stage s + 2 has landed and nobody reads stage s any more
+        wait_stage(min(nst - 1, s + 3) - (s + 2));
+      }
+      lds_barrier();
+    }
   } else {
+    // ---- quantised: codes 0..DEPTH-1 in flight, code 0 dequantised into bf16 stage 0, code 1
+    // landed.  Step s dequantises code s + 1 into the other bf16 stage, then scores, softmax
+    // and P.V of stage s; code s + DEPTH refills the slot of code s.
     for (int s = 0; s < DEPTH && s < nst; ++s) issue(s);
     wait_stage(min(nst - 1, DEPTH - 1));
     lds_barrier();
@@ -675,234 +1106,55 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
                 p.g_rope_log2, bf_stage(0), tid);
     if (nst > 1) wait_stage(min(nst - 1, DEPTH - 1) - 1);
     lds_barrier();
-  }
 
-  // the ring slot refilled in step s: stage s + 3 into the slot of stage s - 1 (bf16) / code
-  // s + DEPTH into the slot of code s (dequantised in step s - 1)
-  constexpr int AHEAD = QUANT ? DEPTH : 3;
-  // stage-table entries of step s, read at the end of step s - 1 so that their LDS latency
-  // overlaps the end-of-step wait
-  int n_info = st_info[0], n_tok = st_tok[0];
-  int n_bid = st_bid[min(nst - 1, AHEAD)], n_btok = st_tok[min(nst - 1, AHEAD)];
-  for (int s = 0; s < nst; ++s) {
-    const int info = __builtin_amdgcn_readfirstlane(n_info);
-    const int valid = (info >> 20) & 63;
-    const int stok = __builtin_amdgcn_readfirstlane(n_tok);
-    if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]), true);
-    const int s_new = s + AHEAD;
-    const bool refill = s_new < nst;
-    const Src sr_new{p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
-                     (__builtin_amdgcn_readfirstlane(n_btok) / ST_TOK) & 1};
-    const bf16_t* KS = QUANT ? bf_stage(s & 1) : bf_stage(s & 3);
-    if (!QUANT && valid < ST_TOK) {
-      // rows past the sequence end came from a stand-in address: zero them
-      bf16_t* Z = bf_stage(s & 3);
-      for (int q = tid; q < (ST_TOK - valid) * 72; q += NT)
-        *(u32x4*)&Z[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
-      lds_barrier();
-    }
-    if constexpr (QUANT) {
+    // stage-table entries of step s, read at the end of step s - 1 so that their LDS latency
+    // overlaps the end-of-step wait
+    int n_info = st_info[0], n_tok = st_tok[0];
+    int n_bid = st_bid[min(nst - 1, DEPTH)], n_btok = st_tok[min(nst - 1, DEPTH)];
+    for (int s = 0; s < nst; ++s) {
+      const int info = __builtin_amdgcn_readfirstlane(n_info);
+      const int valid = (info >> 20) & 63;
+      const int stok = __builtin_amdgcn_readfirstlane(n_tok);
+      if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]), true);
+      const int s_new = s + DEPTH;
+      const bool refill = s_new < nst;
+      const Src sr_new{p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
+                       (__builtin_amdgcn_readfirstlane(n_btok) / ST_TOK) & 1};
+      const bf16_t* KS = bf_stage(s & 1);
       // dequantise the next stage while this one is consumed: its code stage has landed and
       // its bf16 slot was last read in step s - 1
       if (s + 1 < nst)
         QS::dequant(smem + code_slot((s + 1) % DEPTH), (__builtin_amdgcn_readfirstlane(st_info[s + 1]) >> 20) & 63,
                     p.g_lat_log2, p.g_rope_log2, bf_stage((s + 1) & 1), tid);
-    }
 
-    // ---- scores S^T[token][row] for token tiles tt and row tiles rt; the refill's DMA
-    // instructions are spread over the k-steps so that they queue behind MFMA work
-    f32x4 sc[2][RT];
-    {
-      const bf16_t* kb[2][2];
-      int lr_ = lr;
-      asm volatile("" : "+v"(lr_));   // recomputed per stage rather than held across the loop
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = tt * 16 + lr_;
-        const int f = rsw(t);
-        kb[tt][0] = KS + t * 576 + (lg ^ f) * 8;
-        kb[tt][1] = KS + t * 576 + ((4 + lg) ^ f) * 8 - 32;
-      }
-      constexpr int KD = 2;   // prefetch depth in k-steps (deeper gains nothing: the loop is MFMA-issue bound)
-      bf16x8 a[KD + 1][2];
-#pragma unroll
-      for (int i = 0; i < KD; ++i)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) a[i][tt] = *(const bf16x8*)(kb[tt][i & 1] + i * 32);
-      // per k-step: read, MFMA pair (token tile 0), read, MFMA pair (token tile 1): reads issued
-      // between MFMAs keep the matrix pipe busier than reads grouped before four MFMAs
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const int nx = (ks + KD) % (KD + 1), cu = ks % (KD + 1);
-        if (ks + KD < 18) a[nx][0] = *(const bf16x8*)(kb[0][(ks + KD) & 1] + (ks + KD) * 32);
-        if (ks == 0) score2<true, true, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
-        else score2<false, false, false>(sc[0][0], sc[0][1], a[cu][0], qreg[0][ks], qreg[1][ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + KD < 18) a[nx][1] = *(const bf16x8*)(kb[1][(ks + KD) & 1] + (ks + KD) * 32);
-        if (ks == 0) score2<true, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
-        else if (ks == 17) score2<false, false, true>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
-        else score2<false, false, false>(sc[1][0], sc[1][1], a[cu][1], qreg[0][ks], qreg[1][ks]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // ---- softmax of rows row0 + 16 rt (this lane holds tokens 16 tt + 4 lg + i).  On most
-    // steps every token of the stage is visible to every row: no per-token mask.
-    bf16x8 pt[RT], ptl[RT];   // P^T operands: high and low bf16 terms
-    float al[RT];
-    auto softmax = [&](auto FULL) {
-      constexpr bool F = decltype(FULL)::value;
-      float mt[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        // token k = 16 tt + 4 lg + i is kept if k < valid and stok + k <= lim
-        const int kb4 = 4 * lg;
-        const int lim_k = min(valid - 1, lim[rt] - stok);
-        mt[rt] = NEG_INF;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (F) {
-              sc[tt][rt][i] *= p.scale_log2;
-            } else {
-              const bool ok = kb4 <= lim_k - (16 * tt + i);
-              sc[tt][rt][i] = ok ? sc[tt][rt][i] * p.scale_log2 : NEG_INF;
-            }
-            mt[rt] = fmaxf(mt[rt], sc[tt][rt][i]);
-          }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) mt[rt] = max_lg(mt[rt]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float mn = mt[rt] > m_s[rt] + ROWS_SLACK ? mt[rt] : m_s[rt];
-        const float mu = mn == NEG_INF ? 0.f : mn;
-        // while m_s = -inf every P so far was 0 and the accumulators hold zeros: nothing to scale
-        al[rt] = (mn == m_s[rt] || m_s[rt] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_s[rt] - mu);
-        l_x[rt] *= al[rt];
-        m_s[rt] = mn;
-        uint32_t pw[4], pl[4];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          float pf[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pf[i] = __builtin_amdgcn_exp2f(sc[tt][rt][i] - mu);
-            l_x[rt] += pf[i];
-          }
-          split_pair(pf[0], pf[1], pw[2 * tt], pl[2 * tt]);
-          split_pair(pf[2], pf[3], pw[2 * tt + 1], pl[2 * tt + 1]);
-        }
-        pt[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-        ptl[rt] = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-      }
-    };
-    if (valid == ST_TOK && stok + (ST_TOK - 1) <= lim_all) softmax(std::true_type{});
-    else softmax(std::false_type{});
-    if (!fresh && __any(al[0] != 1.f || al[1] != 1.f)) {
-      const uint32_t sa = lds_addr(&resc[tid]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) scale_tile(acc[rt][nt], al[rt], sa);
-    }
-
-    // ---- O^T[col][row] += V^T[col][token] . P^T[token][row]; the 8 tokens of lane group lg
-    // are 4 lg .. 4 lg + 3 (first read) and 16 + 4 lg .. 16 + 4 lg + 3 (second read)
-    {
-      // column d = 16 nt + 4 (lr & 3) of token t is element rst_off(t, d); with nt = 4 q + r its
-      // piece is (2 nt + h) ^ rsw(t) = 8 q + ((2 r + h) ^ rsw(t)), h = (lr & 3) / 2, since
-      // rsw < 8: four per-lane bases (r) and an immediate offset of 64 q elements.  Token
-      // tb = ta + 16 has rsw(tb) = rsw(ta): its pieces sit exactly 16 rows further on (db).
-      int lane_ = lane;
-      asm volatile("" : "+v"(lane_));   // recomputed per stage rather than held across the loop
-      const int lrp = lane_ & 15, lgp = lane_ >> 4;
-      const int ta = 4 * lgp + (lrp >> 2);
-      const int h = (lrp & 3) >> 1, fa = rsw(ta);
-      constexpr int db = 16 * 576;
-      int oa[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oa[r] = ta * 576 + (((2 * r + h) ^ fa) << 3) + (lrp & 1) * 4;
-      // software pipeline: the two halves of the V^T fragment of tile nt + PD are read between
-      // the two MFMAs of tile nt
-      auto rlo = [&](int nt) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + 64 * (nt >> 2)]);
-      };
-      auto rhi = [&](int nt) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&KS[oa[nt & 3] + db + 64 * (nt >> 2)]);
-      };
-      constexpr int PD = 2;   // prefetch depth
-      auto pv_loop = [&](auto FR) {
-        constexpr bool F = decltype(FR)::value;
-        i16x4 lo[PD + 1], hi[PD + 1];
-#pragma unroll
-        for (int i = 0; i < PD; ++i) {
-          lo[i] = rlo(i);
-          hi[i] = rhi(i);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 32; ++nt) {
-          const int cu = nt % (PD + 1), nx = (nt + PD) % (PD + 1);
-          const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[cu], hi[cu], 0, 1, 2, 3, 4, 5, 6, 7));
-          if (nt + PD < 32) lo[nx] = rlo(nt + PD);
-          if (nt == 0) pv1<F, true, false>(acc[0][nt], v, pt[0]);
-          else pv1<F, false, false>(acc[0][nt], v, pt[0]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (nt + PD < 32) hi[nx] = rhi(nt + PD);
-          pv1<F, false, false>(acc[1][nt], v, pt[1]);
-          __builtin_amdgcn_sched_barrier(0);
-          pv1<false, false, false>(acc[0][nt], v, ptl[0]);
-          if (nt == 31) pv1<false, false, true>(acc[1][nt], v, ptl[1]);
-          else pv1<false, false, false>(acc[1][nt], v, ptl[1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      if (fresh) pv_loop(std::true_type{});
-      else pv_loop(std::false_type{});
+      f32x4 sc[2][RT];
+      score_stage(KS, sc, [](int) {});
+      bf16x8 pt[RT], ptl[RT];
+      float al[RT];
+      if (valid == ST_TOK && stok + (ST_TOK - 1) <= lim_all) softmax(std::false_type{}, sc, valid, stok, pt, ptl, al);
+      else softmax(std::true_type{}, sc, valid, stok, pt, ptl, al);
+      if (!fresh && __any(al[0] != 1.f || al[1] != 1.f)) rescale(al);
+      if (fresh) pv_stage(std::true_type{}, KS, pt, ptl, no_hook);
+      else pv_stage(std::false_type{}, KS, pt, ptl, no_hook);
       fresh = false;
-    }
+      if (info & INFO_END) store_piece(cur_b, m_s, l_x);
 
-    // ---- end of a piece: this wave's rows, unnormalised, with 1 / sum(P) and the lse, to
-    // slot cur_b + range; the combine normalises (a range's pieces have distinct slots)
-    if (info & INFO_END) {
-      const size_t slot = (size_t)cur_b + range;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int row = row0 + 16 * rt;
-        const float lx = sum_lg(l_x[rt]);
-        if (row < R) {
-          float* o = p.part_o + (slot * R + row) * 512 + 4 * lg;
-#pragma unroll
-          for (int nt = 0; nt < 32; ++nt) store_tile(o + nt * 16, acc[rt][nt]);
-          if (lg == 0) {
-            p.part_lse[slot * R + row] = lx > 0.f ? (m_s[rt] + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
-            p.part_inv[slot * R + row] = lx > 0.f ? 1.f / lx : 0.f;
-          }
-        }
+      if (s + 1 < nst) {
+        n_info = st_info[s + 1];
+        n_tok = st_tok[s + 1];
+        n_bid = st_bid[min(nst - 1, s + 1 + DEPTH)];
+        n_btok = st_tok[min(nst - 1, s + 1 + DEPTH)];
       }
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
-    }
-
-    if (s + 1 < nst) {
-      n_info = st_info[s + 1];
-      n_tok = st_tok[s + 1];
-      n_bid = st_bid[min(nst - 1, s + 1 + AHEAD)];
-      n_btok = st_tok[min(nst - 1, s + 1 + AHEAD)];
-    }
-    // the refill of this step, issued where the wave waits anyway: an issue blocks while many
-    // reads are outstanding, and between MFMAs that stalls the matrix pipe
-    if (refill) {
+      // the refill of this step, issued where the wave waits anyway: an issue blocks while many
+      // reads are outstanding, and between MFMAs that stalls the matrix pipe
+      if (refill) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) issue_one(s_new, sr_new, i);
-    }
-    // the next step's stage has landed and nobody reads stage s any more
-    if constexpr (!QUANT) {
-      if (s + 1 < nst) wait_stage(min(nst - 1, s + 3) - (s + 1));
-    } else {
+        for (int i = 0; i < LOADS; ++i) issue_one(s_new, sr_new, i);
+      }
+      // the next step's stage has landed and nobody reads stage s any more
       if (s + 2 < nst) wait_stage(min(nst - 1, s + DEPTH) - (s + 2));
+      lds_barrier();
     }
-    lds_barrier();
   }
 }
 
