@@ -60,6 +60,15 @@ __device__ __forceinline__ void dma16a(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same from a wave-uniform base plus a per-lane 32-bit offset (the offset in a VGPR, the
+// base in SGPRs): no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the gfx950 lane
 // swaps: with both operands equal, permlane32_swap / permlane16_swap return x at l and at l ^ 32
 // (l ^ 16), so one max / add per step gives the butterfly without an LDS round trip.
@@ -149,6 +158,32 @@ struct QuantProducer {
     issue_with(half, pl, groups, rgroups, tid, [&](int off, int i, int wbase) {
       dma16(blk + off, (lds_void*)(cstage + (size_t)(i * NT + wbase) * 16));
     });
+  }
+  // byte offsets inside the block (first half, second half) of the piece that code-stage slot
+  // `slot` receives; padding slots re-load a real piece (spread over the stage, never one
+  // shared address)
+  __device__ __forceinline__ static uint2 piece_offsets(const QuantPlanes& pl, int groups, int rgroups, int slot) {
+    const int n_lc = ST_TOK * LB / 16;
+    const int n_ls = ST_TOK * groups * 4 / 16;
+    const int n_rc = ST_TOK * 32 / 16;
+    const int n_rs = (ST_TOK * rgroups * 4 + 15) / 16;
+    const int n_all = n_lc + n_ls + n_rc + n_rs;
+    int p = slot < n_all ? slot : slot - n_all;
+    int base, hstride;
+    if (p < n_lc) {
+      base = pl.lc + p * 16;
+      hstride = ST_TOK * LB;
+    } else if ((p -= n_lc) < n_ls) {
+      base = pl.ls + p * 16;
+      hstride = ST_TOK * groups * 4;
+    } else if ((p -= n_ls) < n_rc) {
+      base = pl.rc + p * 16;
+      hstride = ST_TOK * 32;
+    } else {
+      base = pl.rs + (p - n_rc) * 16;
+      hstride = ST_TOK * rgroups * 4;
+    }
+    return uint2{(uint32_t)base, (uint32_t)(base + hstride)};
   }
   // byte offset inside the block of the piece that slot i * NT + tid of a code stage receives:
   // dma(offset, i, first thread of the wave) for each of this thread's DMA instructions
@@ -747,14 +782,28 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   auto cslot = [&](int k) { return smem + OFF_C + (k % DEPTH) * CBYTES; };
   auto pbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * 2 * PBYTES); };            // high term
   auto plbuf = [&](int k) { return (bf16_t*)(smem + OFF_P + (k & 1) * 2 * PBYTES + PBYTES); };  // low term
-  // every thread issues its LOADS_LO / LOADS_HI pieces of a code stage
+  // every thread issues its LOADS_LO / LOADS_HI pieces of a code stage.  The per-lane source
+  // offsets of both halves of a block are computed once: address arithmetic before each DMA
+  // instruction would sit in the issue stream of every step.
+  // two separate arrays: a select between elements of one 2-D array becomes an indexed load,
+  // which puts the array in scratch memory
+  uint32_t doff0[QP::LOADS_LO], doff1[QP::LOADS_LO];
+#pragma unroll
+  for (int i = 0; i < QP::LOADS_LO; ++i) {
+    const uint2 o = QP::piece_offsets(pl, groups, rgroups, i * NT + tid);
+    doff0[i] = o.x;
+    doff1[i] = o.y;
+  }
+  const uint32_t wslice = (uint32_t)__builtin_amdgcn_readfirstlane((tid & ~63) * 16);
   auto issue = [&](int k) {
     int half, valid;
     const uint8_t* blk = stage_src(k, half, valid);
-    const uint32_t cst = sbase + OFF_C + (k % DEPTH) * CBYTES;
-    QP::issue_with(half, pl, groups, rgroups, tid, [&](int off, int i, int wbase) {
-      dma16a(blk + off, cst + (uint32_t)(i * NT + wbase) * 16);
-    });
+    const uint32_t cst = sbase + OFF_C + (k % DEPTH) * CBYTES + wslice;
+#pragma unroll
+    for (int i = 0; i < QP::LOADS_LO; ++i) {
+      if (i == QP::LOADS_HI && w >= QP::WAVES_LO) break;
+      dma16s(blk, half ? doff1[i] : doff0[i], cst + (uint32_t)(i * NT * 16));
+    }
   };
   // wait until code stage k has landed, `later` code stages having been issued after it
   auto wait_later = [&](int later) {
