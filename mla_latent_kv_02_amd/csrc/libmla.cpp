@@ -286,7 +286,8 @@ size_t gqa_partial_bytes(const mla_gqa_args* a, const GqaPlan& p) {
 namespace {
 
 struct MixedLayout {
-  size_t o_bytes = 0, lse_off = 0, dec_off = 0, total = 0;
+  size_t o_bytes = 0, lse_off = 0, total = 0;
+  size_t dec_off[3] = {0, 0, 0};   // each part's own decode workspace (its partials stay until the merge)
 };
 
 // The args a part is decoded with: its own cache and block table, the shared queries; sink
@@ -322,8 +323,7 @@ int32_t mixed_layout(const mla_decode_args* const parts[3], MixedLayout* m) {
   const int64_t rows = (int64_t)ref->batch * ref->s_q * ref->num_heads;
   m->o_bytes = (size_t)align_up(3 * rows * ref->cache.d_c * 4, 256);
   m->lse_off = m->o_bytes;
-  m->dec_off = m->lse_off + (size_t)align_up(3 * rows * 4, 256);
-  size_t dec = 0;
+  size_t off = m->lse_off + (size_t)align_up(3 * rows * 4, 256);
   int cus = 0;
   int32_t s = device_cus(&cus);
   if (s != MLA_OK) return s;
@@ -336,9 +336,10 @@ int32_t mixed_layout(const mla_decode_args* const parts[3], MixedLayout* m) {
     s = validate_decode(&p, &lay);
     if (s != MLA_OK) return s;
     size_t lse_off = 0;
-    dec = std::max(dec, partial_bytes(&p, make_plan(&p, cus), &lse_off));
+    m->dec_off[i] = off;
+    off += (size_t)align_up((int64_t)partial_bytes(&p, make_plan(&p, cus), &lse_off), 256);
   }
-  m->total = m->dec_off + (size_t)align_up((int64_t)dec, 256);
+  m->total = off;
   return MLA_OK;
 }
 
@@ -424,7 +425,10 @@ namespace {
 
 // The decode with its split partials in `ws`: the caller's workspace (mla_decode_paged) or
 // the library's per-device scratch array (mla_decode_paged_noalloc, ws == nullptr on entry).
-int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream) {
+// With `defer`, only the decode kernel runs and *defer says where its partials are, for a
+// merge over several decodes (a decode without split partials wrote o_lat and lse, which
+// must then be fp32 and present: that pair is its single partial).
+int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream, mla::CombinePart* defer = nullptr) {
   Layout lay;
   int32_t s = validate_decode(a, &lay);
   if (s != MLA_OK) return s;
@@ -487,6 +491,10 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream) {
     r.part_inv = (float*)((char*)ws + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
     hipError_t e = mla::launch_decode_rows(r, a->cache.latent_fmt, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
+    if (defer != nullptr) {
+      *defer = mla::CombinePart{r.part_o, r.part_lse, r.part_inv, r.meta, a->seq_lens, a->max_seq_len, 0, 1};
+      return MLA_OK;
+    }
     {
       mla::CombineParams c{};
       c.part_o = r.part_o;
@@ -548,6 +556,15 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream) {
 
   hipError_t e = plan.rt == 0 ? mla::launch_decode_f32(p, st) : mla::launch_decode_mfma(p, a->cache.latent_fmt, plan.rt, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  if (defer != nullptr) {
+    if (split)
+      *defer = mla::CombinePart{part_o, part_lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, plan.splits, plan.tpc};
+    else if (a->o_dtype != MLA_F32 || a->lse == nullptr)
+      return MLA_ERR_INVALID_ARG;
+    else
+      *defer = mla::CombinePart{(const float*)a->o_lat, a->lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, 1, plan.tpc};
+    return MLA_OK;
+  }
   if (split) {
     mla::CombineParams c{};
     c.part_o = part_o;
@@ -602,33 +619,30 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
   const size_t rows = (size_t)B * R;
   float* part_o = (float*)workspace;
   float* part_lse = (float*)((char*)workspace + m.lse_off);
+  // each part's decode leaves its split partials in its own workspace region; one
+  // log-sum-exp merge then reads all of them (a part with no token for a sequence contributes
+  // nothing; a sequence with no token at all gets o = 0 and lse = -inf)
+  mla::CombinePartsParams c{};
   int n = 0;
   for (int i = 0; i < 3; ++i) {
     if (parts[i] == nullptr) continue;
     mla_decode_args p = part_args(parts[i], i == 2);
     p.o_lat = part_o + (size_t)n * rows * d_c;
     p.lse = part_lse + (size_t)n * rows;
-    p.workspace = (char*)workspace + m.dec_off;
-    p.workspace_bytes = workspace_bytes - m.dec_off;
-    s = mla_decode_paged(&p, stream);
+    p.workspace = (char*)workspace + m.dec_off[i];
+    p.workspace_bytes = workspace_bytes - m.dec_off[i];
+    s = decode_paged(&p, false, stream, &c.part[n]);
     if (s != MLA_OK) return s;
     ++n;
   }
-  // LSE merge of the parts (a part with no token gives o = 0, lse = -inf and weight 0)
-  mla::CombineParams c{};
-  c.part_o = part_o;
-  c.part_lse = part_lse;
-  c.seq_lens = ref->seq_lens;
-  c.max_seq_len = ref->max_seq_len;
+  c.n_parts = n;
+  c.B = B;
   c.R = R;
   c.d_c = d_c;
-  c.max_chunks = n;
-  c.chunk_major = 1;
-  c.B = B;
   c.out = o_lat;
   c.out_bf16 = o_dtype == MLA_BF16;
   c.out_lse = lse;
-  return hip_status(mla::launch_combine(c, B, (hipStream_t)stream));
+  return hip_status(mla::launch_combine_parts(c, (hipStream_t)stream));
 }
 
 int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,

@@ -206,6 +206,105 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   if (p.out_lse != nullptr && tid == 0) p.out_lse[(size_t)b * R + r] = lse_out;
 }
 
+// ---------------------------------------------------------------------------------------
+// Merge over several decodes (the mixed-precision history): attention over disjoint token
+// sets merges exactly by log-sum-exp, so the split partials of every part, partition or range
+// mode, are read in place and merged in one pass: one workgroup of 128 threads per (b, row),
+// each thread owning 4 columns, partials taken in batches of CB per part with a running
+// maximum across parts.  A (b, row) with no token in any part gets o = 0 and lse = -inf.
+// ---------------------------------------------------------------------------------------
+template <int CB>
+__global__ __launch_bounds__(128) void combine_parts_kernel(CombinePartsParams p) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float NEG_INF = -__builtin_inff();
+  const int tid = threadIdx.x;
+  const int R = p.R, d_c = p.d_c;
+  const int b = blockIdx.x / R, r = blockIdx.x % R;
+  const bool vec4 = (d_c & 3) == 0;
+  float lse_out = NEG_INF;
+  for (int d = tid * 4; d < d_c; d += 512) {
+    float m = NEG_INF, wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int pi = 0; pi < p.n_parts; ++pi) {
+      const CombinePart& q = p.part[pi];
+      int L = q.seq_lens[b];
+      L = L < 0 ? 0 : (L > q.max_seq_len ? q.max_seq_len : L);
+      const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+      int nch;
+      size_t base;
+      if (q.meta == nullptr) {
+        nch = (nblk + q.tpc - 1) / q.tpc;
+        nch = nch < 1 ? 1 : (nch > q.max_chunks ? q.max_chunks : nch);
+        base = (size_t)b * q.max_chunks * R + r;
+      } else {
+        if (nblk <= 0) continue;   // no piece
+        const int per = q.meta[0], last = q.meta[2 + b] - 1;
+        const int i0 = (last - nblk + 1) / per, i1 = last / per;
+        nch = i1 - i0 + 1;
+        base = ((size_t)b + i0) * R + r;
+      }
+      const size_t stride = (size_t)R * d_c;
+      for (int c0 = 0; c0 < nch; c0 += CB) {
+        const int n = min(CB, nch - c0);
+        const size_t ub = base + (size_t)c0 * R;
+        float lc[CB], iv[CB];
+        f32x4 v[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          const bool ok = j < n;
+          lc[j] = ok ? q.lse[ub + (size_t)j * R] : NEG_INF;
+          iv[j] = ok && q.inv != nullptr ? q.inv[ub + (size_t)j * R] : 1.f;
+          v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ok) {
+            const float* src = q.o + ub * d_c + d + j * stride;
+            if (vec4) {
+              v[j] = *(const f32x4*)src;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[j][i] = d + i < d_c ? src[i] : 0.f;
+            }
+          }
+        }
+        float mb = NEG_INF;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) mb = fmaxf(mb, lc[j]);
+        if (mb > m) {
+          // earlier weights are relative to m; m = -inf means nothing was added yet
+          const float sc = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m - mb) * LOG2E);
+          acc *= sc;
+          wsum *= sc;
+          m = mb;
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          const float wc = lc[j] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((lc[j] - m) * LOG2E);
+          wsum += wc;
+          acc += (wc * iv[j]) * v[j];
+        }
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const f32x4 o = acc * inv;
+    const size_t ob = ((size_t)b * R + r) * d_c + d;
+    if (!vec4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (d + i >= d_c) break;
+        if (p.out_bf16)
+          ((uint16_t*)p.out)[ob + i] = (uint16_t)f32_to_bf16_bits(o[i]);
+        else
+          ((float*)p.out)[ob + i] = o[i];
+      }
+    } else if (p.out_bf16) {
+      *(uint2*)((bf16_t*)p.out + ob) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      *(f32x4*)((float*)p.out + ob) = o;
+    }
+    lse_out = wsum > 0.f ? m + logf(wsum) : NEG_INF;
+  }
+  if (p.out_lse != nullptr && tid == 0) p.out_lse[(size_t)b * R + r] = lse_out;
+}
+
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st) {
   hipLaunchKernelGGL(decode_f32_kernel, dim3(p.total_units), dim3(128), 0, st, p);
   return hipGetLastError();
@@ -216,6 +315,11 @@ hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
     hipLaunchKernelGGL(combine_kernel<32>, dim3(batch * p.R), dim3(128), 0, st, p);
   else
     hipLaunchKernelGGL(combine_kernel<8>, dim3(batch * p.R), dim3(128), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_parts(const CombinePartsParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(combine_parts_kernel<8>, dim3(p.B * p.R), dim3(128), 0, st, p);
   return hipGetLastError();
 }
 

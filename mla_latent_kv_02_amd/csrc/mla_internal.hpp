@@ -84,6 +84,31 @@ struct CombineParams {
   int B;                    // batch (chunk-major mode)
 };
 
+// Where one decode left its split partials (a merge over several decodes reads them in place).
+// Partition mode (meta == nullptr): normalised o and lse, partial c of (b, row) at row
+// (b * max_chunks + c) * R + row, nch(b) = clamp(ceil(blocks(b) / tpc), 1, max_chunks).  Range
+// mode: unnormalised o with inv = 1 / sum(P), pieces at rows (b + i) * R + row for b's ranges i
+// (meta as the row-owner decode wrote it); a sequence without blocks has no piece.
+struct CombinePart {
+  const float* o;
+  const float* lse;
+  const float* inv;
+  const int32_t* meta;
+  const int32_t* seq_lens;
+  int max_seq_len, max_chunks, tpc;
+};
+
+constexpr int kMaxCombineParts = 3;
+
+struct CombinePartsParams {
+  CombinePart part[kMaxCombineParts];
+  int n_parts;
+  int B, R, d_c;
+  void* out;
+  int out_bf16;
+  float* out_lse;
+};
+
 struct ProjParams {
   const void* X;            // element (n, h, k) at X[n*sxn + h*sxh + k]
   int64_t sxn, sxh;
@@ -183,6 +208,8 @@ hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_decode_mfma(const DecodeParams& p, int fmt, int rt, hipStream_t st);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
+// one log-sum-exp merge over the split partials of up to three decodes (the mixed history)
+hipError_t launch_combine_parts(const CombinePartsParams& p, hipStream_t st);
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
