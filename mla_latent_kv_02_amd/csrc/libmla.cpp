@@ -168,9 +168,9 @@ int32_t device_cus(int* cus) {
   return MLA_OK;
 }
 
-// Workspace layout.  Row-owner kernel: meta [B + 2] int32, then partial o, lse and 1/sum(P)
+// Workspace layout.  Row-owner kernel: meta [B + 3] int32, then partial o, lse and 1/sum(P)
 // of the slots b + i (B + ranges - 1 of them).  Partition kernels: partial o, then lse.
-size_t rows_meta_bytes(const mla_decode_args* a) { return (size_t)align_up(((int64_t)a->batch + 2) * 4, 256); }
+size_t rows_meta_bytes(const mla_decode_args* a) { return (size_t)align_up(((int64_t)a->batch + 3) * 4, 256); }
 
 size_t partial_bytes(const mla_decode_args* a, const Plan& p, size_t* lse_off) {
   if (p.rows) {
@@ -288,7 +288,35 @@ namespace {
 struct MixedLayout {
   size_t o_bytes = 0, lse_off = 0, total = 0;
   size_t dec_off[3] = {0, 0, 0};   // each part's own decode workspace (its partials stay until the merge)
+  bool joint = false;              // one row-owner decode over the joint history (workspace: its own)
 };
+
+// A mixed history that the row-owner kernel decodes as one sequence of blocks per batch
+// entry: a low-bit middle of that kernel's family, with bf16 sink and recent parts (either may
+// be absent).  J: the middle's arguments with the joint history's length bound; false: the
+// parts are decoded one by one and merged.
+bool mixed_joint(const mla_decode_args* const parts[3], int cus, mla_decode_args* J, Plan* plan) {
+  const mla_decode_args* mid = parts[1];
+  if (mid == nullptr || !is_quant_fmt(mid->cache.latent_fmt)) return false;
+  Layout ml;
+  if (!cache_layout(&mid->cache, &ml)) return false;
+  int64_t nblk = ceil_div(mid->max_seq_len, kBlock);
+  for (int i = 0; i < 3; i += 2) {
+    const mla_decode_args* a = parts[i];
+    if (a == nullptr) continue;
+    Layout l;
+    // a bf16 block's slot in the code ring receives a stand-in copy of its first
+    // block_bytes(middle) bytes, so the bf16 block must be at least that long
+    if (a->cache.latent_fmt != MLA_FMT_BF16 || !cache_layout(&a->cache, &l) || l.block_bytes < ml.block_bytes)
+      return false;
+    nblk += ceil_div(a->max_seq_len, kBlock);
+  }
+  if (nblk * kBlock > (1LL << 30)) return false;
+  *J = *mid;
+  J->max_seq_len = (int)(nblk * kBlock);
+  *plan = make_plan(J, cus);
+  return plan->rows;
+}
 
 // The args a part is decoded with: its own cache and block table, the shared queries; sink
 // and middle precede every query, so with s_q = 2 the two queries are decoded as 2H heads.
@@ -340,6 +368,13 @@ int32_t mixed_layout(const mla_decode_args* const parts[3], MixedLayout* m) {
     off += (size_t)align_up((int64_t)partial_bytes(&p, make_plan(&p, cus), &lse_off), 256);
   }
   m->total = off;
+  mla_decode_args J;
+  Plan jp;
+  m->joint = mixed_joint(parts, cus, &J, &jp);
+  if (m->joint) {
+    size_t lse_off = 0;
+    m->total = (size_t)align_up((int64_t)partial_bytes(&J, jp, &lse_off), 256);
+  }
   return MLA_OK;
 }
 
@@ -423,6 +458,71 @@ int32_t mla_decode_workspace_size(const mla_decode_args* args, size_t* bytes) {
 
 namespace {
 
+// Row-owner kernel arguments of decode `a` under `plan`, its split partials in `ws` at the
+// layout partial_bytes gives (lse_off).
+int32_t rows_params(const mla_decode_args* a, const Layout& lay, const Plan& plan, void* ws, size_t lse_off,
+                    mla::RowsParams* out) {
+  mla::RowsParams r{};
+  r.q_lat = a->q_lat;
+  r.q_rope = a->q_rope;
+  r.q_f32 = a->q_dtype == MLA_F32;
+  r.pool = (const uint8_t*)a->cache_pool;
+  r.num_blocks = a->num_blocks;
+  r.block_bytes = lay.block_bytes;
+  r.off_lc = lay.off[0];
+  r.off_ls = lay.off[1];
+  r.off_rc = lay.off[2];
+  r.off_rs = lay.off[3];
+  auto log2i = [](int v) { int l = 0; while ((1 << (l + 1)) <= v) ++l; return l; };
+  r.g_lat_log2 = log2i(a->cache.latent_group > 0 ? a->cache.latent_group : 1);
+  r.g_rope_log2 = log2i(a->cache.rope_group > 0 ? a->cache.rope_group : 1);
+  r.block_table = a->block_table;
+  r.bt_stride = a->block_table_stride;
+  r.seq_lens = a->seq_lens;
+  r.max_seq_len = a->max_seq_len;
+  r.B = a->batch;
+  r.s_q = a->s_q;
+  r.H = a->num_heads;
+  r.R = a->s_q * a->num_heads;
+  r.RG = plan.rg;
+  r.n_ranges = plan.splits;
+  r.phantom = kRowsPhantom;
+  const int64_t units = (int64_t)plan.splits * plan.rg;
+  if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  r.total_units = (int)units;
+  r.units_per_xcd = (int)ceil_div(units, 8);
+  r.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  r.out = a->o_lat;
+  r.out_bf16 = a->o_dtype == MLA_BF16;
+  r.out_lse = a->lse;
+  r.meta = (int32_t*)ws;
+  r.part_o = (float*)((char*)ws + rows_meta_bytes(a));
+  r.part_lse = (float*)((char*)ws + lse_off);
+  r.part_inv = (float*)((char*)ws + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
+  *out = r;
+  return MLA_OK;
+}
+
+// The merge of a row-owner decode's pieces into o_lat and lse.
+int32_t rows_combine(const mla_decode_args* a, const mla::RowsParams& r, const Plan& plan, hipStream_t st) {
+  mla::CombineParams c{};
+  c.part_o = r.part_o;
+  c.part_lse = r.part_lse;
+  c.part_inv = r.part_inv;
+  c.seq_lens = a->seq_lens;
+  c.max_seq_len = a->max_seq_len;
+  c.R = r.R;
+  c.d_c = a->cache.d_c;
+  c.meta = r.meta;
+  c.out = a->o_lat;
+  c.out_bf16 = a->o_dtype == MLA_BF16;
+  c.out_lse = a->lse;
+  c.B = a->batch;
+  // a sequence meets about n_ranges / batch + 1 ranges
+  c.many_parts = plan.splits > 16 * a->batch;
+  return hip_status(mla::launch_combine(c, a->batch, st));
+}
+
 // The decode with its split partials in `ws`: the caller's workspace (mla_decode_paged) or
 // the library's per-device scratch array (mla_decode_paged_noalloc, ws == nullptr on entry).
 // With `defer`, only the decode kernel runs and *defer says where its partials are, for a
@@ -453,67 +553,16 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream, mla::
   hipStream_t st = (hipStream_t)stream;
   if (plan.rows) {
     mla::RowsParams r{};
-    r.q_lat = a->q_lat;
-    r.q_rope = a->q_rope;
-    r.q_f32 = a->q_dtype == MLA_F32;
-    r.pool = (const uint8_t*)a->cache_pool;
-    r.num_blocks = a->num_blocks;
-    r.block_bytes = lay.block_bytes;
-    r.off_lc = lay.off[0];
-    r.off_ls = lay.off[1];
-    r.off_rc = lay.off[2];
-    r.off_rs = lay.off[3];
-    auto log2i = [](int v) { int l = 0; while ((1 << (l + 1)) <= v) ++l; return l; };
-    r.g_lat_log2 = log2i(a->cache.latent_group > 0 ? a->cache.latent_group : 1);
-    r.g_rope_log2 = log2i(a->cache.rope_group > 0 ? a->cache.rope_group : 1);
-    r.block_table = a->block_table;
-    r.bt_stride = a->block_table_stride;
-    r.seq_lens = a->seq_lens;
-    r.max_seq_len = a->max_seq_len;
-    r.B = a->batch;
-    r.s_q = a->s_q;
-    r.H = a->num_heads;
-    r.R = a->s_q * a->num_heads;
-    r.RG = plan.rg;
-    r.n_ranges = plan.splits;
-    r.phantom = kRowsPhantom;
-    const int64_t units = (int64_t)plan.splits * plan.rg;
-    if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
-    r.total_units = (int)units;
-    r.units_per_xcd = (int)ceil_div(units, 8);
-    r.scale_log2 = a->sm_scale * 1.4426950408889634f;
-    r.out = a->o_lat;
-    r.out_bf16 = a->o_dtype == MLA_BF16;
-    r.out_lse = a->lse;
-    r.meta = (int32_t*)ws;
-    r.part_o = (float*)((char*)ws + rows_meta_bytes(a));
-    r.part_lse = (float*)((char*)ws + lse_off);
-    r.part_inv = (float*)((char*)ws + lse_off + align_up((int64_t)(a->batch + plan.splits - 1) * r.R * 4, 256));
+    s = rows_params(a, lay, plan, ws, lse_off, &r);
+    if (s != MLA_OK) return s;
     hipError_t e = mla::launch_decode_rows(r, a->cache.latent_fmt, st);
     if (e != hipSuccess) return MLA_ERR_HIP;
     if (defer != nullptr) {
-      *defer = mla::CombinePart{r.part_o, r.part_lse, r.part_inv, r.meta, a->seq_lens, a->max_seq_len, 0, 1};
+      *defer = mla::CombinePart{r.part_o, r.part_lse, r.part_inv, r.meta, a->seq_lens, a->max_seq_len, 0, 1,
+                                plan.splits > 16 * a->batch};
       return MLA_OK;
     }
-    {
-      mla::CombineParams c{};
-      c.part_o = r.part_o;
-      c.part_lse = r.part_lse;
-      c.part_inv = r.part_inv;
-      c.seq_lens = a->seq_lens;
-      c.max_seq_len = a->max_seq_len;
-      c.R = r.R;
-      c.d_c = a->cache.d_c;
-      c.meta = r.meta;
-      c.out = a->o_lat;
-      c.out_bf16 = a->o_dtype == MLA_BF16;
-      c.out_lse = a->lse;
-      // a sequence meets about n_ranges / batch + 1 ranges
-      c.many_parts = plan.splits > 16 * a->batch;
-      e = mla::launch_combine(c, a->batch, st);
-      if (e != hipSuccess) return MLA_ERR_HIP;
-    }
-    return MLA_OK;
+    return rows_combine(a, r, plan, st);
   }
 
   mla::DecodeParams p{};
@@ -558,11 +607,13 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream, mla::
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (defer != nullptr) {
     if (split)
-      *defer = mla::CombinePart{part_o, part_lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, plan.splits, plan.tpc};
+      *defer = mla::CombinePart{part_o, part_lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, plan.splits, plan.tpc,
+                                plan.splits > 16};
     else if (a->o_dtype != MLA_F32 || a->lse == nullptr)
       return MLA_ERR_INVALID_ARG;
     else
-      *defer = mla::CombinePart{(const float*)a->o_lat, a->lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, 1, plan.tpc};
+      *defer = mla::CombinePart{(const float*)a->o_lat, a->lse, nullptr, nullptr, a->seq_lens, a->max_seq_len, 1, plan.tpc,
+                                0};
     return MLA_OK;
   }
   if (split) {
@@ -614,6 +665,44 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
   if (o_lat == nullptr || !valid_dtype(o_dtype) || !aligned(o_lat, 16) || (lse && !aligned(lse, 4)))
     return MLA_ERR_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < m.total || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (m.joint) {
+    // one row-owner decode over sink ++ middle ++ recent per sequence, then its merge
+    int cus = 0;
+    s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+    mla_decode_args J;
+    Plan plan;
+    mixed_joint(parts, cus, &J, &plan);
+    J.o_lat = o_lat;
+    J.o_dtype = o_dtype;
+    J.lse = lse;
+    Layout lay;
+    cache_layout(&J.cache, &lay);
+    size_t lse_off = 0;
+    partial_bytes(&J, plan, &lse_off);
+    mla::RowsParams r{};
+    s = rows_params(&J, lay, plan, workspace, lse_off, &r);
+    if (s != MLA_OK) return s;
+    r.max_seq_len = middle->max_seq_len;   // the middle's own bound (J has the joint one)
+    for (int i = 0; i < 3; i += 2) {
+      mla::RowsParams::HiPart& h = r.hi[i >> 1];
+      h = mla::RowsParams::HiPart{};
+      const mla_decode_args* a = parts[i];
+      if (a == nullptr) continue;   // no lengths: an absent part
+      Layout l;
+      cache_layout(&a->cache, &l);
+      h.pool = (const uint8_t*)a->cache_pool;
+      h.num_blocks = a->num_blocks;
+      h.block_bytes = l.block_bytes;
+      h.block_table = a->block_table;
+      h.bt_stride = a->block_table_stride;
+      h.seq_lens = a->seq_lens;
+      h.max_seq_len = a->max_seq_len;
+    }
+    if (mla::launch_decode_rows_mixed(r, J.cache.latent_fmt, st) != hipSuccess) return MLA_ERR_HIP;
+    return rows_combine(&J, r, plan, st);
+  }
   const mla_decode_args* ref = sink ? sink : (middle ? middle : recent);
   const int B = ref->batch, R = ref->s_q * ref->num_heads, d_c = ref->cache.d_c;
   const size_t rows = (size_t)B * R;
@@ -636,13 +725,14 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
     ++n;
   }
   c.n_parts = n;
+  for (int i = 0; i < n; ++i) c.many_parts |= c.part[i].many;
   c.B = B;
   c.R = R;
   c.d_c = d_c;
   c.out = o_lat;
   c.out_bf16 = o_dtype == MLA_BF16;
   c.out_lse = lse;
-  return hip_status(mla::launch_combine_parts(c, (hipStream_t)stream));
+  return hip_status(mla::launch_combine_parts(c, st));
 }
 
 int32_t mla_append_kv(const void* c_new, int64_t c_stride, const void* k_rope_new, int64_t k_stride,

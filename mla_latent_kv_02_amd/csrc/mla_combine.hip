@@ -129,10 +129,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
     nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
     base = (size_t)b * p.max_chunks * R + r;
   } else {
-    // sequence b's blocks are the last n_b positions of its part of the block space
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-    const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    // sequence b's blocks are the last n_b positions of its part of the block space, which
+    // holds G more (the charge of its start) when it is not empty
+    const int span = p.meta[2 + b] - p.meta[1 + b];
+    const int nblk = span > 0 ? span - p.meta[p.B + 2] : 0;
     if (nblk <= 0) return;  // empty sequence: written by the decode kernel
     const int per = p.meta[0], last = p.meta[2 + b] - 1;
     const int i0 = (last - nblk + 1) / per, i1 = last / per;
@@ -227,16 +227,18 @@ __global__ __launch_bounds__(128) void combine_parts_kernel(CombinePartsParams p
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int pi = 0; pi < p.n_parts; ++pi) {
       const CombinePart& q = p.part[pi];
-      int L = q.seq_lens[b];
-      L = L < 0 ? 0 : (L > q.max_seq_len ? q.max_seq_len : L);
-      const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
       int nch;
       size_t base;
       if (q.meta == nullptr) {
+        int L = q.seq_lens[b];
+        L = L < 0 ? 0 : (L > q.max_seq_len ? q.max_seq_len : L);
+        const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
         nch = (nblk + q.tpc - 1) / q.tpc;
         nch = nch < 1 ? 1 : (nch > q.max_chunks ? q.max_chunks : nch);
         base = (size_t)b * q.max_chunks * R + r;
       } else {
+        const int span = q.meta[2 + b] - q.meta[1 + b];
+        const int nblk = span > 0 ? span - q.meta[p.B + 2] : 0;   // blocks (see combine_kernel)
         if (nblk <= 0) continue;   // no piece
         const int per = q.meta[0], last = q.meta[2 + b] - 1;
         const int i0 = (last - nblk + 1) / per, i1 = last / per;
@@ -319,7 +321,10 @@ hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
 }
 
 hipError_t launch_combine_parts(const CombinePartsParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(combine_parts_kernel<8>, dim3(p.B * p.R), dim3(128), 0, st, p);
+  if (p.many_parts)
+    hipLaunchKernelGGL(combine_parts_kernel<32>, dim3(p.B * p.R), dim3(128), 0, st, p);
+  else
+    hipLaunchKernelGGL(combine_parts_kernel<8>, dim3(p.B * p.R), dim3(128), 0, st, p);
   return hipGetLastError();
 }
 

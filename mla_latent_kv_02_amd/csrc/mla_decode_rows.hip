@@ -178,33 +178,39 @@ __device__ __forceinline__ void zero_tile(f32x4& c, const bf16x8& z) {
   else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "+a"(c) : "v"(z));
 }
 
-// c *= a (a per lane) for an AGPR tile, through 16 bytes per lane of this wave's LDS scratch:
-// inline asm cannot name the four registers of a tile one by one, and VALU instructions
-// cannot read AGPRs.  LDS operations of one wave complete in order.  Slow (two LDS round
-// trips) but rare: only when a row's running maximum moves.
-__device__ __forceinline__ void scale_tile(f32x4& c, float a, uint32_t lds) {
+// c_k *= a (a per lane) for eight AGPR tiles, through 16 bytes per lane of this wave's LDS
+// scratch: inline asm cannot name the four registers of a tile one by one, and VALU
+// instructions cannot read AGPRs.  A tile goes to the slot, comes back as four VGPRs, is
+// scaled, and goes back to its AGPRs by the slot again; the next tile enters the slot right
+// behind that read-back (LDS operations of one wave complete in order), so each tile costs one
+// wait for an LDS round trip.  Rare: only when a running maximum moves.
+#define MLA_SCALE_TILE(T)                     \
+  "ds_write_b128 %12, %" #T "\n\t"            \
+  "ds_read_b32 %0, %12\n\t"                   \
+  "ds_read_b32 %1, %12 offset:4\n\t"          \
+  "ds_read_b32 %2, %12 offset:8\n\t"          \
+  "ds_read_b32 %3, %12 offset:12\n\t"         \
+  "s_waitcnt lgkmcnt(0)\n\t"                  \
+  "v_mul_f32 %0, %0, %13\n\t"                 \
+  "v_mul_f32 %1, %1, %13\n\t"                 \
+  "v_mul_f32 %2, %2, %13\n\t"                 \
+  "v_mul_f32 %3, %3, %13\n\t"                 \
+  "ds_write_b32 %12, %0\n\t"                  \
+  "ds_write_b32 %12, %1 offset:4\n\t"         \
+  "ds_write_b32 %12, %2 offset:8\n\t"         \
+  "ds_write_b32 %12, %3 offset:12\n\t"        \
+  "ds_read_b128 %" #T ", %12\n\t"
+__device__ __forceinline__ void scale_tiles8(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, f32x4& c4, f32x4& c5,
+                                             f32x4& c6, f32x4& c7, float a, uint32_t lds) {
   float x0, x1, x2, x3;
-  asm volatile(
-      "ds_write_b128 %5, %4\n\t"
-      "ds_read_b32 %0, %5\n\t"
-      "ds_read_b32 %1, %5 offset:4\n\t"
-      "ds_read_b32 %2, %5 offset:8\n\t"
-      "ds_read_b32 %3, %5 offset:12\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_mul_f32 %0, %0, %6\n\t"
-      "v_mul_f32 %1, %1, %6\n\t"
-      "v_mul_f32 %2, %2, %6\n\t"
-      "v_mul_f32 %3, %3, %6\n\t"
-      "ds_write_b32 %5, %0\n\t"
-      "ds_write_b32 %5, %1 offset:4\n\t"
-      "ds_write_b32 %5, %2 offset:8\n\t"
-      "ds_write_b32 %5, %3 offset:12\n\t"
-      "ds_read_b128 %4, %5\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "+a"(c)
-      : "v"(lds), "v"(a)
-      : "memory");
+  asm volatile(MLA_SCALE_TILE(4) MLA_SCALE_TILE(5) MLA_SCALE_TILE(6) MLA_SCALE_TILE(7) MLA_SCALE_TILE(8)
+                   MLA_SCALE_TILE(9) MLA_SCALE_TILE(10) MLA_SCALE_TILE(11) "s_waitcnt lgkmcnt(0)"
+               : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3), "+a"(c4),
+                 "+a"(c5), "+a"(c6), "+a"(c7)
+               : "v"(lds), "v"(a)
+               : "memory");
 }
+#undef MLA_SCALE_TILE
 
 // 16 bytes of an AGPR tile to global memory (counted by vmcnt like the stage loads)
 __device__ __forceinline__ void store_tile(float* dst, const f32x4& c) {
@@ -411,13 +417,19 @@ struct QuantStage {
 // Stage table entry flags (st_info): sequence index in bits 0..19, valid tokens in 20..25.
 constexpr int INFO_START = 1 << 26;   // first stage of a piece (a sequence's blocks inside one range)
 constexpr int INFO_END = 1 << 27;     // last stage of a piece
+constexpr int INFO_PART = 28;         // mixed histories: the stage's part in bits 28..29 (1: low-bit)
 
 // ----------------------------------------------------------------------------------------
 // The kernel
 // ----------------------------------------------------------------------------------------
-template <int FMT, bool QF32>
+// MIXED: the history of sequence b is a bf16 sink ++ the low-bit middle ++ a bf16 recent
+// window (p.hi), decoded as one sequence of blocks: a bf16 block is copied into a bf16 stage by
+// DMA where a low-bit block would be dequantised into it, and every step keeps the code ring's
+// load count (a bf16 block's ring slot receives a stand-in copy of its first bytes, unread).
+template <int FMT, bool QF32, bool MIXED>
 __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   constexpr bool QUANT = FMT != FMT_BF16;
+  static_assert(QUANT || !MIXED, "a mixed history has a low-bit middle");
   using QS = QuantStage<FMT == FMT_BF16 ? FMT_INT4 : FMT>;
   // bf16: 4 ring stages.  Quantised: 2 bf16 stages + DEPTH code stages.
   constexpr int DEPTH = QUANT ? QS::DEPTH : 4;
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   __shared__ int st_len[MAX_ST];
   __shared__ int sh_scan[NT / 64 + 1];
   __shared__ int sh_scanc[NT / 64];
-  __shared__ f32x4 resc[NT];         // per-lane scratch of scale_tile
+  __shared__ f32x4 resc[NT];         // per-lane scratch of scale_tiles8
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -442,6 +454,18 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   const int rg = u % p.RG;
   const int range = u / p.RG;
   const int B = p.B, R = p.R;
+  // mixed histories: the token counts of sequence b's three parts (an absent part has none)
+  auto part_lens = [&](int b, int& Ls, int& Lm, int& Lr) {
+    auto clamp_len = [b](const int32_t* lens, int mx) {
+      if (lens == nullptr) return 0;
+      const int L = lens[b];
+      return L < 0 ? 0 : (L > mx ? mx : L);
+    };
+    Ls = clamp_len(p.hi[0].seq_lens, p.hi[0].max_seq_len);
+    Lm = clamp_len(p.seq_lens, p.max_seq_len);
+    Lr = clamp_len(p.hi[1].seq_lens, p.hi[1].max_seq_len);
+  };
+  auto nblocks = [](int L) { return (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS; };
 
   // ---- flattened block space: sequence b owns positions [P_b, P_{b+1}): G positions that
   // stand for the cost of starting a piece (a query load, a piece store), then its n_b cache
@@ -457,12 +481,23 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   int carry = 0, carry_c = 0;
   for (int base = 0; base < B; base += NT) {
     const int b = base + tid;
-    int L = 0;
+    int L = 0, n = 0;
     if (b < B) {
-      L = p.seq_lens[b];
-      L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+      if constexpr (MIXED) {
+        // blocks in joint positions (each part padded to whole blocks); the causal mask of the
+        // recent window, which starts at position 64 nsm, as L - s_q + query index, with every
+        // sink and middle token visible when the window holds fewer than s_q tokens
+        int Ls, Lm, Lr;
+        part_lens(b, Ls, Lm, Lr);
+        const int nsm = nblocks(Ls) + nblocks(Lm);
+        n = nsm + nblocks(Lr);
+        L = n > 0 ? BLOCK_TOKENS * nsm + max(Lr, p.s_q - 1) : 0;
+      } else {
+        L = p.seq_lens[b];
+        L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+        n = nblocks(L);
+      }
     }
-    const int n = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
     const int c = n > 0 ? 1 : 0;
     int x = n, xc = c;
 #pragma unroll
@@ -501,11 +536,12 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     tabC[B] = carry_c;
   }
   __syncthreads();
+  int G;
   {
     const int per0 = max(1, (carry + p.n_ranges - 1) / p.n_ranges);
     int off = 0;
     for (int b = tid; b < B; b += NT) off |= (tabP[b + 1] > tabP[b] && tabP[b] % per0 != 0) ? 1 : 0;
-    const int G = __syncthreads_or(off) ? p.phantom : 0;
+    G = __syncthreads_or(off) ? p.phantom : 0;
     for (int b = tid; b <= B; b += NT) tabP[b] += G * tabC[b];
   }
   __syncthreads();
@@ -513,7 +549,10 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   const int per = max(1, (total + p.n_ranges - 1) / p.n_ranges);
   __syncthreads();
   if (u == 0) {
-    if (tid == 0) p.meta[0] = per;
+    if (tid == 0) {
+      p.meta[0] = per;
+      p.meta[B + 2] = G;
+    }
     for (int b = tid; b <= B; b += NT) p.meta[1 + b] = tabP[b];
   }
   // empty sequences (no blocks): o = 0 and lse = -inf, written by the workgroups of the range
@@ -606,9 +645,17 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   {
     const int j = start + tid;
     int b = 0, jb = -1;
+    int Ls = 0, Lm = 0, Lr = 0;
     if (j < end) {
       b = seq_of(j);
-      jb = j - (tabP[b + 1] - (tabL[b] + BLOCK_TOKENS - 1) / BLOCK_TOKENS);   // < 0: a phantom
+      int n;
+      if constexpr (MIXED) {
+        part_lens(b, Ls, Lm, Lr);
+        n = nblocks(Ls) + nblocks(Lm) + nblocks(Lr);
+      } else {
+        n = nblocks(tabL[b]);
+      }
+      jb = j - (tabP[b + 1] - n);   // < 0: a phantom
     }
     const int is_blk = jb >= 0 ? 1 : 0;
     int x = is_blk;
@@ -628,9 +675,32 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     const int k = woff + x - is_blk;
     if (is_blk) {
       const int L = tabL[b];
-      int id = p.block_table[(size_t)b * p.bt_stride + jb];
-      int v = min(BLOCK_TOKENS, L - jb * BLOCK_TOKENS);
-      if (id < 0 || (int64_t)id >= p.num_blocks) {
+      int part = 1, jl = jb, Lp = L;   // the block's part, its index there and the part's tokens
+      const int32_t* bt = p.block_table;
+      int64_t bts = p.bt_stride, nbp = p.num_blocks;
+      if constexpr (MIXED) {
+        const int nS = nblocks(Ls), nM = nblocks(Lm);
+        if (jb < nS) {
+          part = 0;
+          Lp = Ls;
+        } else if (jb < nS + nM) {
+          jl = jb - nS;
+          Lp = Lm;
+        } else {
+          part = 2;
+          jl = jb - nS - nM;
+          Lp = Lr;
+        }
+        if (part != 1) {
+          const RowsParams::HiPart& hp = p.hi[part >> 1];
+          bt = hp.block_table;
+          bts = hp.bt_stride;
+          nbp = hp.num_blocks;
+        }
+      }
+      int id = bt[(size_t)b * bts + jl];
+      int v = min(BLOCK_TOKENS, Lp - jl * BLOCK_TOKENS);
+      if (id < 0 || (int64_t)id >= nbp) {
         id = 0;
         v = 0;
       }
@@ -638,7 +708,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       for (int h = 0; h < 2; ++h) {
         const int kk = 2 * k + h;
         const int valid = min(ST_TOK, max(0, v - ST_TOK * h));
-        int info = b | (valid << 20);
+        int info = b | (valid << 20) | (MIXED ? part << INFO_PART : 0);
         if (h == 0 && (k == 0 || jb == 0)) info |= INFO_START;
         if (h == 1 && (k == tot - 1 || j == tabP[b + 1] - 1)) info |= INFO_END;
         st_bid[kk] = id;
@@ -669,9 +739,17 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     const uint8_t* blk;
     int half;
   };
+  // the cache of a part (mixed histories: 0 sink, 1 middle, 2 recent window)
+  auto part_block = [&](int part, int id) -> const uint8_t* {
+    if (MIXED && part != 1) return p.hi[part >> 1].pool + (size_t)id * (size_t)p.hi[part >> 1].block_bytes;
+    return p.pool + (size_t)id * (size_t)p.block_bytes;
+  };
+  auto part_of = [](int info) { return MIXED ? (info >> INFO_PART) & 3 : 1; };
   auto src_of = [&](int s) {
     const int id = __builtin_amdgcn_readfirstlane(st_bid[s]);
-    return Src{p.pool + (size_t)id * (size_t)p.block_bytes, (__builtin_amdgcn_readfirstlane(st_tok[s]) / ST_TOK) & 1};
+    const int half = (__builtin_amdgcn_readfirstlane(st_tok[s]) / ST_TOK) & 1;
+    if constexpr (MIXED) return Src{part_block(part_of(__builtin_amdgcn_readfirstlane(st_info[s])), id), half};
+    else return Src{p.pool + (size_t)id * (size_t)p.block_bytes, half};
   };
   // per-lane DMA source offsets (held for the whole kernel) and this wave's LDS slice
   const uint32_t wlds = (uint32_t)__builtin_amdgcn_readfirstlane((tid & ~63) * 16);
@@ -813,7 +891,9 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) scale_tile(acc[rt][nt], a[rt], sa);
+      for (int q = 0; q < 32; q += 8)
+        scale_tiles8(acc[rt][q], acc[rt][q + 1], acc[rt][q + 2], acc[rt][q + 3], acc[rt][q + 4], acc[rt][q + 5],
+                     acc[rt][q + 6], acc[rt][q + 7], a[rt], sa);
   };
 
   // acc = 0 (the bf16 loop starts every piece from zeroed accumulators)
@@ -879,9 +959,16 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) mt[rt] = max_lg(mt[rt]);
+    // a rescale costs the same however many of the wave's rows move: once one row must move,
+    // every row takes its current maximum, which spares the later rescales that rows reaching
+    // higher scores one by one would each cost (a piece that opens on low scores)
+    bool up = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) up |= mt[rt] > m_s[rt] + ROWS_SLACK;
+    const bool move = __any(up);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float mn = mt[rt] > m_s[rt] + ROWS_SLACK ? mt[rt] : m_s[rt];
+      const float mn = move && mt[rt] > m_s[rt] ? mt[rt] : m_s[rt];
       const float mu = mn == NEG_INF ? 0.f : mn;
       // while m_s = -inf every P so far was 0 and the accumulators hold zeros: nothing to scale
       al[rt] = (mn == m_s[rt] || m_s[rt] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_s[rt] - mu);
@@ -1099,18 +1186,34 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     // ---- quantised: codes 0..DEPTH-1 in flight, code 0 dequantised into bf16 stage 0, code 1
     // landed.  Step s dequantises code s + 1 into the other bf16 stage, then scores, softmax
     // and P.V of stage s; code s + DEPTH refills the slot of code s.
+    // mixed histories: the bf16 rows of stage s by DMA into its bf16 slot (no code to dequantise)
+    auto issue_bf = [&](int s) {
+      const Src sr = src_of(s);
+      const auto bo = BfProducer::offsets(tid);
+#pragma unroll
+      for (int i = 0; i < BfProducer::LOADS; ++i)
+        BfProducer::issue_one(i, bo, sr.blk + sr.half * ST_TOK * 1152, smem_base + (s & 1) * ST_BYTES + wlds);
+    };
     for (int s = 0; s < DEPTH && s < nst; ++s) issue(s);
-    wait_stage(min(nst - 1, DEPTH - 1));
-    lds_barrier();
-    QS::dequant(smem + code_slot(0), (__builtin_amdgcn_readfirstlane(st_info[0]) >> 20) & 63, p.g_lat_log2,
-                p.g_rope_log2, bf_stage(0), tid);
-    if (nst > 1) wait_stage(min(nst - 1, DEPTH - 1) - 1);
+    const int info0 = __builtin_amdgcn_readfirstlane(st_info[0]);
+    if (part_of(info0) != 1) {
+      issue_bf(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      if (((info0 >> 20) & 63) < ST_TOK) zero_tail(0, (info0 >> 20) & 63);
+    } else {
+      wait_stage(min(nst - 1, DEPTH - 1));
+      lds_barrier();
+      QS::dequant(smem + code_slot(0), (info0 >> 20) & 63, p.g_lat_log2, p.g_rope_log2, bf_stage(0), tid);
+      if (nst > 1) wait_stage(min(nst - 1, DEPTH - 1) - 1);
+    }
     lds_barrier();
 
     // stage-table entries of step s, read at the end of step s - 1 so that their LDS latency
     // overlaps the end-of-step wait
     int n_info = st_info[0], n_tok = st_tok[0];
     int n_bid = st_bid[min(nst - 1, DEPTH)], n_btok = st_tok[min(nst - 1, DEPTH)];
+    int n_bpart = MIXED ? st_info[min(nst - 1, DEPTH)] : 0;
     for (int s = 0; s < nst; ++s) {
       const int info = __builtin_amdgcn_readfirstlane(n_info);
       const int valid = (info >> 20) & 63;
@@ -1118,14 +1221,25 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       if (s > 0 && (info & INFO_START)) start_piece(info & 0xFFFFF, __builtin_amdgcn_readfirstlane(st_len[s]), true);
       const int s_new = s + DEPTH;
       const bool refill = s_new < nst;
-      const Src sr_new{p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
+      const Src sr_new{MIXED ? part_block(part_of(__builtin_amdgcn_readfirstlane(n_bpart)), __builtin_amdgcn_readfirstlane(n_bid))
+                             : p.pool + (size_t)__builtin_amdgcn_readfirstlane(n_bid) * (size_t)p.block_bytes,
                        (__builtin_amdgcn_readfirstlane(n_btok) / ST_TOK) & 1};
       const bf16_t* KS = bf_stage(s & 1);
       // dequantise the next stage while this one is consumed: its code stage has landed and
-      // its bf16 slot was last read in step s - 1
-      if (s + 1 < nst)
-        QS::dequant(smem + code_slot((s + 1) % DEPTH), (__builtin_amdgcn_readfirstlane(st_info[s + 1]) >> 20) & 63,
-                    p.g_lat_log2, p.g_rope_log2, bf_stage((s + 1) & 1), tid);
+      // its bf16 slot was last read in step s - 1 (a bf16 block of a mixed history: its DMA
+      // into that slot, complete at the end of this step)
+      int info1 = 0;
+      bool bf_next = false;
+      if (s + 1 < nst) {
+        info1 = __builtin_amdgcn_readfirstlane(st_info[s + 1]);
+        if (MIXED && part_of(info1) != 1) {
+          bf_next = true;
+          issue_bf(s + 1);
+        } else {
+          QS::dequant(smem + code_slot((s + 1) % DEPTH), (info1 >> 20) & 63, p.g_lat_log2, p.g_rope_log2,
+                      bf_stage((s + 1) & 1), tid);
+        }
+      }
 
       f32x4 sc[2][RT];
       score_stage(KS, sc, [](int) {});
@@ -1144,6 +1258,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         n_tok = st_tok[s + 1];
         n_bid = st_bid[min(nst - 1, s + 1 + DEPTH)];
         n_btok = st_tok[min(nst - 1, s + 1 + DEPTH)];
+        if constexpr (MIXED) n_bpart = st_info[min(nst - 1, s + 1 + DEPTH)];
       }
       // the refill of this step, issued where the wave waits anyway: an issue blocks while many
       // reads are outstanding, and between MFMAs that stalls the matrix pipe
@@ -1152,7 +1267,15 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         for (int i = 0; i < LOADS; ++i) issue_one(s_new, sr_new, i);
       }
       // the next step's stage has landed and nobody reads stage s any more
-      if (s + 2 < nst) wait_stage(min(nst - 1, s + DEPTH) - (s + 2));
+      if (bf_next) {
+        // the bf16 rows of stage s + 1 (issued before this step's refill) and every code stage
+        if (refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();
+        if (((info1 >> 20) & 63) < ST_TOK) zero_tail((s + 1) & 1, (info1 >> 20) & 63);
+      } else if (s + 2 < nst) {
+        wait_stage(min(nst - 1, s + DEPTH) - (s + 2));
+      }
       lds_barrier();
     }
   }
@@ -1193,13 +1316,13 @@ __global__ __launch_bounds__(NT) void dequant_stage_rows_kernel(DequantParams p)
   }
 }
 
-template <int FMT>
+template <int FMT, bool MIXED = false>
 static hipError_t launch_fmt(const RowsParams& p, hipStream_t st) {
   const int grid = 8 * p.units_per_xcd;
   if (p.q_f32)
-    hipLaunchKernelGGL((decode_rows_kernel<FMT, true>), dim3(grid), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((decode_rows_kernel<FMT, true, MIXED>), dim3(grid), dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_rows_kernel<FMT, false>), dim3(grid), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((decode_rows_kernel<FMT, false, MIXED>), dim3(grid), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1220,6 +1343,14 @@ hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st) {
     case FMT_BF16: return rows::launch_fmt<FMT_BF16>(p, st);
     case FMT_INT4: return rows::launch_fmt<FMT_INT4>(p, st);
     case FMT_INT2: return rows::launch_fmt<FMT_INT2>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_rows_mixed(const RowsParams& p, int fmt, hipStream_t st) {
+  switch (fmt) {
+    case FMT_INT4: return rows::launch_fmt<FMT_INT4, true>(p, st);
+    case FMT_INT2: return rows::launch_fmt<FMT_INT2, true>(p, st);
   }
   return hipErrorInvalidValue;
 }

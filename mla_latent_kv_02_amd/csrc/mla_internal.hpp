@@ -60,7 +60,19 @@ struct RowsParams {
   float* part_lse;          // [B + n_ranges - 1][R]
   float* part_inv;          // [B + n_ranges - 1][R]
   int32_t* meta;            // [0]: positions per range; [1 + b]: first position of sequence b, b <= B
-                            // (its blocks are the last n_b positions before that of b + 1)
+                            // (its blocks are the last n_b positions before that of b + 1);
+                            // [B + 2]: positions charged for a non-empty sequence's start
+  // Mixed histories (decode_rows_kernel's MIXED variant): sequence b's blocks are those of
+  // hi[0] (a bf16 sink), then those of the cache above (the low-bit middle), then those of
+  // hi[1] (a bf16 recent window that ends with the s_q new tokens).
+  struct HiPart {
+    const uint8_t* pool;
+    int64_t num_blocks, block_bytes;
+    const int32_t* block_table;
+    int bt_stride;
+    const int32_t* seq_lens;  // null: the part is absent (no token in any sequence)
+    int max_seq_len;
+  } hi[2];
 };
 
 // Combine of split partials.  Chunk-major mode: the parts of a decode over several caches.
@@ -96,6 +108,7 @@ struct CombinePart {
   const int32_t* meta;
   const int32_t* seq_lens;
   int max_seq_len, max_chunks, tpc;
+  int many;                 // rows usually hold more than 16 partials of this part
 };
 
 constexpr int kMaxCombineParts = 3;
@@ -103,6 +116,7 @@ constexpr int kMaxCombineParts = 3;
 struct CombinePartsParams {
   CombinePart part[kMaxCombineParts];
   int n_parts;
+  int many_parts;           // some part usually holds more than 16 partials per row: wider batches
   int B, R, d_c;
   void* out;
   int out_bf16;
@@ -211,6 +225,8 @@ hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st);
 // one log-sum-exp merge over the split partials of up to three decodes (the mixed history)
 hipError_t launch_combine_parts(const CombinePartsParams& p, hipStream_t st);
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
+// the same kernel over mixed histories (p.hi; fmt: the middle's INT4 or INT2)
+hipError_t launch_decode_rows_mixed(const RowsParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
 hipError_t launch_dequant_partition(const DequantParams& p, int fmt, hipStream_t st);

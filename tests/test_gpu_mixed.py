@@ -154,3 +154,78 @@ def test_sink_and_window_in_one_cache(mla, H):
     el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
     assert e <= 2e-3 and el <= 2e-3
+
+
+def _mixed_case(mla, H, s_q, low, sink, middle, recent, seed, o_dtype=None):
+    """Decode sink ++ middle ++ recent (token counts per sequence) with mla_decode_mixed and
+    return (o, lse, ref_o, ref_lse); a part whose counts are all zero is passed as absent."""
+    lo_cfg = CONFIGS[low].with_(H=H)
+    hi_cfg = CONFIGS["2"].with_(H=H)
+    B = len(sink)
+    rng = np.random.default_rng(seed)
+    T = [sink[b] + middle[b] + recent[b] for b in range(B)]
+    rows = [append_rows(lo_cfg, t + 6, seed + b) for b, t in enumerate(T)]
+    c_all = [to_bf16_exact(r[0][6:]) for r in rows]
+    k_all = [to_bf16_exact(r[1][6:]) for r in rows]
+    cuts = [(c_all[b][:sink[b]], c_all[b][sink[b]:sink[b] + middle[b]], c_all[b][sink[b] + middle[b]:]) for b in range(B)]
+    kuts = [(k_all[b][:sink[b]], k_all[b][sink[b]:sink[b] + middle[b]], k_all[b][sink[b] + middle[b]:]) for b in range(B)]
+    parts = []
+    for i, (cfg, n) in enumerate(((hi_cfg, sink), (lo_cfg, middle), (hi_cfg, recent))):
+        parts.append(_part(mla, cfg, [cuts[b][i] for b in range(B)], [kuts[b][i] for b in range(B)], rng)
+                     if max(n) > 0 else None)
+    q_lat = to_bf16_exact(rng.standard_normal((B, s_q, H, 512)).astype(np.float32) * 0.1)
+    q_rope = to_bf16_exact(rng.standard_normal((B, s_q, H, 64)).astype(np.float32) * 0.1)
+    kw = {} if o_dtype is None else {"o_dtype": o_dtype}
+    o, lse = mla.decode_mixed(torch.from_numpy(q_lat).to(torch.bfloat16).to(dev()),
+                              torch.from_numpy(q_rope).to(torch.bfloat16).to(dev()), *parts, lo_cfg.sm_scale, **kw)
+    torch.cuda.synchronize()
+    cs, ks = [], []
+    for b in range(B):
+        sc, sk = _logical(hi_cfg, cuts[b][0], kuts[b][0])
+        mc, mk = _logical(lo_cfg, cuts[b][1], kuts[b][1])
+        rc, rk = _logical(hi_cfg, cuts[b][2], kuts[b][2])
+        cs.append(np.concatenate([sc, mc, rc]).reshape(-1, 512))
+        ks.append(np.concatenate([sk, mk, rk]).reshape(-1, 64))
+    # the oracle over the non-empty histories (an empty one has no attention to compare)
+    idx = [b for b in range(B) if T[b] > 0]
+    ro, rl = oracle.attend_latent(q_lat[idx].astype(np.float64), q_rope[idx].astype(np.float64),
+                                  [cs[b] for b in idx], [ks[b] for b in idx], np.array([T[b] for b in idx]), s_q,
+                                  lo_cfg.sm_scale)
+    ref_o = np.full((B, s_q, H, 512), np.nan)
+    ref_lse = np.full((B, s_q, H), np.nan)
+    ref_o[idx], ref_lse[idx] = ro, rl
+    return o.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_lse
+
+
+@pytest.mark.parametrize("low", ["4", "5"])
+def test_mixed_one_loop_edge_sequences(mla, low):
+    """128 heads (one decode over the joint history): sequences with only a sink, only a recent
+    window, nothing at all, a partial sink block and no middle, and a long middle, in one batch;
+    the empty one gets o = 0 and lse = -inf."""
+    sink = [64, 40, 0, 0, 5, 64]
+    middle = [900, 0, 0, 0, 0, 2500]
+    recent = [70, 0, 130, 0, 66, 512]
+    print(f"[case] mixed edge sequences middle {CONFIGS[low].latent_fmt}", flush=True)
+    o, lse, ref_o, ref_lse = _mixed_case(mla, 128, 1, low, sink, middle, recent, 700 + int(low))
+    e = norm_err(o[[0, 1, 2, 4, 5]], ref_o[[0, 1, 2, 4, 5]])
+    el = float(np.max(np.abs(lse[[0, 1, 2, 4, 5]] - ref_lse[[0, 1, 2, 4, 5]])))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 2e-3 and el <= 2e-3
+    assert np.all(o[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_mixed_one_loop_many_ranges(mla, s_q):
+    """128 heads, INT2 middle: a batch of ragged histories whose blocks are cut into ranges that
+    straddle the part boundaries of several sequences, with bf16 output."""
+    rng = np.random.default_rng(800 + s_q)
+    B = 10
+    sink = [int(v) for v in rng.choice([0, 17, 64, 64], B)]
+    middle = [int(v) for v in rng.integers(0, 3000, B)]
+    recent = [int(v) for v in rng.integers(2, 600, B)]
+    print(f"[case] mixed many ranges s_q={s_q} B={B}", flush=True)
+    o, lse, ref_o, ref_lse = _mixed_case(mla, 128, s_q, "5", sink, middle, recent, 900 + s_q, o_dtype=torch.bfloat16)
+    e = norm_err(o, ref_o)
+    el = float(np.max(np.abs(lse - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 4e-3 and el <= 2e-3   # bf16 output: its own rounding (2^-9 relative) on top
