@@ -314,8 +314,27 @@ bool mixed_joint(const mla_decode_args* const parts[3], int cus, mla_decode_args
   if (nblk * kBlock > (1LL << 30)) return false;
   *J = *mid;
   J->max_seq_len = (int)(nblk * kBlock);
+  if (mid->total_seq_len > 0) {
+    int64_t t = mid->total_seq_len;
+    for (int i = 0; i < 3; i += 2)
+      if (parts[i] != nullptr)
+        t += parts[i]->total_seq_len > 0 ? parts[i]->total_seq_len : (int64_t)mid->batch * parts[i]->max_seq_len;
+    J->total_seq_len = t;
+  }
   *plan = make_plan(J, cus);
-  return plan->rows;
+  if (plan->rows) return true;   // the row-owner kernel
+  // the pipelined partition kernel (at most 16 query rows): partitions over weighted positions
+  if (plan->rt != 1 || !mla::pipe_mixed_fits(mid->cache.latent_fmt, mid->cache.latent_group, mid->cache.rope_group))
+    return false;
+  int64_t hi_blk = 0;
+  for (int i = 0; i < 3; i += 2)
+    if (parts[i] != nullptr) hi_blk += ceil_div(parts[i]->max_seq_len, kBlock);
+  const int64_t wblk = mla::kMixedBf16Weight * hi_blk + ceil_div(mid->max_seq_len, kBlock);
+  if (wblk * kBlock > (1LL << 30)) return false;
+  J->max_seq_len = (int)(wblk * kBlock);
+  J->total_seq_len = 0;   // plan by the weighted bound
+  *plan = make_plan(J, cus);
+  return !plan->rows && plan->rt == 1;
 }
 
 // The args a part is decoded with: its own cache and block table, the shared queries; sink
@@ -523,6 +542,75 @@ int32_t rows_combine(const mla_decode_args* a, const mla::RowsParams& r, const P
   return hip_status(mla::launch_combine(c, a->batch, st));
 }
 
+// Partition-kernel arguments of decode `a` under `plan`: split partials in `ws` (layout of
+// partial_bytes, lse at lse_off) when the plan splits, else o_lat and lse directly.
+int32_t partition_params(const mla_decode_args* a, const Layout& lay, const Plan& plan, void* ws, size_t lse_off,
+                         mla::DecodeParams* out) {
+  mla::DecodeParams p{};
+  p.q_lat = a->q_lat;
+  p.q_rope = a->q_rope;
+  p.q_f32 = a->q_dtype == MLA_F32;
+  p.pool = (const uint8_t*)a->cache_pool;
+  p.num_blocks = a->num_blocks;
+  p.block_bytes = lay.block_bytes;
+  p.off_lc = lay.off[0];
+  p.off_ls = lay.off[1];
+  p.off_rc = lay.off[2];
+  p.off_rs = lay.off[3];
+  p.g_lat = a->cache.latent_group > 0 ? a->cache.latent_group : 1;
+  p.g_rope = a->cache.rope_group > 0 ? a->cache.rope_group : 1;
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.seq_lens = a->seq_lens;
+  p.max_seq_len = a->max_seq_len;
+  p.B = a->batch;
+  p.s_q = a->s_q;
+  p.H = a->num_heads;
+  p.R = a->s_q * a->num_heads;
+  p.RG = plan.rg;
+  p.d_c = a->cache.d_c;
+  p.d_r = a->cache.d_r;
+  p.max_chunks = plan.splits;
+  p.tpc = plan.tpc;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  const bool split = plan.splits > 1;
+  p.out = split ? ws : a->o_lat;
+  p.out_bf16 = split ? 0 : (a->o_dtype == MLA_BF16);
+  p.out_lse = split ? (float*)((char*)ws + lse_off) : a->lse;
+  const int64_t units = (int64_t)a->batch * plan.splits * plan.rg;
+  if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  p.total_units = (int)units;
+  p.units_per_xcd = (int)ceil_div(units, 8);
+  *out = p;
+  return MLA_OK;
+}
+
+// The merge of a split partition decode into o_lat and lse (hi: the bf16 parts of a mixed
+// history, whose blocks count with the sequence's, or null).
+int32_t partition_combine(const mla_decode_args* a, const mla::DecodeParams& p, const Plan& plan,
+                          const mla::MixedPart* hi, hipStream_t st) {
+  mla::CombineParams c{};
+  c.part_o = (const float*)p.out;
+  c.part_lse = p.out_lse;
+  c.seq_lens = a->seq_lens;
+  c.max_seq_len = a->max_seq_len;
+  c.R = p.R;
+  c.d_c = p.d_c;
+  c.max_chunks = plan.splits;
+  c.tpc = plan.tpc;
+  c.out = a->o_lat;
+  c.out_bf16 = a->o_dtype == MLA_BF16;
+  c.out_lse = a->lse;
+  c.many_parts = plan.splits > 16;
+  c.B = a->batch;
+  c.mixed = hi != nullptr;
+  for (int k = 0; k < 2 && hi != nullptr; ++k) {
+    c.hi_lens[k] = hi[k].seq_lens;
+    c.hi_max[k] = hi[k].max_seq_len;
+  }
+  return hip_status(mla::launch_combine(c, a->batch, st));
+}
+
 // The decode with its split partials in `ws`: the caller's workspace (mla_decode_paged) or
 // the library's per-device scratch array (mla_decode_paged_noalloc, ws == nullptr on entry).
 // With `defer`, only the decode kernel runs and *defer says where its partials are, for a
@@ -566,42 +654,11 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream, mla::
   }
 
   mla::DecodeParams p{};
-  p.q_lat = a->q_lat;
-  p.q_rope = a->q_rope;
-  p.q_f32 = a->q_dtype == MLA_F32;
-  p.pool = (const uint8_t*)a->cache_pool;
-  p.num_blocks = a->num_blocks;
-  p.block_bytes = lay.block_bytes;
-  p.off_lc = lay.off[0];
-  p.off_ls = lay.off[1];
-  p.off_rc = lay.off[2];
-  p.off_rs = lay.off[3];
-  p.g_lat = a->cache.latent_group > 0 ? a->cache.latent_group : 1;
-  p.g_rope = a->cache.rope_group > 0 ? a->cache.rope_group : 1;
-  p.block_table = a->block_table;
-  p.bt_stride = a->block_table_stride;
-  p.seq_lens = a->seq_lens;
-  p.max_seq_len = a->max_seq_len;
-  p.B = a->batch;
-  p.s_q = a->s_q;
-  p.H = a->num_heads;
-  p.R = a->s_q * a->num_heads;
-  p.RG = plan.rg;
-  p.d_c = a->cache.d_c;
-  p.d_r = a->cache.d_r;
-  p.max_chunks = plan.splits;
-  p.tpc = plan.tpc;
-  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  s = partition_params(a, lay, plan, ws, lse_off, &p);
+  if (s != MLA_OK) return s;
   const bool split = plan.splits > 1;
-  float* part_o = split ? (float*)ws : nullptr;
-  float* part_lse = split ? (float*)((char*)ws + lse_off) : nullptr;
-  p.out = split ? (void*)part_o : a->o_lat;
-  p.out_bf16 = split ? 0 : (a->o_dtype == MLA_BF16);
-  p.out_lse = split ? part_lse : a->lse;
-  const int64_t units = (int64_t)a->batch * plan.splits * plan.rg;
-  if (units > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
-  p.total_units = (int)units;
-  p.units_per_xcd = (int)ceil_div(units, 8);
+  float* part_o = split ? (float*)p.out : nullptr;
+  float* part_lse = split ? p.out_lse : nullptr;
 
   hipError_t e = plan.rt == 0 ? mla::launch_decode_f32(p, st) : mla::launch_decode_mfma(p, a->cache.latent_fmt, plan.rt, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
@@ -616,23 +673,7 @@ int32_t decode_paged(const mla_decode_args* a, bool noalloc, void* stream, mla::
                                 0};
     return MLA_OK;
   }
-  if (split) {
-    mla::CombineParams c{};
-    c.part_o = part_o;
-    c.part_lse = part_lse;
-    c.seq_lens = a->seq_lens;
-    c.max_seq_len = a->max_seq_len;
-    c.R = p.R;
-    c.d_c = p.d_c;
-    c.max_chunks = plan.splits;
-    c.tpc = plan.tpc;
-    c.out = a->o_lat;
-    c.out_bf16 = a->o_dtype == MLA_BF16;
-    c.out_lse = a->lse;
-    c.many_parts = plan.splits > 16;
-    e = mla::launch_combine(c, a->batch, st);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-  }
+  if (split) return partition_combine(a, p, plan, nullptr, st);
   return MLA_OK;
 }
 
@@ -667,7 +708,7 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
   if (workspace == nullptr || workspace_bytes < m.total || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (m.joint) {
-    // one row-owner decode over sink ++ middle ++ recent per sequence, then its merge
+    // one decode over sink ++ middle ++ recent per sequence, then its merge
     int cus = 0;
     s = device_cus(&cus);
     if (s != MLA_OK) return s;
@@ -681,17 +722,13 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
     cache_layout(&J.cache, &lay);
     size_t lse_off = 0;
     partial_bytes(&J, plan, &lse_off);
-    mla::RowsParams r{};
-    s = rows_params(&J, lay, plan, workspace, lse_off, &r);
-    if (s != MLA_OK) return s;
-    r.max_seq_len = middle->max_seq_len;   // the middle's own bound (J has the joint one)
+    mla::MixedPart hi[2] = {};
     for (int i = 0; i < 3; i += 2) {
-      mla::RowsParams::HiPart& h = r.hi[i >> 1];
-      h = mla::RowsParams::HiPart{};
       const mla_decode_args* a = parts[i];
       if (a == nullptr) continue;   // no lengths: an absent part
       Layout l;
       cache_layout(&a->cache, &l);
+      mla::MixedPart& h = hi[i >> 1];
       h.pool = (const uint8_t*)a->cache_pool;
       h.num_blocks = a->num_blocks;
       h.block_bytes = l.block_bytes;
@@ -700,8 +737,26 @@ int32_t mla_decode_mixed(const mla_decode_args* sink, const mla_decode_args* mid
       h.seq_lens = a->seq_lens;
       h.max_seq_len = a->max_seq_len;
     }
-    if (mla::launch_decode_rows_mixed(r, J.cache.latent_fmt, st) != hipSuccess) return MLA_ERR_HIP;
-    return rows_combine(&J, r, plan, st);
+    if (plan.rows) {
+      mla::RowsParams r{};
+      s = rows_params(&J, lay, plan, workspace, lse_off, &r);
+      if (s != MLA_OK) return s;
+      r.max_seq_len = middle->max_seq_len;   // the middle's own bound (J has the joint one)
+      r.hi[0] = hi[0];
+      r.hi[1] = hi[1];
+      if (mla::launch_decode_rows_mixed(r, J.cache.latent_fmt, st) != hipSuccess) return MLA_ERR_HIP;
+      return rows_combine(&J, r, plan, st);
+    }
+    mla::DecodeParams p{};
+    s = partition_params(&J, lay, plan, workspace, lse_off, &p);
+    if (s != MLA_OK) return s;
+    p.max_seq_len = middle->max_seq_len;
+    p.hi[0] = hi[0];
+    p.hi[1] = hi[1];
+    if (mla::launch_decode_pipe_mixed(p, J.cache.latent_fmt, st) != hipSuccess) return MLA_ERR_HIP;
+    if (plan.splits <= 1) return MLA_OK;
+    J.max_seq_len = middle->max_seq_len;   // the combine counts the middle's blocks from its own lengths
+    return partition_combine(&J, p, plan, hi, st);
   }
   const mla_decode_args* ref = sink ? sink : (middle ? middle : recent);
   const int B = ref->batch, R = ref->s_q * ref->num_heads, d_c = ref->cache.d_c;

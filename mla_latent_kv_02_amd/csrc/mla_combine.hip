@@ -124,7 +124,18 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   } else if (p.meta == nullptr) {
     int L = p.seq_lens[b];
     L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-    const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    if (p.mixed) {
+      // a mixed history: weighted positions of its three parts
+      int nk[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        int Lk = p.hi_lens[k] != nullptr ? p.hi_lens[k][b] : 0;
+        Lk = Lk < 0 ? 0 : (Lk > p.hi_max[k] ? p.hi_max[k] : Lk);
+        nk[k] = (Lk + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+      }
+      nblk = mixed_positions(nk[0], nblk, nk[1]);
+    }
     nch = (nblk + p.tpc - 1) / p.tpc;
     nch = nch < 1 ? 1 : (nch > p.max_chunks ? p.max_chunks : nch);
     base = (size_t)b * p.max_chunks * R + r;

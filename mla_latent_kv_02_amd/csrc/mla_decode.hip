@@ -60,6 +60,48 @@ __device__ __forceinline__ void dma16a(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// A wave-uniform pointer held as such (scalar registers), for values that are uniform by
+// construction but chosen in ways the compiler cannot follow.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The fields of a part of a mixed history as values: a choice between parts then selects
+// values (a choice between two fields of a kernel argument can become a load from a chosen
+// address, which moves the whole argument to scratch memory).
+struct MixedLocal {
+  const uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+  const int32_t* block_table;
+  int bt_stride;
+};
+__device__ __forceinline__ MixedLocal mixed_local(const MixedPart& h) {
+  return MixedLocal{uniform_ptr(h.pool), uniform_i64(h.num_blocks), uniform_i64(h.block_bytes),
+                    (const int32_t*)uniform_ptr((const uint8_t*)h.block_table),
+                    (int)__builtin_amdgcn_readfirstlane((uint32_t)h.bt_stride)};
+}
+
+// v1, or v0 for part 0 and v2 for part 2, as v1 plus differences: every choice has a constant
+// arm (a choice between two loaded variables becomes a load from a chosen address, which keeps
+// the variables, and the kernel argument they come from, in scratch memory)
+__device__ __forceinline__ int64_t by_part(int part, int64_t v0, int64_t v1, int64_t v2) {
+  return v1 + (part == 0 ? v0 - v1 : 0) + (part == 2 ? v2 - v1 : 0);
+}
+
+// Mixed histories in joint positions: the part of joint block jb (0 sink, 1 middle, 2 recent
+// window) given the sink's and the middle's block counts, and the first block of a part.
+__device__ __forceinline__ int mixed_part(int jb, int nS, int nM) { return jb < nS ? 0 : (jb < nS + nM ? 1 : 2); }
+__device__ __forceinline__ int mixed_start(int part, int nS, int nM) { return part == 0 ? 0 : (part == 1 ? nS : nS + nM); }
+
 // The same from a wave-uniform base plus a per-lane 32-bit offset (the offset in a VGPR, the
 // base in SGPRs): no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint32_t lds_base) {
@@ -702,7 +744,24 @@ __global__ __launch_bounds__(NT) void decode_mfma_kernel(DecodeParams p) {
 template <int FMT>
 using PipeQP = QuantProducer<FMT, 3>;
 
-template <int FMT, bool QF32>
+// Mixed histories: the bf16 rows of a half block (its first row at `half`) by DMA into a bf16
+// stage, and the rows from `valid` on zeroed once landed.  Out of line: the pipelined kernel
+// takes this path for a few blocks of a sequence, and inlined it perturbs the scheduling of
+// the kernel's every step.
+__device__ __attribute__((noinline)) void pipe_issue_bf16(const uint8_t* half, bf16_t* stage, int tid) {
+  Producer<FMT_BF16>::issue(half, Producer<FMT_BF16>::offsets(tid), stage, tid);
+}
+__device__ __attribute__((noinline)) void pipe_zero_rows(bf16_t* stage, int valid, int tid, int nt) {
+  for (int q = tid; q < (ST_TOK - valid) * 72; q += nt)
+    *(u32x4*)&stage[(valid + q / 72) * 576 + (q % 72) * 8] = u32x4{0, 0, 0, 0};
+}
+
+// MIXED: the history of sequence b is a bf16 sink ++ the low-bit middle ++ a bf16 recent
+// window (p.hi), each part in whole blocks, partitions cut over that joint list.  A bf16 block
+// is copied by DMA into the bf16 buffer that the dequantising wavefronts would fill, and its
+// code-ring slot receives a stand-in copy of its first bytes (unread), so every step keeps the
+// ring's load count.
+template <int FMT, bool QF32, bool MIXED>
 __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   using QP = PipeQP<FMT>;
   constexpr int DEPTH = 4;                         // code ring slots
@@ -725,14 +784,40 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   if (u >= p.total_units) return;
   const int bc = u / p.RG;                         // RG = 1: at most 16 rows
   const int b = bc / p.max_chunks, c = bc % p.max_chunks;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
-  int nch = (nblk + p.tpc - 1) / p.tpc;
+  auto clamp_len = [b](const int32_t* lens, int mx) {
+    if (lens == nullptr) return 0;
+    const int v = lens[b];
+    return v < 0 ? 0 : (v > mx ? mx : v);
+  };
+  // L: the length in the causal mask (query i sees positions <= L - s_q + i), Lend: the end of
+  // the last part's tokens.  Mixed histories in joint positions (each part padded to whole
+  // blocks, the recent window from position 64 (nS + nM)), with every sink and middle token
+  // visible when the window holds fewer than s_q tokens.
+  const int Ls = MIXED ? clamp_len(p.hi[0].seq_lens, p.hi[0].max_seq_len) : 0;
+  int Lm = p.seq_lens[b];
+  Lm = Lm < 0 ? 0 : (Lm > p.max_seq_len ? p.max_seq_len : Lm);
+  const int Lr = MIXED ? clamp_len(p.hi[1].seq_lens, p.hi[1].max_seq_len) : 0;
+  const int nS = (Ls + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  const int nM = (Lm + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  const int nR = (Lr + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  const int nblk = nS + nM + nR;
+  const int L = !MIXED ? Lm : (nblk > 0 ? BLOCK_TOKENS * (nS + nM) + max(Lr, p.s_q - 1) : 0);
+  const int Lend = !MIXED ? Lm : (nR > 0 ? BLOCK_TOKENS * (nS + nM) + Lr : (nM > 0 ? BLOCK_TOKENS * nS + Lm : Ls));
+  // this partition's joint blocks [jb0, jb1) (mixed histories: weighted positions)
+  int nch, jb0, jb1;
+  if constexpr (MIXED) {
+    nch = (mixed_positions(nS, nM, nR) + p.tpc - 1) / p.tpc;
+    jb0 = mixed_blocks_before(c * p.tpc, nS, nM, nR);
+    jb1 = mixed_blocks_before((c + 1) * p.tpc, nS, nM, nR);
+  } else {
+    nch = (nblk + p.tpc - 1) / p.tpc;
+    jb0 = c * p.tpc;
+    jb1 = min(nblk, (c + 1) * p.tpc);
+  }
   nch = nch < 1 ? 1 : nch;
   if (c >= nch) return;
-  const int T0 = c * p.tpc * BLOCK_TOKENS;
-  const int T1 = min((c + 1) * p.tpc * BLOCK_TOKENS, L);
+  const int T0 = jb0 * BLOCK_TOKENS;
+  const int T1 = min(jb1 * BLOCK_TOKENS, Lend);
   const int nst = T1 > T0 ? (T1 - T0 + ST_TOK - 1) / ST_TOK : 0;
   const int R = p.R;
 
@@ -760,17 +845,52 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   const int gl_log2 = 31 - __builtin_clz(p.g_lat > 0 ? p.g_lat : 1);
   const int gr_log2 = 31 - __builtin_clz(p.g_rope > 0 ? p.g_rope : 1);
   const int32_t* btab = p.block_table + (size_t)b * p.bt_stride;
-  const int blk0 = T0 / BLOCK_TOKENS;
-  const int nb_unit = min(p.tpc, nblk - blk0);
-  for (int j = tid; j < nb_unit; j += NT) bids[j] = btab[blk0 + j];
+  const int blk0 = jb0;
+  const int nb_unit = jb1 - jb0;   // at most tpc
+  // the part of joint block jb (mixed histories: 0 sink, 1 middle, 2 recent) and its first block
+  const MixedLocal h0 = MIXED ? mixed_local(p.hi[0]) : MixedLocal{};
+  const MixedLocal h1 = MIXED ? mixed_local(p.hi[1]) : MixedLocal{};
+  const MixedLocal hm = MIXED ? mixed_local(MixedPart{p.pool, p.num_blocks, p.block_bytes, p.block_table, p.bt_stride,
+                                                      p.seq_lens, p.max_seq_len})
+                              : MixedLocal{};
+  for (int j = tid; j < nb_unit; j += NT) {
+    if constexpr (MIXED) {
+      // the block's id in its part's pool, -1 when outside that pool
+      const int jb = blk0 + j, part = mixed_part(jb, nS, nM), jl = jb - mixed_start(part, nS, nM);
+      const int32_t* ht = (const int32_t*)(uintptr_t)by_part(part, (int64_t)(uintptr_t)h0.block_table,
+                                                               (int64_t)(uintptr_t)hm.block_table,
+                                                               (int64_t)(uintptr_t)h1.block_table);
+      const int hs = (int)by_part(part, h0.bt_stride, hm.bt_stride, h1.bt_stride);
+      const int64_t nbp = by_part(part, h0.num_blocks, hm.num_blocks, h1.num_blocks);
+      const int id = ht[(size_t)b * hs + jl];
+      bids[j] = id < 0 || (int64_t)id >= nbp ? -1 : id;
+    } else {
+      bids[j] = btab[blk0 + j];
+    }
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries and block ids, before any DMA
   __syncthreads();
 
-  auto stage_src = [&](int s, int& half, int& valid) -> const uint8_t* {
+  auto stage_src = [&](int s, int& half, int& valid) __attribute__((always_inline)) -> const uint8_t* {
     const int tok = T0 + s * ST_TOK;
     half = (tok / ST_TOK) & 1;
-    valid = min(ST_TOK, T1 - tok);
     int id = __builtin_amdgcn_readfirstlane(bids[tok / BLOCK_TOKENS - blk0]);
+    if constexpr (MIXED) {
+      // part and valid tokens from the parts' lengths (scalar arithmetic); ids were checked
+      const int jb = tok / BLOCK_TOKENS, part = mixed_part(jb, nS, nM);
+      const int Lp = (int)by_part(part, Ls, Lm, Lr);
+      valid = min(ST_TOK, max(0, Lp - ((jb - mixed_start(part, nS, nM)) * BLOCK_TOKENS + half * ST_TOK)));
+      if (id < 0) {
+        id = 0;
+        valid = 0;
+      }
+      const uint8_t* base = (const uint8_t*)(uintptr_t)by_part(part, (int64_t)(uintptr_t)h0.pool,
+                                                               (int64_t)(uintptr_t)hm.pool, (int64_t)(uintptr_t)h1.pool);
+      const int64_t bb = by_part(part, h0.block_bytes, hm.block_bytes, h1.block_bytes);
+      return uniform_ptr(base + (size_t)id * (size_t)bb);
+    } else {
+      valid = min(ST_TOK, T1 - tok);
+    }
     if (id < 0 || (int64_t)id >= p.num_blocks) {
       id = 0;
       valid = 0;
@@ -795,7 +915,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     doff1[i] = o.y;
   }
   const uint32_t wslice = (uint32_t)__builtin_amdgcn_readfirstlane((tid & ~63) * 16);
-  auto issue = [&](int k) {
+  auto issue = [&](int k) __attribute__((always_inline)) {
     int half, valid;
     const uint8_t* blk = stage_src(k, half, valid);
     const uint32_t cst = sbase + OFF_C + (k % DEPTH) * CBYTES + wslice;
@@ -822,7 +942,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   };
 
   // wavefront 0: scores of stage s, softmax, P into pbuf(s), rescale factors into alpha[s & 1]
-  auto score_softmax = [&](int s) {
+  auto score_softmax = [&](int s) __attribute__((always_inline)) {
     const bf16_t* KS = bbuf(s);
     int half_unused, valid;
     stage_src(s, half_unused, valid);
@@ -933,16 +1053,43 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     }
   };
 
+  // mixed histories: a bf16 block of stage k by DMA into bf16 buffer k (waves 0-3 issue 5
+  // instructions, waves 4-7 four), and its rows past the part's end zeroed once landed
+  auto is_bf = [&](int k) __attribute__((always_inline)) {
+    return MIXED && mixed_part((T0 + k * ST_TOK) / BLOCK_TOKENS, nS, nM) != 1;
+  };
+  auto issue_bf = [&](int k) __attribute__((always_inline)) {
+    int half, valid;
+    const uint8_t* blk = stage_src(k, half, valid);
+    pipe_issue_bf16(blk + half * ST_TOK * 1152, bbuf(k), tid);
+  };
+  auto zero_rows = [&](int k) __attribute__((always_inline)) {
+    int half_unused, valid;
+    stage_src(k, half_unused, valid);
+    if (valid < ST_TOK) pipe_zero_rows(bbuf(k), valid, tid, NT);
+  };
+
   if (nst > 0) {
     // prologue: code stages 0..3 issued, 0 and 1 dequantised by every thread, code 4 issued,
     // stage 0 scored, code 2 landed
     for (int k = 0; k < DEPTH && k < nst; ++k) issue(k);
-    wait_later(min(nst - 1, DEPTH - 1) - min(nst - 1, 1));
+    bool bf_pro = false;
+    for (int k = 0; k < 2 && k < nst; ++k)
+      if (is_bf(k)) {
+        issue_bf(k);
+        bf_pro = true;
+      }
+    if (bf_pro) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else wait_later(min(nst - 1, DEPTH - 1) - min(nst - 1, 1));
     lds_barrier();
-      for (int k = 0; k < 2 && k < nst; ++k) {
-      int half_unused, valid;
-      stage_src(k, half_unused, valid);
-      QP::dequant(cslot(k), valid, gl_log2, gr_log2, bbuf(k), tid);
+    for (int k = 0; k < 2 && k < nst; ++k) {
+      if (is_bf(k)) {
+        zero_rows(k);
+      } else {
+        int half_unused, valid;
+        stage_src(k, half_unused, valid);
+        QP::dequant(cslot(k), valid, gl_log2, gr_log2, bbuf(k), tid);
+      }
     }
     lds_barrier();
     if (DEPTH < nst) issue(DEPTH);
@@ -951,13 +1098,18 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     lds_barrier();
 
     for (int s = 0; s < nst; ++s) {
+      // a bf16 block of stage s + 2: its DMA into the buffer of stage s - 1 (read in step s - 1)
+      // before this step's code refill
+      const bool bf2 = s + 2 < nst && is_bf(s + 2);
+      if (bf2) issue_bf(s + 2);
       // refill the slot of code s + 1 (dequantised in step s - 1) with code s + 5
-      if (s + DEPTH + 1 < nst) issue(s + DEPTH + 1);
+      const bool refill = s + DEPTH + 1 < nst;
+      if (refill) issue(s + DEPTH + 1);
       if (w == 0 && s + 1 < nst) score_softmax(s + 1);
       pv(s, w, acc);
       // dequantisation by the six wavefronts that share no SIMD with wavefront 0 (waves are
       // dealt to SIMDs w mod 4): the scorer keeps its SIMD's issue slots to itself
-      if ((w & 3) != 0 && s + 2 < nst) {
+      if ((w & 3) != 0 && s + 2 < nst && !bf2) {
         int half_unused, valid;
         stage_src(s + 2, half_unused, valid);
         const int q = (w < 4 ? w - 1 : w - 2) * 64 + lane;
@@ -966,7 +1118,16 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
           QP::dequant_task(cslot(s + 2), valid, it * 384 + q, gl_log2, gr_log2, bbuf(s + 2));
       }
       // code s + 3 landed (dequantised in the next step); nobody reads the buffers of stage s
-      if (s + 3 < nst) wait_later(min(nst - 1, s + DEPTH + 1) - (s + 3));
+      if (bf2) {
+        // the bf16 rows of stage s + 2 (issued before this step's refill) and every code stage
+        if (!refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        else if (w < QP::WAVES_LO) __builtin_amdgcn_s_waitcnt(vmcnt_imm(QP::LOADS_LO));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(QP::LOADS_HI));
+        lds_barrier();
+        zero_rows(s + 2);
+      } else if (s + 3 < nst) {
+        wait_later(min(nst - 1, s + DEPTH + 1) - (s + 3));
+      }
       lds_barrier();
     }
   }
@@ -1063,9 +1224,9 @@ static hipError_t launch_mfma(const DecodeParams& p, int grid, hipStream_t st) {
     // layout, else the split kernel with 32-row tiles (same grid: one row group either way)
     if (PipeQP<FMT>::slots_needed(512 / p.g_lat, 64 / p.g_rope) > PipeQP<FMT>::SLOTS) return launch_mfma<2, FMT>(p, grid, st);
     if (p.q_f32)
-      hipLaunchKernelGGL((decode_pipe_kernel<FMT, true>), dim3(grid), dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((decode_pipe_kernel<FMT, true, false>), dim3(grid), dim3(NT), 0, st, p);
     else
-      hipLaunchKernelGGL((decode_pipe_kernel<FMT, false>), dim3(grid), dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((decode_pipe_kernel<FMT, false, false>), dim3(grid), dim3(NT), 0, st, p);
     return hipGetLastError();
   }
   if (p.q_f32)
@@ -1082,6 +1243,30 @@ static hipError_t launch_fmt(const DecodeParams& p, int fmt, int grid, hipStream
     case FMT_INT4: return launch_mfma<RT, FMT_INT4>(p, grid, st);
     case FMT_INT2: return launch_mfma<RT, FMT_INT2>(p, grid, st);
   }
+  return hipErrorInvalidValue;
+}
+
+bool pipe_mixed_fits(int fmt, int g_lat, int g_rope) {
+  if (g_lat <= 0 || g_rope <= 0) return false;
+  if (fmt == FMT_INT4) return PipeQP<FMT_INT4>::slots_needed(512 / g_lat, 64 / g_rope) <= PipeQP<FMT_INT4>::SLOTS;
+  if (fmt == FMT_INT2) return PipeQP<FMT_INT2>::slots_needed(512 / g_lat, 64 / g_rope) <= PipeQP<FMT_INT2>::SLOTS;
+  return false;
+}
+
+template <int FMT>
+static hipError_t launch_pipe_mixed(const DecodeParams& p, hipStream_t st) {
+  const int grid = 8 * p.units_per_xcd;
+  if (p.q_f32)
+    hipLaunchKernelGGL((decode_pipe_kernel<FMT, true, true>), dim3(grid), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_pipe_kernel<FMT, false, true>), dim3(grid), dim3(NT), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_pipe_mixed(const DecodeParams& p, int fmt, hipStream_t st) {
+  if (!pipe_mixed_fits(fmt, p.g_lat, p.g_rope) || p.R > 16) return hipErrorInvalidValue;
+  if (fmt == FMT_INT4) return launch_pipe_mixed<FMT_INT4>(p, st);
+  if (fmt == FMT_INT2) return launch_pipe_mixed<FMT_INT2>(p, st);
   return hipErrorInvalidValue;
 }
 

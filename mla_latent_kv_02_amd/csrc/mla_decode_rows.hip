@@ -692,10 +692,11 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
           Lp = Lr;
         }
         if (part != 1) {
-          const RowsParams::HiPart& hp = p.hi[part >> 1];
-          bt = hp.block_table;
-          bts = hp.bt_stride;
-          nbp = hp.num_blocks;
+          // fields picked by selects: a kernel argument indexed at run time goes to scratch
+          const bool rec = part == 2;
+          bt = rec ? p.hi[1].block_table : p.hi[0].block_table;
+          bts = rec ? p.hi[1].bt_stride : p.hi[0].bt_stride;
+          nbp = rec ? p.hi[1].num_blocks : p.hi[0].num_blocks;
         }
       }
       int id = bt[(size_t)b * bts + jl];
@@ -741,7 +742,10 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
   };
   // the cache of a part (mixed histories: 0 sink, 1 middle, 2 recent window)
   auto part_block = [&](int part, int id) -> const uint8_t* {
-    if (MIXED && part != 1) return p.hi[part >> 1].pool + (size_t)id * (size_t)p.hi[part >> 1].block_bytes;
+    if (MIXED && part != 1) {
+      const bool rec = part == 2;
+      return (rec ? p.hi[1].pool : p.hi[0].pool) + (size_t)id * (size_t)(rec ? p.hi[1].block_bytes : p.hi[0].block_bytes);
+    }
     return p.pool + (size_t)id * (size_t)p.block_bytes;
   };
   auto part_of = [](int info) { return MIXED ? (info >> INFO_PART) & 3 : 1; };

@@ -6,6 +6,33 @@
 
 namespace mla {
 
+// Mixed histories in the partition kernels: partitions are cut over weighted block positions,
+// a bf16 block counting kMixedBf16Weight (its rows come by DMA one step ahead of use, where a
+// low-bit block's codes come four steps ahead), so the partition that holds the recent window
+// takes fewer blocks.  Sequence b has nS sink, nM middle and nR recent blocks.
+constexpr int kMixedBf16Weight = 2;
+__host__ __device__ inline int mixed_positions(int nS, int nM, int nR) { return kMixedBf16Weight * (nS + nR) + nM; }
+// the number of joint blocks whose first weighted position lies below x
+__host__ __device__ inline int mixed_blocks_before(int x, int nS, int nM, int nR) {
+  const int W = kMixedBf16Weight;
+  const int xs = x, xm = x - W * nS, xr = x - W * nS - nM;
+  const int s = xs <= 0 ? 0 : ((xs + W - 1) / W < nS ? (xs + W - 1) / W : nS);
+  const int m = xm <= 0 ? 0 : (xm < nM ? xm : nM);
+  const int r = xr <= 0 ? 0 : ((xr + W - 1) / W < nR ? (xr + W - 1) / W : nR);
+  return s + m + r;
+}
+
+// A bf16 part of a mixed history (a sink of the earliest tokens or a recent window), decoded
+// together with a low-bit middle as one sequence of blocks per batch entry.
+struct MixedPart {
+  const uint8_t* pool;
+  int64_t num_blocks, block_bytes;
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* seq_lens;  // null: the part is absent (no token in any sequence)
+  int max_seq_len;
+};
+
 // Arguments of the decode kernels, resolved by the host layer.
 struct DecodeParams {
   const void* q_lat;        // [B][R][d_c]
@@ -27,6 +54,11 @@ struct DecodeParams {
   void* out;                // partials [B*max_chunks][R][d_c] fp32, or o_lat when max_chunks == 1
   int out_bf16;
   float* out_lse;           // [B*max_chunks][R] or lse (may be null when writing o_lat directly)
+  // mixed histories (decode_pipe_kernel's MIXED variant): sequence b's blocks are those of hi[0]
+  // (bf16 sink), then those of the cache above (low-bit middle), then those of hi[1] (bf16
+  // recent window ending with the s_q new tokens); partition c holds the joint blocks whose
+  // weighted positions start in [c tpc, (c + 1) tpc)
+  MixedPart hi[2];
 };
 
 // Arguments of the row-owner decode kernel (128 query rows per workgroup).  The batch's
@@ -65,14 +97,7 @@ struct RowsParams {
   // Mixed histories (decode_rows_kernel's MIXED variant): sequence b's blocks are those of
   // hi[0] (a bf16 sink), then those of the cache above (the low-bit middle), then those of
   // hi[1] (a bf16 recent window that ends with the s_q new tokens).
-  struct HiPart {
-    const uint8_t* pool;
-    int64_t num_blocks, block_bytes;
-    const int32_t* block_table;
-    int bt_stride;
-    const int32_t* seq_lens;  // null: the part is absent (no token in any sequence)
-    int max_seq_len;
-  } hi[2];
+  MixedPart hi[2];
 };
 
 // Combine of split partials.  Chunk-major mode: the parts of a decode over several caches.
@@ -94,6 +119,11 @@ struct CombineParams {
   int many_parts;           // rows usually hold more than 16 partials: wider load batches
   int chunk_major;          // max_chunks normalised partials per (b, row) at rows (c * B + b) * R + r
   int B;                    // batch (chunk-major mode)
+  // partition mode over mixed histories (mixed != 0): the bf16 parts' token counts (null: an
+  // absent part); partitions count weighted positions (mixed_positions)
+  int mixed;
+  const int32_t* hi_lens[2];
+  int hi_max[2];
 };
 
 // Where one decode left its split partials (a merge over several decodes reads them in place).
@@ -227,6 +257,10 @@ hipError_t launch_combine_parts(const CombinePartsParams& p, hipStream_t st);
 hipError_t launch_decode_rows(const RowsParams& p, int fmt, hipStream_t st);
 // the same kernel over mixed histories (p.hi; fmt: the middle's INT4 or INT2)
 hipError_t launch_decode_rows_mixed(const RowsParams& p, int fmt, hipStream_t st);
+// The pipelined partition kernel (at most 16 query rows, a quantised middle) over mixed
+// histories (p.hi); pipe_mixed_fits says whether that kernel takes the middle's layout.
+bool pipe_mixed_fits(int fmt, int g_lat, int g_rope);
+hipError_t launch_decode_pipe_mixed(const DecodeParams& p, int fmt, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_dequant(const DequantParams& p, int fmt, hipStream_t st);
 hipError_t launch_dequant_partition(const DequantParams& p, int fmt, hipStream_t st);

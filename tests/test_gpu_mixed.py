@@ -198,15 +198,17 @@ def _mixed_case(mla, H, s_q, low, sink, middle, recent, seed, o_dtype=None):
 
 
 @pytest.mark.parametrize("low", ["4", "5"])
-def test_mixed_one_loop_edge_sequences(mla, low):
-    """128 heads (one decode over the joint history): sequences with only a sink, only a recent
-    window, nothing at all, a partial sink block and no middle, and a long middle, in one batch;
-    the empty one gets o = 0 and lse = -inf."""
+@pytest.mark.parametrize("H", [16, 128])
+def test_mixed_one_loop_edge_sequences(mla, H, low):
+    """One decode over the joint history (16 heads: the pipelined partition kernel, 128: the
+    row-owner kernel): sequences with only a sink, only a recent window, nothing at all, a
+    partial sink block and no middle, and a long middle, in one batch; the empty one gets
+    o = 0 and lse = -inf."""
     sink = [64, 40, 0, 0, 5, 64]
     middle = [900, 0, 0, 0, 0, 2500]
     recent = [70, 0, 130, 0, 66, 512]
-    print(f"[case] mixed edge sequences middle {CONFIGS[low].latent_fmt}", flush=True)
-    o, lse, ref_o, ref_lse = _mixed_case(mla, 128, 1, low, sink, middle, recent, 700 + int(low))
+    print(f"[case] mixed edge sequences H={H} middle {CONFIGS[low].latent_fmt}", flush=True)
+    o, lse, ref_o, ref_lse = _mixed_case(mla, H, 1, low, sink, middle, recent, 700 + H + int(low))
     e = norm_err(o[[0, 1, 2, 4, 5]], ref_o[[0, 1, 2, 4, 5]])
     el = float(np.max(np.abs(lse[[0, 1, 2, 4, 5]] - ref_lse[[0, 1, 2, 4, 5]])))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
@@ -214,17 +216,18 @@ def test_mixed_one_loop_edge_sequences(mla, low):
     assert np.all(o[3] == 0) and np.all(np.isneginf(lse[3]))
 
 
-@pytest.mark.parametrize("s_q", [1, 2])
-def test_mixed_one_loop_many_ranges(mla, s_q):
-    """128 heads, INT2 middle: a batch of ragged histories whose blocks are cut into ranges that
-    straddle the part boundaries of several sequences, with bf16 output."""
-    rng = np.random.default_rng(800 + s_q)
+@pytest.mark.parametrize("H,s_q", [(16, 1), (128, 1), (128, 2)])
+def test_mixed_one_loop_many_ranges(mla, H, s_q):
+    """INT2 middle: a batch of ragged histories whose blocks are cut into ranges (128 heads) or
+    partitions (16 heads) that straddle the part boundaries of several sequences, with bf16
+    output."""
+    rng = np.random.default_rng(800 + s_q + H)
     B = 10
     sink = [int(v) for v in rng.choice([0, 17, 64, 64], B)]
     middle = [int(v) for v in rng.integers(0, 3000, B)]
     recent = [int(v) for v in rng.integers(2, 600, B)]
-    print(f"[case] mixed many ranges s_q={s_q} B={B}", flush=True)
-    o, lse, ref_o, ref_lse = _mixed_case(mla, 128, s_q, "5", sink, middle, recent, 900 + s_q, o_dtype=torch.bfloat16)
+    print(f"[case] mixed many ranges H={H} s_q={s_q} B={B}", flush=True)
+    o, lse, ref_o, ref_lse = _mixed_case(mla, H, s_q, "5", sink, middle, recent, 900 + s_q + H, o_dtype=torch.bfloat16)
     e = norm_err(o, ref_o)
     el = float(np.max(np.abs(lse - ref_lse)))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
