@@ -209,9 +209,13 @@ int32_t mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
  *   tokens and carries the causal mask (query i sees its tokens 0 .. L - s_q + i); every query
  *   sees all sink and middle tokens (the sink and the recent window may also share one
  *   cache, passed as the recent part with no sink part: the attention does not depend on
- *   token order apart from that mask).  Each part is decoded into fp32 partials and the parts
- *   are merged by log-sum-exp (exactly the attention over the concatenated history, up to
- *   rounding): o_lat [batch][s_q][H][d_c] of o_dtype, lse [batch][s_q][H] or NULL.  A part
+ *   token order apart from that mask).  With a low-bit middle and bf16 sink and recent parts
+ *   (the deployed policy), one decode streams each sequence's blocks of all three caches in
+ *   one loop (bf16 blocks copied into the stage where low-bit blocks are dequantised) and
+ *   merges its split partials; other combinations decode each part into fp32 partials and
+ *   merge the parts by log-sum-exp.  Either way the result is the attention over the
+ *   concatenated history, up to rounding: o_lat [batch][s_q][H][d_c] of o_dtype, lse
+ *   [batch][s_q][H] or NULL.  A part
  *   with no token for a sequence contributes nothing; a sequence with no token at all gets
  *   o_lat = 0 and lse = -inf.  workspace: >= mla_decode_mixed_workspace_size() bytes,
  *   256-byte aligned, scratch.
