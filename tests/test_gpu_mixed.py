@@ -232,3 +232,33 @@ def test_mixed_one_loop_many_ranges(mla, H, s_q):
     el = float(np.max(np.abs(lse - ref_lse)))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
     assert e <= 4e-3 and el <= 2e-3   # bf16 output: its own rounding (2^-9 relative) on top
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mixed_random_sweep(mla, seed):
+    """Seeded random mixed histories: 16 or 128 heads, s_q 1 or 2, INT4 or INT2 middle, 1-7
+    sequences with random sink (0-130), middle (0-2000) and window (s_q-700) token counts,
+    an absent sink part now and then, fp32 or bf16 output.  Against the oracle at the decode
+    bar (4e-3 with bf16 output); empty histories give o = 0 and lse = -inf."""
+    rng = np.random.default_rng(5000 + seed)
+    H = int(rng.choice([16, 128]))
+    s_q = int(rng.choice([1, 2]))
+    low = str(rng.choice(["4", "5"]))
+    B = int(rng.integers(1, 8))
+    no_sink = rng.random() < 0.25
+    sink = [0 if no_sink else int(v) for v in rng.integers(0, 131, B)]
+    middle = [int(v) for v in rng.integers(0, 2001, B)]
+    recent = [int(v) for v in rng.integers(s_q, 701, B)]
+    if no_sink:
+        sink[0] = 0
+    bf16_out = bool(rng.random() < 0.5)
+    print(f"[case] mixed sweep seed={seed} H={H} s_q={s_q} low={low} B={B} sink={sink} middle={middle} "
+          f"recent={recent} bf16_out={bf16_out}", flush=True)
+    o, lse, ref_o, ref_lse = _mixed_case(mla, H, s_q, low, sink, middle, recent, 6000 + seed,
+                                         o_dtype=torch.bfloat16 if bf16_out else None)
+    T = [sink[b] + middle[b] + recent[b] for b in range(B)]
+    full = [b for b in range(B) if T[b] > 0]
+    e = norm_err(o[full], ref_o[full])
+    el = float(np.max(np.abs(lse[full] - ref_lse[full])))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= (4e-3 if bf16_out else 2e-3) and el <= 2e-3
