@@ -262,3 +262,55 @@ def test_mixed_random_sweep(mla, seed):
     el = float(np.max(np.abs(lse[full] - ref_lse[full])))
     print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
     assert e <= (4e-3 if bf16_out else 2e-3) and el <= 2e-3
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_mixed_out_of_range_block_ids(mla, H):
+    """Block ids outside their part's pool (a negative id in the sink table, one past the pool
+    in the middle's, a huge one in the window's) take no part in the softmax: the result is
+    the oracle's attention over the remaining tokens (each part checks ids against its own
+    pool)."""
+    lo_cfg = CONFIGS["4"].with_(H=H)
+    hi_cfg = CONFIGS["2"].with_(H=H)
+    sink, middle, recent = [64, 100], [300, 700], [130, 70]
+    B = 2
+    print(f"[case] mixed out-of-range block ids H={H}", flush=True)
+    rng = np.random.default_rng(1200 + H)
+    T = [sink[b] + middle[b] + recent[b] for b in range(B)]
+    rows = [append_rows(lo_cfg, t + 6, 1300 + b) for b, t in enumerate(T)]
+    c_all = [to_bf16_exact(r[0][6:]) for r in rows]
+    k_all = [to_bf16_exact(r[1][6:]) for r in rows]
+    cut = lambda x, b: (x[:sink[b]], x[sink[b]:sink[b] + middle[b]], x[sink[b] + middle[b]:])  # noqa: E731
+    pc = [cut(c_all[b], b) for b in range(B)]
+    pk = [cut(k_all[b], b) for b in range(B)]
+    parts = [_part(mla, cfg, [pc[b][i] for b in range(B)], [pk[b][i] for b in range(B)], rng)
+             for i, cfg in enumerate((hi_cfg, lo_cfg, hi_cfg))]
+    # knock out: sequence 0's sink block 0, sequence 1's middle block 2, sequence 1's window block 1
+    dropped = {(0, 0, 0), (1, 1, 2), (1, 2, 1)}
+    for (b, i, blk) in dropped:
+        pool, desc, bt, sl, mx = parts[i]
+        bt[b, blk] = {0: -1, 1: pool.shape[0], 2: 1 << 30}[i]
+    q_lat = to_bf16_exact(rng.standard_normal((B, 1, H, 512)).astype(np.float32) * 0.1)
+    q_rope = to_bf16_exact(rng.standard_normal((B, 1, H, 64)).astype(np.float32) * 0.1)
+    o, lse = mla.decode_mixed(torch.from_numpy(q_lat).to(torch.bfloat16).to(dev()),
+                              torch.from_numpy(q_rope).to(torch.bfloat16).to(dev()), *parts, lo_cfg.sm_scale)
+    torch.cuda.synchronize()
+    cs, ks, Ts = [], [], []
+    for b in range(B):
+        keep_c, keep_k = [], []
+        for i, cfg in enumerate((hi_cfg, lo_cfg, hi_cfg)):
+            lc, lk = _logical(cfg, pc[b][i], pk[b][i])
+            lc, lk = lc.reshape(-1, 512), lk.reshape(-1, 64)
+            for blk in range(-(-len(lc) // 64)):
+                if (b, i, blk) not in dropped:
+                    keep_c.append(lc[64 * blk:64 * blk + 64])
+                    keep_k.append(lk[64 * blk:64 * blk + 64])
+        cs.append(np.concatenate(keep_c))
+        ks.append(np.concatenate(keep_k))
+        Ts.append(len(cs[-1]))
+    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks,
+                                          np.array(Ts), 1, lo_cfg.sm_scale)
+    e = norm_err(o.cpu().numpy(), ref_o)
+    el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 2e-3 and el <= 2e-3
