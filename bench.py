@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -40,17 +41,23 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 KERNEL_SOURCES = ["mla_latent_kv_02_amd/csrc/mla_decode.hip", "mla_latent_kv_02_amd/csrc/mla_decode_rows.hip",
                   "mla_latent_kv_02_amd/csrc/mla_combine.hip", "mla_latent_kv_02_amd/csrc/mla_stage.hpp",
-                  "mla_latent_kv_02_amd/csrc/mla_device.hpp"]
+                  "mla_latent_kv_02_amd/csrc/mla_device.hpp", "mla_latent_kv_02_amd/csrc/mla_internal.hpp"]
 
 
 GQA_KERNEL_SOURCES = ["mla_latent_kv_02_amd/csrc/mla_gqa.hip", "mla_latent_kv_02_amd/csrc/mla_combine.hip",
-                      "mla_latent_kv_02_amd/csrc/mla_stage.hpp", "mla_latent_kv_02_amd/csrc/mla_device.hpp"]
+                      "mla_latent_kv_02_amd/csrc/mla_stage.hpp", "mla_latent_kv_02_amd/csrc/mla_device.hpp",
+                      "mla_latent_kv_02_amd/csrc/mla_internal.hpp"]
 
 
 def kernel_hash(sources=None) -> str:
+    """Hash of the decode kernels' code: the sources with comments and layout removed, so that
+    an edit of a comment keeps the counter summaries that were measured on the same code."""
     h = hashlib.sha256()
     for f in sources or KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        text = open(os.path.join(ROOT, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -847,7 +847,7 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   const int32_t* btab = p.block_table + (size_t)b * p.bt_stride;
   const int blk0 = jb0;
   const int nb_unit = jb1 - jb0;   // at most tpc
-  // the part of joint block jb (mixed histories: 0 sink, 1 middle, 2 recent) and its first block
+  // mixed histories: the fields of the sink (h0), middle (hm) and recent (h1) parts as values
   const MixedLocal h0 = MIXED ? mixed_local(p.hi[0]) : MixedLocal{};
   const MixedLocal h1 = MIXED ? mixed_local(p.hi[1]) : MixedLocal{};
   const MixedLocal hm = MIXED ? mixed_local(MixedPart{p.pool, p.num_blocks, p.block_bytes, p.block_table, p.bt_stride,
