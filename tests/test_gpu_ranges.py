@@ -97,6 +97,38 @@ def test_range_deterministic(mla):
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("name,H", [("3", 128), ("3b", 112)])
+def test_range_workspace_reuse(mla, name, H):
+    """The workspace carries nothing from one call to the next: one holding stale bytes (all
+    0x7F) and the same workspace reused call after call give the bits of a zeroed one, with or
+    without lse.  112 heads x 2 queries leave a second row group of 96 rows; 30 ranges over these
+    lengths give sequences of one piece and of several, and ranges that hold several sequences."""
+    x = make_inputs(CONFIGS[name], 53, lens=[2, 700, 2900, 64, 3, 450], H=H)
+    t = to_device(x)
+    q_lat64 = bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))
+    q = torch.from_numpy(q_lat64).to(torch.bfloat16).to(dev())
+    args = (q, t["q_rope"], t["pool"], desc_of(x.cfg), t["block_table"], t["seq_lens"], int(x.seq_lens.max()),
+            x.cfg.sm_scale)
+    n = mla.decode_workspace_size(*args, num_splits=30)
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev())
+    _say("workspace reuse", name, H)
+    runs = []
+    for fill, want_lse in ((0, True), (0x7F, True), (None, True), (None, False), (None, True)):
+        if fill is not None:
+            ws.fill_(fill)
+        o, l = mla.decode_paged(*args, num_splits=30, workspace=ws, want_lse=want_lse)
+        torch.cuda.synchronize()
+        runs.append((o.cpu().numpy(), None if l is None else l.cpu().numpy()))
+    for o, l in runs[1:]:
+        np.testing.assert_array_equal(o, runs[0][0])
+        if l is not None:
+            np.testing.assert_array_equal(l, runs[0][1])
+    c, k = logical_cache(x)
+    ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c, k, x.seq_lens, x.cfg.s_q,
+                                          x.cfg.sm_scale)
+    _check(runs[0][0], runs[0][1], ref_o, ref_lse)
+
+
 def _run(mla, x, seq_lens, block_table, splits=0):
     cfg = x.cfg
     t = to_device(x)
