@@ -1107,15 +1107,19 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
       if (refill) issue(s + DEPTH + 1);
       if (w == 0 && s + 1 < nst) score_softmax(s + 1);
       pv(s, w, acc);
-      // dequantisation by the six wavefronts that share no SIMD with wavefront 0 (waves are
-      // dealt to SIMDs w mod 4): the scorer keeps its SIMD's issue slots to itself
-      if ((w & 3) != 0 && s + 2 < nst && !bf2) {
+      // dequantisation by wavefronts 1-7: the 768 tasks over their 448 lanes, lane slot q of
+      // wavefront w taking tasks q and 448 + q.  Slots 0..63 get two latent tasks, 64..319 a
+      // latent and a RoPE task, 320..447 one latent task; waves are dealt to SIMDs w mod 4, so
+      // the slot blocks go to waves (1..7) as 0, 1, 3, 6, 5, 2, 4: the SIMDs that share no
+      // wavefront with the scorer carry 3 + 0, 2 + 2 and 2 + 2 latent + RoPE tasks, and
+      // wavefront 4, beside the scorer, one latent task
+      if (w != 0 && s + 2 < nst && !bf2) {
         int half_unused, valid;
         stage_src(s + 2, half_unused, valid);
-        const int q = (w < 4 ? w - 1 : w - 2) * 64 + lane;
+        const int q = (int)((0x42563100u >> (4 * w)) & 15u) * 64 + lane;
 #pragma unroll
         for (int it = 0; it < 2; ++it)
-          QP::dequant_task(cslot(s + 2), valid, it * 384 + q, gl_log2, gr_log2, bbuf(s + 2));
+          if (it * 448 + q < 768) QP::dequant_task(cslot(s + 2), valid, it * 448 + q, gl_log2, gr_log2, bbuf(s + 2));
       }
       // code s + 3 landed (dequantised in the next step); nobody reads the buffers of stage s
       if (bf2) {
