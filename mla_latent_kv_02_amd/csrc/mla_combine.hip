@@ -218,6 +218,89 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Range mode over a 512-wide latent (the row-owner decode's pieces, a few per (b, row)): the
+// same merge as combine_kernel with one wavefront per (b, row), each lane owning 8 columns,
+// four wavefronts per workgroup.  Everything that depends only on (b, row) (the block-space
+// positions, the pieces' lse and 1/sum(P)) is wave-uniform and read through the scalar cache,
+// all loads of a batch of 8 pieces are issued together, and the kernel keeps few enough
+// registers that every wavefront of a V3-sized batch is resident at once.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
+  constexpr int CB = 4;
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float NEG_INF = -__builtin_inff();
+  const int lane = threadIdx.x & 63;
+  const int R = p.R, B = p.B;
+  const int idx = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // b * R + row
+  if (idx >= B * R) return;
+  const int b = idx / R, r = idx - b * R;
+  const int32_t* meta = p.meta;
+  // sequence b's blocks are the last n_b positions of its part of the block space, which
+  // holds G more (the charge of its start) when it is not empty
+  const int P0 = meta[1 + b], P1 = meta[2 + b];
+  const int nblk = P1 > P0 ? P1 - P0 - meta[B + 2] : 0;
+  if (nblk <= 0) return;  // empty sequence: written by the decode kernel
+  const int per = meta[0], last = P1 - 1;
+  const int i0 = (last - nblk + 1) / per, i1 = last / per;
+  const int nch = i1 - i0 + 1;
+  const size_t base = ((size_t)b + i0) * R + r;   // piece c of (b, row) at row base + c * R
+  const int d = lane * 8;
+  const float* po = p.part_o + base * 512 + d;
+  const size_t stride = (size_t)R * 512;
+  float m = NEG_INF, wsum = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int c0 = 0; c0 < nch; c0 += CB) {
+    const int n = min(CB, nch - c0);
+    float lc[CB], iv[CB];
+    f32x4 v0[CB], v1[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      // past the last piece the loads repeat it (no branches around them) and are dropped
+      const bool ok = j < n;
+      const int c = ok ? c0 + j : nch - 1;
+      const size_t u = base + (size_t)c * R;
+      const float l_ = p.part_lse[u], i_ = p.part_inv[u];
+      const f32x4 a_ = *(const f32x4*)(po + (size_t)c * stride);
+      const f32x4 b_ = *(const f32x4*)(po + (size_t)c * stride + 4);
+      lc[j] = ok ? l_ : NEG_INF;
+      iv[j] = ok ? i_ : 0.f;
+      v0[j] = a_;
+      v1[j] = b_;
+    }
+    float mb = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) mb = fmaxf(mb, lc[j]);
+    if (mb > m) {
+      // every earlier weight is relative to m; m = -inf means nothing was added yet
+      const float sc = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m - mb) * LOG2E);
+      acc0 *= sc;
+      acc1 *= sc;
+      wsum *= sc;
+      m = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float wc = lc[j] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((lc[j] - m) * LOG2E);
+      wsum += wc;
+      const float f = wc * iv[j];   // 0 for the repeated loads past the last piece
+      acc0 += f * v0[j];
+      acc1 += f * v1[j];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const f32x4 o0 = acc0 * inv, o1 = acc1 * inv;
+  const size_t ob = (size_t)idx * 512 + d;
+  if (p.out_bf16) {
+    *(u32x4*)((bf16_t*)p.out + ob) =
+        u32x4{pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]), pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+  } else {
+    *(f32x4*)((float*)p.out + ob) = o0;
+    *(f32x4*)((float*)p.out + ob + 4) = o1;
+  }
+  if (p.out_lse != nullptr && lane == 0) p.out_lse[idx] = wsum > 0.f ? m + logf(wsum) : NEG_INF;
+}
+
+// ---------------------------------------------------------------------------------------
 // Merge over several decodes (the mixed-precision history): attention over disjoint token
 // sets merges exactly by log-sum-exp, so the split partials of every part, partition or range
 // mode, are read in place and merged in one pass: one workgroup of 128 threads per (b, row),
@@ -324,6 +407,11 @@ hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st) {
 }
 
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
+  if (p.meta != nullptr && !p.chunk_major && !p.many_parts && p.d_c == 512 && p.part_inv != nullptr) {
+    const int64_t quads = ((int64_t)batch * p.R + 3) / 4;
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)quads), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   if (p.many_parts)
     hipLaunchKernelGGL(combine_kernel<32>, dim3(batch * p.R), dim3(128), 0, st, p);
   else
