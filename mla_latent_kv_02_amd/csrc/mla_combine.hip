@@ -218,20 +218,23 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Range mode over a 512-wide latent (the row-owner decode's pieces, a few per (b, row)): the
-// same merge as combine_kernel with one wavefront per (b, row), each lane owning 8 columns,
-// four wavefronts per workgroup.  Everything that depends only on (b, row) (the block-space
-// positions, the pieces' lse and 1/sum(P)) is wave-uniform and read through the scalar cache,
-// all loads of a batch of 8 pieces are issued together, and the kernel keeps few enough
-// registers that every wavefront of a V3-sized batch is resident at once.
+// Range mode over a 512-wide latent (the row-owner decode's pieces): the same merge as
+// combine_kernel, each lane owning 8 columns of a (b, row).  WPR = 1: one wavefront per
+// (b, row), four per workgroup, for rows with a few pieces; WPR = 4: the four wavefronts of a
+// workgroup share the pieces of one (b, row) (wavefront w takes pieces w, w + 4, ...) and
+// merge their running (max, sum, o) through LDS, for rows with many pieces.  Everything that
+// depends only on (b, row) (the block-space positions, the pieces' lse and 1/sum(P)) is
+// wave-uniform and read through the scalar cache, and all loads of a batch of CB pieces are
+// issued together.
 // ---------------------------------------------------------------------------------------
+template <int WPR, int CB>
 __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
-  constexpr int CB = 4;
   constexpr float LOG2E = 1.4426950408889634f;
   const float NEG_INF = -__builtin_inff();
   const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int R = p.R, B = p.B;
-  const int idx = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // b * R + row
+  const int idx = WPR == 1 ? (int)blockIdx.x * 4 + w : (int)blockIdx.x;   // b * R + row
   if (idx >= B * R) return;
   const int b = idx / R, r = idx - b * R;
   const int32_t* meta = p.meta;
@@ -247,25 +250,26 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
   const int d = lane * 8;
   const float* po = p.part_o + base * 512 + d;
   const size_t stride = (size_t)R * 512;
+  // this wavefront's pieces: c = w0 + WPR k, k < nk
+  const int w0 = WPR == 1 ? 0 : w;
+  const int nk = nch > w0 ? (nch - w0 + WPR - 1) / WPR : 0;
   float m = NEG_INF, wsum = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  for (int c0 = 0; c0 < nch; c0 += CB) {
-    const int n = min(CB, nch - c0);
+  for (int k0 = 0; k0 < nk; k0 += CB) {
+    const int n = min(CB, nk - k0);
     float lc[CB], iv[CB];
     f32x4 v0[CB], v1[CB];
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       // past the last piece the loads repeat it (no branches around them) and are dropped
       const bool ok = j < n;
-      const int c = ok ? c0 + j : nch - 1;
+      const int c = w0 + WPR * (ok ? k0 + j : nk - 1);
       const size_t u = base + (size_t)c * R;
       const float l_ = p.part_lse[u], i_ = p.part_inv[u];
-      const f32x4 a_ = *(const f32x4*)(po + (size_t)c * stride);
-      const f32x4 b_ = *(const f32x4*)(po + (size_t)c * stride + 4);
+      v0[j] = *(const f32x4*)(po + (size_t)c * stride);
+      v1[j] = *(const f32x4*)(po + (size_t)c * stride + 4);
       lc[j] = ok ? l_ : NEG_INF;
       iv[j] = ok ? i_ : 0.f;
-      v0[j] = a_;
-      v1[j] = b_;
     }
     float mb = NEG_INF;
 #pragma unroll
@@ -286,6 +290,41 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
       acc0 += f * v0[j];
       acc1 += f * v1[j];
     }
+  }
+  if constexpr (WPR > 1) {
+    // the wavefronts' running states, merged by wavefront 0 (a wavefront without pieces
+    // has m = -inf and weight 0)
+    __shared__ f32x4 xo[WPR - 1][2][64];
+    __shared__ float xm[WPR - 1], xs[WPR - 1];
+    if (w > 0) {
+      xo[w - 1][0][lane] = acc0;
+      xo[w - 1][1][lane] = acc1;
+      if (lane == 0) {
+        xm[w - 1] = m;
+        xs[w - 1] = wsum;
+      }
+    }
+    __syncthreads();
+    if (w > 0) return;
+    float mm = m;
+#pragma unroll
+    for (int q = 0; q < WPR - 1; ++q) mm = fmaxf(mm, xm[q]);
+    if (mm == NEG_INF) {
+      wsum = 0.f;
+    } else {
+      const float e = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m - mm) * LOG2E);
+      acc0 *= e;
+      acc1 *= e;
+      wsum *= e;
+#pragma unroll
+      for (int q = 0; q < WPR - 1; ++q) {
+        const float eq = xm[q] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((xm[q] - mm) * LOG2E);
+        wsum += eq * xs[q];
+        acc0 += eq * xo[q][0][lane];
+        acc1 += eq * xo[q][1][lane];
+      }
+    }
+    m = mm;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const f32x4 o0 = acc0 * inv, o1 = acc1 * inv;
@@ -407,9 +446,13 @@ hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t st) {
 }
 
 hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
-  if (p.meta != nullptr && !p.chunk_major && !p.many_parts && p.d_c == 512 && p.part_inv != nullptr) {
-    const int64_t quads = ((int64_t)batch * p.R + 3) / 4;
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)quads), dim3(256), 0, st, p);
+  if (p.meta != nullptr && !p.chunk_major && p.d_c == 512 && p.part_inv != nullptr) {
+    if (p.many_parts) {
+      hipLaunchKernelGGL((combine_rows_kernel<4, 8>), dim3((unsigned)((int64_t)batch * p.R)), dim3(256), 0, st, p);
+    } else {
+      const int64_t quads = ((int64_t)batch * p.R + 3) / 4;
+      hipLaunchKernelGGL((combine_rows_kernel<1, 4>), dim3((unsigned)quads), dim3(256), 0, st, p);
+    }
     return hipGetLastError();
   }
   if (p.many_parts)
