@@ -447,7 +447,7 @@ def main():
     if cfg.dtype != "bf16":
         roof["kernel"] = "mla_decode_paged (decode_f32_kernel + combine_kernel)"
     elif s_q * H >= 96:
-        roof["kernel"] = "mla_decode_paged (decode_rows_kernel + combine_kernel)"
+        roof["kernel"] = "mla_decode_paged (decode_rows_kernel + combine_rows_kernel)"
     elif cfg.latent_fmt in ("int4", "int2") and s_q * H <= 16:
         roof["kernel"] = "mla_decode_paged (decode_pipe_kernel + combine_kernel)"
     else:
