@@ -334,7 +334,17 @@ bool mixed_joint(const mla_decode_args* const parts[3], int cus, mla_decode_args
   J->max_seq_len = (int)(wblk * kBlock);
   J->total_seq_len = 0;   // plan by the weighted bound
   *plan = make_plan(J, cus);
-  return !plan->rows && plan->rt == 1;
+  if (plan->rows || plan->rt != 1 || plan->tpc > mla::kPipeMixedMaxBlocks) return false;
+  // the kernel keeps each block's address in 56 bits
+  for (int i = 0; i < 3; ++i) {
+    const mla_decode_args* a = parts[i];
+    if (a == nullptr) continue;
+    Layout l;
+    cache_layout(&a->cache, &l);
+    if ((uint64_t)(uintptr_t)a->cache_pool + (uint64_t)a->num_blocks * (uint64_t)l.block_bytes >= (1ULL << 56))
+      return false;
+  }
+  return true;
 }
 
 // The args a part is decoded with: its own cache and block table, the shared queries; sink

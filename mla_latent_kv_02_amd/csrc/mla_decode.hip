@@ -774,7 +774,10 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ __attribute__((aligned(16))) float alpha[2][16];
   __shared__ float fin[2][16];                     // row sums of P, maximum
-  __shared__ int bids[MAX_TPC];
+  // block ids of the partition; mixed histories: per block its address (bits 0..55) and
+  // valid tokens (bits 56..63), kPipeMixedMaxBlocks = MAX_TPC / 2 blocks at most (the host
+  // checks both)
+  __shared__ __attribute__((aligned(8))) int bids[MAX_TPC];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -863,7 +866,13 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
       const int hs = (int)by_part(part, h0.bt_stride, hm.bt_stride, h1.bt_stride);
       const int64_t nbp = by_part(part, h0.num_blocks, hm.num_blocks, h1.num_blocks);
       const int id = ht[(size_t)b * hs + jl];
-      bids[j] = id < 0 || (int64_t)id >= nbp ? -1 : id;
+      const bool ok = id >= 0 && (int64_t)id < nbp;
+      const int Lp = (int)by_part(part, Ls, Lm, Lr);
+      const int vb = ok ? min(BLOCK_TOKENS, max(0, Lp - jl * BLOCK_TOKENS)) : 0;
+      const uint8_t* base = (const uint8_t*)(uintptr_t)by_part(part, (int64_t)(uintptr_t)h0.pool,
+                                                               (int64_t)(uintptr_t)hm.pool, (int64_t)(uintptr_t)h1.pool);
+      const uint64_t a = (uint64_t)(uintptr_t)(base + (size_t)(ok ? id : 0) * (size_t)by_part(part, h0.block_bytes, hm.block_bytes, h1.block_bytes));
+      ((uint2*)bids)[j] = uint2{(uint32_t)a, (uint32_t)(a >> 32) | ((uint32_t)vb << 24)};
     } else {
       bids[j] = btab[blk0 + j];
     }
@@ -874,23 +883,15 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   auto stage_src = [&](int s, int& half, int& valid) __attribute__((always_inline)) -> const uint8_t* {
     const int tok = T0 + s * ST_TOK;
     half = (tok / ST_TOK) & 1;
-    int id = __builtin_amdgcn_readfirstlane(bids[tok / BLOCK_TOKENS - blk0]);
     if constexpr (MIXED) {
-      // part and valid tokens from the parts' lengths (scalar arithmetic); ids were checked
-      const int jb = tok / BLOCK_TOKENS, part = mixed_part(jb, nS, nM);
-      const int Lp = (int)by_part(part, Ls, Lm, Lr);
-      valid = min(ST_TOK, max(0, Lp - ((jb - mixed_start(part, nS, nM)) * BLOCK_TOKENS + half * ST_TOK)));
-      if (id < 0) {
-        id = 0;
-        valid = 0;
-      }
-      const uint8_t* base = (const uint8_t*)(uintptr_t)by_part(part, (int64_t)(uintptr_t)h0.pool,
-                                                               (int64_t)(uintptr_t)hm.pool, (int64_t)(uintptr_t)h1.pool);
-      const int64_t bb = by_part(part, h0.block_bytes, hm.block_bytes, h1.block_bytes);
-      return uniform_ptr(base + (size_t)id * (size_t)bb);
-    } else {
-      valid = min(ST_TOK, T1 - tok);
+      // the block's address and valid tokens, resolved once per block before the loop
+      const uint2 e = ((const uint2*)bids)[tok / BLOCK_TOKENS - blk0];
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(e.x), hi = __builtin_amdgcn_readfirstlane(e.y);
+      valid = min(ST_TOK, max(0, (int)(hi >> 24) - half * ST_TOK));
+      return (const uint8_t*)(uintptr_t)(((uint64_t)(hi & 0xFFFFFFu) << 32) | lo);
     }
+    int id = __builtin_amdgcn_readfirstlane(bids[tok / BLOCK_TOKENS - blk0]);
+    valid = min(ST_TOK, T1 - tok);
     if (id < 0 || (int64_t)id >= p.num_blocks) {
       id = 0;
       valid = 0;
@@ -1097,11 +1098,12 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
     if (2 < nst) wait_later(min(nst - 1, DEPTH) - 2);
     lds_barrier();
 
-    for (int s = 0; s < nst; ++s) {
+    // step s; BF2: stage s + 2 is a bf16 block of a mixed history
+    auto step = [&](int s, auto BF2) __attribute__((always_inline)) {
+      constexpr bool bf2 = decltype(BF2)::value;
       // a bf16 block of stage s + 2: its DMA into the buffer of stage s - 1 (read in step s - 1)
       // before this step's code refill
-      const bool bf2 = s + 2 < nst && is_bf(s + 2);
-      if (bf2) issue_bf(s + 2);
+      if constexpr (bf2) issue_bf(s + 2);
       // refill the slot of code s + 1 (dequantised in step s - 1) with code s + 5
       const bool refill = s + DEPTH + 1 < nst;
       if (refill) issue(s + DEPTH + 1);
@@ -1113,16 +1115,18 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
       // the slot blocks go to waves (1..7) as 0, 1, 3, 6, 5, 2, 4: the SIMDs that share no
       // wavefront with the scorer carry 3 + 0, 2 + 2 and 2 + 2 latent + RoPE tasks, and
       // wavefront 4, beside the scorer, one latent task
-      if (w != 0 && s + 2 < nst && !bf2) {
-        int half_unused, valid;
-        stage_src(s + 2, half_unused, valid);
-        const int q = (int)((0x42563100u >> (4 * w)) & 15u) * 64 + lane;
+      if constexpr (!bf2) {
+        if (w != 0 && s + 2 < nst) {
+          int half_unused, valid;
+          stage_src(s + 2, half_unused, valid);
+          const int q = (int)((0x42563100u >> (4 * w)) & 15u) * 64 + lane;
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
-          if (it * 448 + q < 768) QP::dequant_task(cslot(s + 2), valid, it * 448 + q, gl_log2, gr_log2, bbuf(s + 2));
+          for (int it = 0; it < 2; ++it)
+            if (it * 448 + q < 768) QP::dequant_task(cslot(s + 2), valid, it * 448 + q, gl_log2, gr_log2, bbuf(s + 2));
+        }
       }
       // code s + 3 landed (dequantised in the next step); nobody reads the buffers of stage s
-      if (bf2) {
+      if constexpr (bf2) {
         // the bf16 rows of stage s + 2 (issued before this step's refill) and every code stage
         if (!refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         else if (w < QP::WAVES_LO) __builtin_amdgcn_s_waitcnt(vmcnt_imm(QP::LOADS_LO));
@@ -1133,6 +1137,23 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
         wait_later(min(nst - 1, s + DEPTH + 1) - (s + 3));
       }
       lds_barrier();
+    };
+    if constexpr (!MIXED) {
+      for (int s = 0; s < nst; ++s) step(s, std::false_type{});
+    } else {
+      // The partition's stages k < kS are sink blocks and k >= kR recent-window blocks.  The
+      // steps run in stretches whose stage s + 2 is low-bit (or past the end), each a loop with
+      // no bf16 code in its body (the bf16 path inside every step's code slowed the whole loop
+      // by ~6% even where it was never taken), and the steps whose stage s + 2 is a bf16 block
+      // one by one in between.
+      const int kS = max(0, 2 * (nS - jb0)), kR = max(0, 2 * (nS + nM - jb0));
+      int s = 0;
+      while (s < nst) {
+        int e = s + 2 < kS ? s : max(s, kR - 2);
+        e = e + 2 < nst ? e : nst;
+        for (; s < e; ++s) step(s, std::false_type{});
+        if (s < nst) step(s++, std::true_type{});
+      }
     }
   }
 
@@ -1249,6 +1270,8 @@ static hipError_t launch_fmt(const DecodeParams& p, int fmt, int grid, hipStream
   }
   return hipErrorInvalidValue;
 }
+
+static_assert(kPipeMixedMaxBlocks * 2 <= MAX_TPC, "the mixed block table aliases the block ids");
 
 bool pipe_mixed_fits(int fmt, int g_lat, int g_rope) {
   if (g_lat <= 0 || g_rope <= 0) return false;
