@@ -334,14 +334,14 @@ bool mixed_joint(const mla_decode_args* const parts[3], int cus, mla_decode_args
   J->max_seq_len = (int)(wblk * kBlock);
   J->total_seq_len = 0;   // plan by the weighted bound
   *plan = make_plan(J, cus);
-  if (plan->rows || plan->rt != 1 || plan->tpc > mla::kPipeMixedMaxBlocks) return false;
+  if (plan->rows || plan->rt != 1) return false;
   // the kernel keeps each block's address in 56 bits
   for (int i = 0; i < 3; ++i) {
     const mla_decode_args* a = parts[i];
     if (a == nullptr) continue;
     Layout l;
     cache_layout(&a->cache, &l);
-    if ((uint64_t)(uintptr_t)a->cache_pool + (uint64_t)a->num_blocks * (uint64_t)l.block_bytes >= (1ULL << 56))
+    if ((uint64_t)(uintptr_t)a->cache_pool + (uint64_t)a->num_blocks * (uint64_t)l.block_bytes >= mla::kPipeAddrLimit)
       return false;
   }
   return true;

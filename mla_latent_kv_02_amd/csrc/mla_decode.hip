@@ -774,10 +774,9 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ __attribute__((aligned(16))) float alpha[2][16];
   __shared__ float fin[2][16];                     // row sums of P, maximum
-  // block ids of the partition; mixed histories: per block its address (bits 0..55) and
-  // valid tokens (bits 56..63), kPipeMixedMaxBlocks = MAX_TPC / 2 blocks at most (the host
-  // checks both)
-  __shared__ __attribute__((aligned(8))) int bids[MAX_TPC];
+  // per block of the partition: its address (bits 0..55) and valid tokens (bits 56..63),
+  // resolved once before the loop (the host keeps pools below 2^56)
+  __shared__ uint2 btab2[MAX_TPC];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -872,9 +871,13 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
       const uint8_t* base = (const uint8_t*)(uintptr_t)by_part(part, (int64_t)(uintptr_t)h0.pool,
                                                                (int64_t)(uintptr_t)hm.pool, (int64_t)(uintptr_t)h1.pool);
       const uint64_t a = (uint64_t)(uintptr_t)(base + (size_t)(ok ? id : 0) * (size_t)by_part(part, h0.block_bytes, hm.block_bytes, h1.block_bytes));
-      ((uint2*)bids)[j] = uint2{(uint32_t)a, (uint32_t)(a >> 32) | ((uint32_t)vb << 24)};
+      btab2[j] = uint2{(uint32_t)a, (uint32_t)(a >> 32) | ((uint32_t)vb << 24)};
     } else {
-      bids[j] = btab[blk0 + j];
+      const int id = btab[blk0 + j];
+      const bool ok = id >= 0 && (int64_t)id < p.num_blocks;
+      const int vb = ok ? min(BLOCK_TOKENS, max(0, Lm - (blk0 + j) * BLOCK_TOKENS)) : 0;
+      const uint64_t a = (uint64_t)(uintptr_t)(p.pool + (size_t)(ok ? id : 0) * (size_t)p.block_bytes);
+      btab2[j] = uint2{(uint32_t)a, (uint32_t)(a >> 32) | ((uint32_t)vb << 24)};
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries and block ids, before any DMA
@@ -883,20 +886,11 @@ __global__ __launch_bounds__(NT) void decode_pipe_kernel(DecodeParams p) {
   auto stage_src = [&](int s, int& half, int& valid) __attribute__((always_inline)) -> const uint8_t* {
     const int tok = T0 + s * ST_TOK;
     half = (tok / ST_TOK) & 1;
-    if constexpr (MIXED) {
-      // the block's address and valid tokens, resolved once per block before the loop
-      const uint2 e = ((const uint2*)bids)[tok / BLOCK_TOKENS - blk0];
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(e.x), hi = __builtin_amdgcn_readfirstlane(e.y);
-      valid = min(ST_TOK, max(0, (int)(hi >> 24) - half * ST_TOK));
-      return (const uint8_t*)(uintptr_t)(((uint64_t)(hi & 0xFFFFFFu) << 32) | lo);
-    }
-    int id = __builtin_amdgcn_readfirstlane(bids[tok / BLOCK_TOKENS - blk0]);
-    valid = min(ST_TOK, T1 - tok);
-    if (id < 0 || (int64_t)id >= p.num_blocks) {
-      id = 0;
-      valid = 0;
-    }
-    return p.pool + (size_t)id * (size_t)p.block_bytes;
+    // the block's address and valid tokens, resolved once per block before the loop
+    const uint2 e = btab2[tok / BLOCK_TOKENS - blk0];
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(e.x), hi = __builtin_amdgcn_readfirstlane(e.y);
+    valid = min(ST_TOK, max(0, (int)(hi >> 24) - half * ST_TOK));
+    return (const uint8_t*)(uintptr_t)(((uint64_t)(hi & 0xFFFFFFu) << 32) | lo);
   };
   const uint32_t sbase = (uint32_t)(uintptr_t)(lds_void*)smem;
   auto bbuf = [&](int k) { return (bf16_t*)(smem + (k % 3) * BF); };
@@ -1247,7 +1241,10 @@ static hipError_t launch_mfma(const DecodeParams& p, int grid, hipStream_t st) {
   if constexpr (RT == 1 && FMT != FMT_BF16) {
     // quantised cache, at most 16 rows: the pipelined kernel when its code stage holds the
     // layout, else the split kernel with 32-row tiles (same grid: one row group either way)
-    if (PipeQP<FMT>::slots_needed(512 / p.g_lat, 64 / p.g_rope) > PipeQP<FMT>::SLOTS) return launch_mfma<2, FMT>(p, grid, st);
+    // (and when the pool ends beyond the 56 bits of its per-block address table)
+    const uint64_t pool_end = (uint64_t)(uintptr_t)p.pool + (uint64_t)p.num_blocks * (uint64_t)p.block_bytes;
+    if (PipeQP<FMT>::slots_needed(512 / p.g_lat, 64 / p.g_rope) > PipeQP<FMT>::SLOTS || pool_end >= kPipeAddrLimit)
+      return launch_mfma<2, FMT>(p, grid, st);
     if (p.q_f32)
       hipLaunchKernelGGL((decode_pipe_kernel<FMT, true, false>), dim3(grid), dim3(NT), 0, st, p);
     else
@@ -1270,8 +1267,6 @@ static hipError_t launch_fmt(const DecodeParams& p, int fmt, int grid, hipStream
   }
   return hipErrorInvalidValue;
 }
-
-static_assert(kPipeMixedMaxBlocks * 2 <= MAX_TPC, "the mixed block table aliases the block ids");
 
 bool pipe_mixed_fits(int fmt, int g_lat, int g_rope) {
   if (g_lat <= 0 || g_rope <= 0) return false;

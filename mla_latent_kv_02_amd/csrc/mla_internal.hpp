@@ -11,9 +11,8 @@ namespace mla {
 // low-bit block's codes come four steps ahead), so the partition that holds the recent window
 // takes fewer blocks.  Sequence b has nS sink, nM middle and nR recent blocks.
 constexpr int kMixedBf16Weight = 2;
-// blocks per partition of the pipelined kernel's mixed variant (its per-block table of
-// addresses shares the LDS of the block ids); addresses below 2^56
-constexpr int kPipeMixedMaxBlocks = 128;
+// The pipelined kernel keeps each block's address in 56 bits of a per-block table.
+constexpr uint64_t kPipeAddrLimit = 1ULL << 56;
 __host__ __device__ inline int mixed_positions(int nS, int nM, int nR) { return kMixedBf16Weight * (nS + nR) + nM; }
 // the number of joint blocks whose first weighted position lies below x
 __host__ __device__ inline int mixed_blocks_before(int x, int nS, int nM, int nR) {
