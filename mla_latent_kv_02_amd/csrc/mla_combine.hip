@@ -340,6 +340,96 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Partition mode over a 512-wide latent (not a mixed history): the same merge as
+// combine_kernel with one wavefront per (b, row), four per workgroup, each lane owning 8
+// columns.  A partial's address does not depend on the sequence's partition count, so the
+// first batch of partials (and their lse) is loaded together with seq_lens[b], and the
+// partitions past the count (never written by this decode) are masked afterwards: the kernel
+// costs one memory round trip, not the two of a count loaded first.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_part_kernel(CombineParams p) {
+  constexpr int CB = 8;
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float NEG_INF = -__builtin_inff();
+  const int lane = threadIdx.x & 63;
+  const int R = p.R, B = p.B, MC = p.max_chunks;
+  const int idx = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // b * R + row
+  if (idx >= B * R) return;
+  const int b = idx / R, r = idx - b * R;
+  const size_t base = (size_t)b * MC * R + r;   // partial c of (b, row) at row base + c * R
+  const int d = lane * 8;
+  const float* po = p.part_o + base * 512 + d;
+  const size_t stride = (size_t)R * 512;
+  float lc[CB];
+  f32x4 v0[CB], v1[CB];
+  // first batch: partitions 0 .. CB - 1 (repeating the last one when there are fewer)
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int c = j < MC ? j : MC - 1;
+    lc[j] = p.part_lse[base + (size_t)c * R];
+    v0[j] = *(const f32x4*)(po + (size_t)c * stride);
+    v1[j] = *(const f32x4*)(po + (size_t)c * stride + 4);
+  }
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  const int nblk = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  int nch = (nblk + p.tpc - 1) / p.tpc;
+  nch = nch < 1 ? 1 : (nch > MC ? MC : nch);
+  float m = NEG_INF, wsum = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  // merge a loaded batch of partitions c0 .. c0 + CB - 1; those past nch (stale bytes) drop out
+  auto merge = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const bool ok = c0 + j < nch;
+      lc[j] = ok ? lc[j] : NEG_INF;
+      v0[j] = ok ? v0[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[j] = ok ? v1[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) mb = fmaxf(mb, lc[j]);
+    if (mb > m) {
+      // every earlier weight is relative to m; m = -inf means nothing was added yet
+      const float sc = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((m - mb) * LOG2E);
+      acc0 *= sc;
+      acc1 *= sc;
+      wsum *= sc;
+      m = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float wc = lc[j] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((lc[j] - m) * LOG2E);
+      wsum += wc;
+      acc0 += wc * v0[j];
+      acc1 += wc * v1[j];
+    }
+  };
+  merge(0);
+  for (int c0 = CB; c0 < nch; c0 += CB) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = c0 + j < nch ? c0 + j : nch - 1;
+      lc[j] = p.part_lse[base + (size_t)c * R];
+      v0[j] = *(const f32x4*)(po + (size_t)c * stride);
+      v1[j] = *(const f32x4*)(po + (size_t)c * stride + 4);
+    }
+    merge(c0);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const f32x4 o0 = acc0 * inv, o1 = acc1 * inv;
+  const size_t ob = (size_t)idx * 512 + d;
+  if (p.out_bf16) {
+    *(u32x4*)((bf16_t*)p.out + ob) =
+        u32x4{pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]), pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+  } else {
+    *(f32x4*)((float*)p.out + ob) = o0;
+    *(f32x4*)((float*)p.out + ob + 4) = o1;
+  }
+  if (p.out_lse != nullptr && lane == 0) p.out_lse[idx] = wsum > 0.f ? m + logf(wsum) : NEG_INF;
+}
+
+// ---------------------------------------------------------------------------------------
 // Merge over several decodes (the mixed-precision history): attention over disjoint token
 // sets merges exactly by log-sum-exp, so the split partials of every part, partition or range
 // mode, are read in place and merged in one pass: one workgroup of 128 threads per (b, row),
@@ -453,6 +543,12 @@ hipError_t launch_combine(const CombineParams& p, int batch, hipStream_t st) {
       const int64_t quads = ((int64_t)batch * p.R + 3) / 4;
       hipLaunchKernelGGL((combine_rows_kernel<1, 4>), dim3((unsigned)quads), dim3(256), 0, st, p);
     }
+    return hipGetLastError();
+  }
+  if (p.meta == nullptr && !p.chunk_major && !p.mixed && p.d_c == 512 && p.part_inv == nullptr &&
+      p.max_chunks >= 1) {
+    const int64_t quads = ((int64_t)batch * p.R + 3) / 4;
+    hipLaunchKernelGGL(combine_part_kernel, dim3((unsigned)quads), dim3(256), 0, st, p);
     return hipGetLastError();
   }
   if (p.many_parts)
