@@ -449,9 +449,9 @@ def main():
     elif s_q * H >= 96:
         roof["kernel"] = "mla_decode_paged (decode_rows_kernel + combine_rows_kernel)"
     elif cfg.latent_fmt in ("int4", "int2") and s_q * H <= 16:
-        roof["kernel"] = "mla_decode_paged (decode_pipe_kernel + combine_kernel)"
+        roof["kernel"] = "mla_decode_paged (decode_pipe_kernel + combine_part_kernel)"
     else:
-        roof["kernel"] = "mla_decode_paged (decode_mfma_kernel + combine_kernel)"
+        roof["kernel"] = "mla_decode_paged (decode_mfma_kernel + combine_part_kernel)"
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops
     roof["traffic"] = counted_traffic(args.workload)
