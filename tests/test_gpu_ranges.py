@@ -129,6 +129,40 @@ def test_range_workspace_reuse(mla, name, H):
     _check(runs[0][0], runs[0][1], ref_o, ref_lse)
 
 
+@pytest.mark.parametrize("name,splits", [("2", 3), ("2", 12), ("4", 12)])
+def test_partition_workspace_stale_bytes(mla, name, splits):
+    """Partition mode (16 heads): the merge reads a partition slot only when the sequence has
+    that partition.  A workspace full of NaN (0xFF) or of huge finite values (0x7F), and one
+    reused call after call, give the bits of a zeroed one.  Twelve partitions take the merge's
+    second batch of eight, and the short sequences leave most of their partition slots
+    unwritten by the decode (bf16 cache: the partition kernel; INT4: the pipelined kernel)."""
+    x = make_inputs(CONFIGS[name], 61, lens=[1, 64, 200, 2900, 1500, 5], H=16)
+    t = to_device(x)
+    q_lat64 = bf16_exact(oracle.absorb_q(x.q_nope, x.w_uk))
+    q = torch.from_numpy(q_lat64).to(torch.bfloat16).to(dev())
+    args = (q, t["q_rope"], t["pool"], desc_of(x.cfg), t["block_table"], t["seq_lens"], int(x.seq_lens.max()),
+            x.cfg.sm_scale)
+    plan = mla.decode_plan(*args, num_splits=splits)
+    assert plan[0] == splits, plan
+    n = mla.decode_workspace_size(*args, num_splits=splits)
+    ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=dev())
+    _say("partition workspace", name, splits)
+    runs = []
+    for fill in (0, 0xFF, 0x7F, None):
+        if fill is not None:
+            ws.fill_(fill)
+        o, l = mla.decode_paged(*args, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((o.cpu().numpy(), l.cpu().numpy()))
+    for o, l in runs[1:]:
+        np.testing.assert_array_equal(o, runs[0][0])
+        np.testing.assert_array_equal(l, runs[0][1])
+    c, k = logical_cache(x)
+    ref_o, ref_lse = oracle.attend_latent(q_lat64, x.q_rope.astype(np.float64), c, k, x.seq_lens, x.cfg.s_q,
+                                          x.cfg.sm_scale)
+    _check(runs[0][0], runs[0][1], ref_o, ref_lse)
+
+
 def _run(mla, x, seq_lens, block_table, splits=0):
     cfg = x.cfg
     t = to_device(x)
