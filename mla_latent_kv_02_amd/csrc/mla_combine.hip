@@ -259,17 +259,37 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
     const int n = min(CB, nk - k0);
     float lc[CB], iv[CB];
     f32x4 v0[CB], v1[CB];
+    // the pieces' lse and 1/sum(P) first: a negative factor marks an fp16 piece (a range's last
+    // piece: 512 fp16 values in the first half of its row, scaled by -factor), whose lane chunk
+    // is then loaded twice (the second load hits the cache) instead of two fp32 halves
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       // past the last piece the loads repeat it (no branches around them) and are dropped
-      const bool ok = j < n;
-      const int c = w0 + WPR * (ok ? k0 + j : nk - 1);
+      const int c = w0 + WPR * (j < n ? k0 + j : nk - 1);
       const size_t u = base + (size_t)c * R;
-      const float l_ = p.part_lse[u], i_ = p.part_inv[u];
-      v0[j] = *(const f32x4*)(po + (size_t)c * stride);
-      v1[j] = *(const f32x4*)(po + (size_t)c * stride + 4);
-      lc[j] = ok ? l_ : NEG_INF;
-      iv[j] = ok ? i_ : 0.f;
+      lc[j] = p.part_lse[u];
+      iv[j] = p.part_inv[u];
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = w0 + WPR * (j < n ? k0 + j : nk - 1);
+      const bool h = iv[j] < 0.f;
+      const float* a = h ? p.part_o + (base + (size_t)c * R) * 512 + lane * 4 : po + (size_t)c * stride;
+      v0[j] = *(const f32x4*)a;
+      v1[j] = *(const f32x4*)(h ? a : a + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      if (iv[j] < 0.f) {
+        const u32x4 q = __builtin_bit_cast(u32x4, v0[j]);
+        v0[j] = f32x4{half_bits_to_f32(q[0] & 0xFFFFu), half_bits_to_f32(q[0] >> 16), half_bits_to_f32(q[1] & 0xFFFFu),
+                      half_bits_to_f32(q[1] >> 16)};
+        v1[j] = f32x4{half_bits_to_f32(q[2] & 0xFFFFu), half_bits_to_f32(q[2] >> 16), half_bits_to_f32(q[3] & 0xFFFFu),
+                      half_bits_to_f32(q[3] >> 16)};
+        iv[j] = -iv[j];
+      }
+      lc[j] = j < n ? lc[j] : NEG_INF;
+      iv[j] = j < n ? iv[j] : 0.f;
     }
     float mb = NEG_INF;
 #pragma unroll
@@ -482,7 +502,13 @@ __global__ __launch_bounds__(128) void combine_parts_kernel(CombinePartsParams p
           v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
           if (ok) {
             const float* src = q.o + ub * d_c + d + j * stride;
-            if (vec4) {
+            if (iv[j] < 0.f) {
+              // a range's last piece of a row-owner decode: fp16 values scaled by -iv
+              const uint2 hh = *(const uint2*)((const uint16_t*)(q.o + (ub + (size_t)j * R) * d_c) + d);
+              v[j] = f32x4{half_bits_to_f32(hh.x & 0xFFFFu), half_bits_to_f32(hh.x >> 16), half_bits_to_f32(hh.y & 0xFFFFu),
+                           half_bits_to_f32(hh.y >> 16)};
+              iv[j] = -iv[j];
+            } else if (vec4) {
               v[j] = *(const f32x4*)src;
             } else {
 #pragma unroll

@@ -217,6 +217,12 @@ __device__ __forceinline__ void store_tile(float* dst, const f32x4& c) {
   asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "a"(c) : "memory");
 }
 
+// 16 bytes of an AGPR tile to LDS (the epilogue's way from the accumulators to VGPRs)
+template <int OFF>
+__device__ __forceinline__ void lds_put_tile(uint32_t addr, const f32x4& c) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "a"(c), "i"(OFF) : "memory");
+}
+
 // Reductions over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the gfx950 lane
 // swaps: with both operands equal, permlane32_swap / permlane16_swap return x at l and at l ^ 32
 // (l ^ 16), so one max / add per step gives the butterfly without an LDS round trip.
@@ -934,6 +940,69 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // as at a piece start: nothing left pending
   };
 
+  // The range's last piece, after the loop, as fp16: the stage ring is free, so each wave
+  // moves a row tile's 32 accumulator tiles through its 32 KB of the ring into VGPRs, reading
+  // them back as 8 consecutive columns of its row per 16-byte chunk (lane lg takes chunks
+  // lg, lg + 4, ..).  Each row is scaled by 2^-e so that its largest |o / sum(P)| lies in
+  // [2^14, 2^15), rounded to fp16 (RNE: error at most 2^-11 of the row's largest value) and
+  // stored row-major in the first half of its fp32 row; part_inv holds -2^e (the sign marks
+  // the format for the combine).
+  auto store_piece16 = [&](int b, const float(&m)[RT], const float(&l)[RT]) MLA_INLINE {
+    const size_t slot = (size_t)b + range;
+    int r0 = row0;
+    asm volatile("" : "+v"(r0));
+    const uint32_t wreg = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)w * 32768u);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint32_t put = wreg + (uint32_t)lane * 16u;
+      static_for<32>([&](auto NT_) MLA_INLINE {
+        constexpr int nt = decltype(NT_)::value;
+        lds_put_tile<nt * 1024>(put, acc[rt][nt]);
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // chunk q = 4 j + lg of row lr: columns 8 q .. 8 q + 7 = tile q / 2, lane groups
+      // 2 (q & 1) and 2 (q & 1) + 1 of that tile
+      f32x4 v[32];
+      const uint8_t* reg = smem + (size_t)w * 32768u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int q = 4 * j + lg;
+        const int t = q >> 1, g0 = 2 * (q & 1);
+        v[2 * j] = *(const f32x4*)(reg + t * 1024 + (lr + 16 * g0) * 16);
+        v[2 * j + 1] = *(const f32x4*)(reg + t * 1024 + (lr + 16 * (g0 + 1)) * 16);
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+      mx = max_lg(mx);
+      const float lx = sum_lg(l[rt]);
+      const float il = lx > 0.f ? 1.f / lx : 0.f;
+      const float a = mx * il;
+      // e: a 2^-e in [2^14, 2^15) (a > 0), clamped so that 2^-e and 2^e stay normal floats
+      int e = a > 0.f ? (int)((__float_as_uint(a) >> 23) & 0xFF) - 127 - 14 : 0;
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+      const float f = il * __uint_as_float((uint32_t)(127 - e) << 23);
+      const int row = r0 + 16 * rt;
+      if (row < R) {
+        uint16_t* o16 = (uint16_t*)(p.part_o + (slot * R + row) * 512);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          u32x4 h;
+          h[0] = pack_f16x2(v[2 * j][0] * f, v[2 * j][1] * f);
+          h[1] = pack_f16x2(v[2 * j][2] * f, v[2 * j][3] * f);
+          h[2] = pack_f16x2(v[2 * j + 1][0] * f, v[2 * j + 1][1] * f);
+          h[3] = pack_f16x2(v[2 * j + 1][2] * f, v[2 * j + 1][3] * f);
+          *(u32x4*)(o16 + (4 * j + lg) * 8) = h;
+        }
+        if (lg == 0) {
+          p.part_lse[slot * R + row] = lx > 0.f ? (m[rt] + __log2f(lx)) * 0.69314718055994531f : NEG_INF;
+          p.part_inv[slot * R + row] = -__uint_as_float((uint32_t)(127 + e) << 23);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read of the region done before it is reused
+    }
+  };
+
   // softmax of rows row0 + 16 rt over one stage's scores sc (this lane holds tokens 16 tt +
   // 4 lg + i) in one piece: P^T operands pt (high bf16 terms) and ptl (low terms), the
   // accumulator factor al, the running maximum m_s and sum l_x updated.  MASK: token k of the
@@ -1031,6 +1100,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
     int n_info = st_info[min(nst - 1, 1)], n_tok = st_tok[min(nst - 1, 1)];
     int n_bid = st_bid[min(nst - 1, 3)], n_btok = st_tok[min(nst - 1, 3)];
     float m_e[RT], l_e[RT];   // state of the piece ending with stage s
+    int fin_b = 0;            // the sequence of the range's last piece
     for (int s = 0; s < nst; ++s) {
       const bool has_n = s + 1 < nst;
       const int info_n = __builtin_amdgcn_readfirstlane(n_info);
@@ -1166,7 +1236,8 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
         }
       };
       pv_stage(std::false_type{}, bf_stage(s & 3), pt, ptl, hook);
-      if (info_c & INFO_END) store_piece(info_c & 0xFFFFF, m_e, l_e);
+      if ((info_c & INFO_END) && s + 1 < nst) store_piece(info_c & 0xFFFFF, m_e, l_e);
+      if (s + 1 == nst) fin_b = info_c & 0xFFFFF;
       if (has_n) {
         if (!(info_n & INFO_START) && __any(aln[0] != 1.f || aln[1] != 1.f)) rescale(aln);
 #pragma unroll
@@ -1186,6 +1257,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       }
       lds_barrier();
     }
+    store_piece16(fin_b, m_e, l_e);
   } else {
     // ---- quantised: codes 0..DEPTH-1 in flight, code 0 dequantised into bf16 stage 0, code 1
     // landed.  Step s dequantises code s + 1 into the other bf16 stage, then scores, softmax
@@ -1255,7 +1327,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       if (fresh) pv_stage(std::true_type{}, KS, pt, ptl, no_hook);
       else pv_stage(std::false_type{}, KS, pt, ptl, no_hook);
       fresh = false;
-      if (info & INFO_END) store_piece(cur_b, m_s, l_x);
+      if ((info & INFO_END) && s + 1 < nst) store_piece(cur_b, m_s, l_x);
 
       if (s + 1 < nst) {
         n_info = st_info[s + 1];
@@ -1282,6 +1354,7 @@ __global__ __launch_bounds__(NT, 1) void decode_rows_kernel(RowsParams p) {
       }
       lds_barrier();
     }
+    store_piece16(cur_b, m_s, l_x);
   }
 }
 
