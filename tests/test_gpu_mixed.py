@@ -114,6 +114,41 @@ def test_mixed_history_matches_oracle(mla, H, s_q, low):
     assert float(np.max(np.abs(lse2.cpu().numpy() - ref2_lse))) <= 2e-3
 
 
+@pytest.mark.parametrize("s_q", [1, 2])
+@pytest.mark.parametrize("H", [16, 128])
+def test_mixed_bf16_parts_merged_per_part(mla, H, s_q):
+    """A history whose middle is bf16 too is not decoded as one loop: each part is its own
+    decode (16 heads: split partitions; 128 heads: the row-owner kernel, whose ranges' last
+    pieces are fp16) and one merge reads every part's partials in place."""
+    cfg = CONFIGS["2"].with_(H=H)
+    sink, middle, recent = [64, 3, 128], [900, 0, 2100], [130, 77, 5]
+    B = 3
+    print(f"[case] bf16 parts merged per part H={H} s_q={s_q}", flush=True)
+    rng = np.random.default_rng(300 + H + s_q)
+    T = [sink[b] + middle[b] + recent[b] for b in range(B)]
+    rows = [append_rows(cfg, t + 6, 400 + b) for b, t in enumerate(T)]
+    c_all = [to_bf16_exact(r[0][6:]) for r in rows]
+    k_all = [to_bf16_exact(r[1][6:]) for r in rows]
+    cut = lambda x, b: (x[:sink[b]], x[sink[b]:sink[b] + middle[b]], x[sink[b] + middle[b]:])  # noqa: E731
+    parts_c = [cut(c_all[b], b) for b in range(B)]
+    parts_k = [cut(k_all[b], b) for b in range(B)]
+    p = [_part(mla, cfg, [parts_c[b][i] for b in range(B)], [parts_k[b][i] for b in range(B)], rng) for i in range(3)]
+    q_lat = to_bf16_exact(rng.standard_normal((B, s_q, H, 512)).astype(np.float32) * 0.1)
+    q_rope = to_bf16_exact(rng.standard_normal((B, s_q, H, 64)).astype(np.float32) * 0.1)
+    qt = torch.from_numpy(q_lat).to(torch.bfloat16).to(dev())
+    rt = torch.from_numpy(q_rope).to(torch.bfloat16).to(dev())
+    o, lse = mla.decode_mixed(qt, rt, p[0], p[1], p[2], cfg.sm_scale)
+    torch.cuda.synchronize()
+    cs = [np.concatenate([x.astype(np.float64) for x in parts_c[b]]) for b in range(B)]
+    ks = [np.concatenate([x.astype(np.float64) for x in parts_k[b]]) for b in range(B)]
+    ref_o, ref_lse = oracle.attend_latent(q_lat.astype(np.float64), q_rope.astype(np.float64), cs, ks,
+                                          np.array(T), s_q, cfg.sm_scale)
+    e = norm_err(o.cpu().numpy(), ref_o)
+    el = float(np.max(np.abs(lse.cpu().numpy() - ref_lse)))
+    print(f"  o_lat err {e:.3e}  lse abs err {el:.3e}", flush=True)
+    assert e <= 2e-3 and el <= 2e-3
+
+
 @pytest.mark.parametrize("H", [16, 128])
 def test_sink_and_window_in_one_cache(mla, H):
     """The sink and the recent window stored as one bf16 cache (sink ++ window, ending with the
